@@ -1,0 +1,28 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+def pytest_collection_modifyitems(config, items):
+    # GPU tests need a device; on a CPU-only host they are skipped, not failed,
+    # unless the run asked for them explicitly with -m gpu.
+    try:
+        import torch
+        have_gpu = torch.cuda.is_available()
+    except Exception:
+        have_gpu = False
+    if have_gpu or config.getoption("-m", default="").strip() == "gpu":
+        return
+    skip = pytest.mark.skip(reason="no GPU on this host")
+    for it in items:
+        if "gpu" in it.keywords:
+            it.add_marker(skip)
