@@ -1,0 +1,239 @@
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  * the fused causal prefill forward at B=4, H=16, N=8192, d=128 (bf16),
+  * the paged split-KV decode at B=64, Hq=32, Hkv=8, d=128, contexts
+    U{512..32768}, page 16 (bf16), including its combine kernel.
+Inputs are resident in HBM before timing starts. Each kernel launch is timed
+with HIP events recorded on the stream the kernels run on; the step time is the
+wall clock over K steps between device synchronisations.
+
+Printed: one JSON line. ``value`` is the prefill throughput in TFLOP/s (causal
+FLOPs counted as 4*B*H*N^2*d/2); the decode rate in GB/s of algorithmic HBM
+bytes sits under ``decode``. ``roofline`` describes the dominant kernel (the
+prefill forward, MFMA-bound); ``roofline_decode`` the decode (HBM-bound).
+``cpu_baseline`` times the CPU fp64 oracle on a bounded sample of the same
+workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attn fwd TFLOP/s (bf16 d=128 8K causal) + paged decode HBM GB/s"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+# HBM bytes measured by rocprofv3 (FETCH_SIZE + WRITE_SIZE) per launch, scaled by
+# the copy-kernel calibration factor; None until measured for the current kernels.
+TRAFFIC_PREFILL = None
+TRAFFIC_DECODE = None
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--exp-mode", type=int, default=0)
+    p.add_argument("--only", choices=["prefill", "decode"], default=None,
+                   help="time one kernel family only (profiling runs)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle time budget per leg")
+    return p.parse_args()
+
+
+def prefill_flops(B, H, N, d):
+    return 4.0 * B * H * N * N * d / 2.0
+
+
+def decode_bytes(seq_lens, Hq, Hkv, d, page_size):
+    L = np.asarray(seq_lens, dtype=np.int64)
+    kv = int(L.sum()) * Hkv * d * 2 * 2                 # K and V, bf16
+    qo = 2 * len(L) * Hq * d * 2                        # q read + o written, bf16
+    bt = 4 * int(((L + page_size - 1) // page_size).sum()) + 4 * len(L)
+    return kv + qo + bt
+
+
+def cpu_baseline_prefill(inp, budget_s):
+    """The oracle on whole (batch, head) slices of the prefill workload until the
+    time budget is used; returns achieved TFLOP/s (same FLOP convention)."""
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    B, N, H, d = inp.q.shape
+    done_flops, t0, heads = 0.0, time.perf_counter(), 0
+    for b in range(B):
+        for h in range(H):
+            q = _f64(inp.q[b:b + 1, :, h:h + 1])
+            k = _f64(inp.k[b:b + 1, :, h:h + 1])
+            v = _f64(inp.v[b:b + 1, :, h:h + 1])
+            oracle.attention(q, k, v, True, inp.scale, threads=threads)
+            done_flops += prefill_flops(1, 1, N, d)
+            heads += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return done_flops / dt / 1e12, threads, heads, dt
+
+
+def cpu_baseline_decode(pg, budget_s):
+    import oracle
+    import workloads as W
+    threads = len(os.sched_getaffinity(0))
+    order = list(range(pg.q.shape[0]))
+    t_total, nbytes, seqs = 0.0, 0, 0
+    for b in order:
+        sub = W.host_subpool(pg, [b])            # copy to host, untimed
+        t0 = time.perf_counter()
+        oracle.decode_paged(sub.q, sub.k_cache, sub.v_cache, sub.block_table, sub.seq_lens, sub.scale,
+                            threads=threads)
+        t_total += time.perf_counter() - t0
+        nbytes += decode_bytes(sub.seq_lens, pg.q.shape[1], sub.k_cache.shape[2], pg.q.shape[2], pg.page_size)
+        seqs += 1
+        if t_total > budget_s:
+            break
+    return nbytes / t_total / 1e9, threads, seqs, t_total
+
+
+def _f64(bits):
+    return (np.asarray(bits).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the library has no "
+              "multi-GPU path: the per-GPU kernels are each GPU's share.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import exact_attention_amd as ea
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def dev_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    run_prefill = args.only in (None, "prefill")
+    run_decode = args.only in (None, "decode")
+    t_gen = time.perf_counter()
+    if run_prefill:
+        inp = W.prefill(True)
+        q, k, v = dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v)
+        o = torch.empty_like(q)
+        B, N, H, d = inp.q.shape
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        tun = ea.tuning(exp_mode=args.exp_mode)
+    if run_decode:
+        pg = W.paged_decode_device(dev)
+        dq = dev_bf16(pg.q)
+        bt = torch.from_numpy(pg.block_table).to(dev)
+        sl = torch.from_numpy(pg.seq_lens).to(dev)
+        Bd, Hq, dd = pg.q.shape
+        Hkv = pg.k_cache.shape[2]
+        ws = torch.empty(ea.decode_workspace_size(Bd, Hq, Hkv, dd, bt.shape[1] * pg.page_size, pg.page_size),
+                         dtype=torch.uint8, device=dev)
+        # a second copy of the pool with its pages in another order, so repeats
+        # alternate between two 4.4 GB pools and cannot be served from cache
+        perm = torch.randperm(pg.k_cache.shape[0], generator=torch.Generator().manual_seed(5)).to(dev)
+        inv = torch.empty_like(perm)
+        inv[perm] = torch.arange(perm.numel(), device=dev)
+        kc2, vc2 = pg.k_cache[perm], pg.v_cache[perm]
+        bt2 = torch.where(bt >= 0, inv[bt.clamp(min=0).long()].int(), bt)
+        pools = [(pg.k_cache, pg.v_cache, bt), (kc2, vc2, bt2)]
+        do = torch.empty_like(dq)
+        dlse = torch.empty((Bd, Hq), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+
+    def step(i, ev):
+        if run_prefill:
+            ev[0].record(stream)
+            ea.attn_fwd(q, k, v, True, inp.scale, tuning=tun, out=o, lse=lse)
+            ev[1].record(stream)
+        if run_decode:
+            kc_, vc_, bt_ = pools[i % 2]
+            ev[2].record(stream)
+            r = ea.lib().ea_attn_decode_paged(ea._ptr(dq), ea._ptr(kc_), ea._ptr(vc_), ea._ptr(bt_), ea._ptr(sl),
+                                            ea._ptr(do), ea._ptr(dlse), Bd, Hq, Hkv, dd, pg.page_size,
+                                            kc_.shape[0], bt_.shape[1], pg.scale, 0, ea._ptr(ws), ws.numel(),
+                                            stream.cuda_stream)
+            ea._check(r, "ea_attn_decode_paged")
+            ev[3].record(stream)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    wev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for i in range(args.warmup):
+        step(i, wev)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1), bf16-rounded)"}
+    cfg = {"workload": "prefill fwd B=4 H=16 N=8192 d=128 causal bf16 + paged decode B=64 Hq=32 Hkv=8 "
+                       "d=128 ctx U[512,32768] page 16 bf16 (split-KV + LSE combine)",
+           "exp_mode": args.exp_mode, "input_gen_s": round(t_gen, 1)}
+    if run_prefill:
+        t_pf = np.array([e[0].elapsed_time(e[1]) for e in evs])      # ms
+        flops = prefill_flops(B, H, N, d)
+        tf = flops / (t_pf.mean() * 1e-3) / 1e12
+        out["value"] = tf
+        out["unit"] = "TFLOP/s"
+        out["prefill"] = {"ms_mean": float(t_pf.mean()), "ms_min": float(t_pf.min()), "ms_median": float(np.median(t_pf)),
+                          "tflops_best": flops / (t_pf.min() * 1e-3) / 1e12, "flop_per_launch": flops}
+        out["roofline"] = {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": tf / PEAK_BF16_TFLOPS, "traffic": TRAFFIC_PREFILL,
+                           "kernel": "ea::fwd_bf16_kernel<128, causal>"}
+    if run_decode:
+        t_dc = np.array([e[2].elapsed_time(e[3]) for e in evs])
+        nbytes = decode_bytes(pg.seq_lens, Hq, Hkv, dd, pg.page_size)
+        gbs = nbytes / (t_dc.mean() * 1e-3) / 1e9
+        out["decode"] = {"value": gbs, "unit": "GB/s", "ms_mean": float(t_dc.mean()), "ms_min": float(t_dc.min()),
+                         "bytes_per_launch": nbytes, "gbs_best": nbytes / (t_dc.min() * 1e-3) / 1e9}
+        out["roofline_decode"] = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                  "frac": gbs / PEAK_HBM_GBS, "traffic": TRAFFIC_DECODE,
+                                  "kernel": "ea::decode_split_kernel<4> + decode_combine_kernel"}
+        if not run_prefill:
+            out["value"], out["unit"] = gbs, "GB/s"
+    props = torch.cuda.get_device_properties(dev)
+    cfg["device"] = props.name
+    cfg["cus"] = props.multi_processor_count
+    out["config"] = cfg
+
+    if not args.no_cpu_baseline:
+        cb = {"kind": "oracle"}
+        if run_prefill:
+            tfc, thr, heads, dt = cpu_baseline_prefill(inp, args.cpu_seconds)
+            cb.update({"value": tfc, "unit": "TFLOP/s", "cores": thr,
+                       "sample": f"fp64 oracle on {heads} whole causal (batch, head) slices of the prefill "
+                                 f"workload ({dt:.1f} s)"})
+        if run_decode:
+            gbc, thr, seqs, dt = cpu_baseline_decode(pg, args.cpu_seconds)
+            cb["decode"] = {"value": gbc, "unit": "GB/s", "cores": thr,
+                            "sample": f"fp64 oracle on {seqs} whole sequences of the decode workload ({dt:.1f} s)"}
+            if not run_prefill:
+                cb.update({"value": gbc, "unit": "GB/s", "cores": thr, "sample": cb["decode"]["sample"]})
+        out["cpu_baseline"] = cb
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

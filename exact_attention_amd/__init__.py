@@ -1,0 +1,212 @@
+"""exact_attention_amd -- exact fused attention for AMD MI355X (gfx950).
+
+A thin ctypes binding of ``libexactattn.so`` (built in-tree by
+``exact_attention_amd.build``). Every step of the computation runs in the
+library's HIP kernels; this module only checks tensor metadata, allocates
+outputs with torch (device memory + streams) and passes raw pointers. There is
+no CPU or PyTorch fallback: if the library is missing, calls raise.
+
+Entry points mirror include/ea.h:
+  attn_fwd(q, k, v, causal, scale) -> (o, lse)
+  attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, causal, scale) -> (o, lse)
+  attn_fwd_mx8(q8, k8, v8, q_scale, k_scale, v_scale, causal, scale) -> (o, lse)
+  attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, page_size) -> (o, lse)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libexactattn.so")
+
+EA_EXP_HW, EA_EXP_POLY, EA_EXP_HYBRID = 0, 1, 2
+
+_c_int, _c_float, _c_void_p, _c_size_t = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+
+class FwdTuning(ctypes.Structure):
+    _fields_ = [("exp_mode", _c_int), ("rescale_log2", _c_float), ("natural_order", _c_int)]
+
+
+class EAError(RuntimeError):
+    pass
+
+
+_SIGNATURES = {
+    "ea_version": ([], _c_int),
+    "ea_last_error": ([], ctypes.c_char_p),
+    "ea_fwd_tuning_default": ([ctypes.POINTER(FwdTuning)], None),
+    "ea_attn_fwd": ([_c_void_p] * 5 + [_c_int] * 7 + [_c_float, _c_void_p], _c_int),
+    "ea_attn_fwd_tuned": ([_c_void_p] * 5 + [_c_int] * 7 + [_c_float, ctypes.POINTER(FwdTuning), _c_void_p], _c_int),
+    "ea_attn_fwd_varlen": ([_c_void_p] * 7 + [_c_int] * 8 + [_c_float, ctypes.POINTER(FwdTuning), _c_void_p], _c_int),
+    "ea_attn_fwd_mx8": ([_c_void_p] * 8 + [_c_int] * 6 + [_c_float, _c_void_p], _c_int),
+    "ea_decode_workspace_size": ([_c_int] * 7, _c_size_t),
+    "ea_attn_decode_paged": ([_c_void_p] * 7 + [_c_int] * 7 + [_c_float, _c_int, _c_void_p, _c_size_t, _c_void_p], _c_int),
+    "ea_test_exp2": ([_c_void_p, _c_void_p, _c_int, _c_int, _c_void_p], _c_int),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libexactattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise EAError(f"{LIB_PATH} is missing; build it with exact_attention_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        msg = lib().ea_last_error().decode(errors="replace")
+        raise EAError(f"{what} failed with status {status}: {msg}")
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype, dim: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dims, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def default_tuning() -> FwdTuning:
+    t = FwdTuning()
+    lib().ea_fwd_tuning_default(ctypes.byref(t))
+    return t
+
+
+def tuning(exp_mode: int = EA_EXP_HW, rescale_log2: float = 8.0, natural_order: int = 0) -> FwdTuning:
+    return FwdTuning(exp_mode, rescale_log2, natural_order)
+
+
+def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, *, tuning: FwdTuning | None = None,
+             out: torch.Tensor | None = None, lse: torch.Tensor | None = None, want_lse: bool = True):
+    """Exact attention forward. q [B,Nq,Hq,d], k/v [B,Nk,Hkv,d] bf16 (BSHD).
+    Returns (o [B,Nq,Hq,d] bf16, lse [B,Hq,Nq] fp32 natural log or None)."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    B, Nq, Hq, d = q.shape
+    _, Nk, Hkv, _ = k.shape
+    if tuple(v.shape) != tuple(k.shape) or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("k and v must be [B, Nk, Hkv, d] matching q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = out if out is not None else torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    st = lib().ea_attn_fwd_tuned(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Nq, Nk, Hq, Hkv, d,
+                                 int(bool(causal)), float(scale),
+                                 ctypes.byref(tuning) if tuning is not None else None, _stream(q))
+    _check(st, "ea_attn_fwd")
+    return o, lse
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, causal: bool = False,
+                    scale: float | None = None, *, tuning: FwdTuning | None = None, want_lse: bool = True):
+    """Packed variable-length forward. q [Tq,Hq,d], k/v [Tk,Hkv,d] bf16 (THD);
+    cu_seqlens int32 [S+1] on the GPU. Returns (o [Tq,Hq,d], lse [Hq,Tq])."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k, "k", torch.bfloat16, 3)
+    _need(v, "v", torch.bfloat16, 3)
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
+    _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1)
+    Tq, Hq, d = q.shape
+    Tk, Hkv, _ = k.shape
+    S = cu_seqlens_q.shape[0] - 1
+    if cu_seqlens_k.shape[0] != S + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device) if want_lse else None
+    st = lib().ea_attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens_q),
+                                  _ptr(cu_seqlens_k), S, Tq, Tk, int(max_seqlen_q), Hq, Hkv, d,
+                                  int(bool(causal)), float(scale),
+                                  ctypes.byref(tuning) if tuning is not None else None, _stream(q))
+    _check(st, "ea_attn_fwd_varlen")
+    return o, lse
+
+
+def attn_fwd_mx8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = True, scale: float | None = None,
+                 *, want_lse: bool = True):
+    """MX fp8 forward. q8/k8/v8 [B,N,H,d] uint8 e4m3 codes; q_scale/k_scale
+    [B,N,H,d/32] and v_scale [B,N/32,Hkv,d] uint8 e8m0. Returns (o bf16, lse)."""
+    for t, n in ((q8, "q8"), (k8, "k8"), (v8, "v8"), (q_scale, "q_scale"), (k_scale, "k_scale"), (v_scale, "v_scale")):
+        _need(t, n, torch.uint8, 4)
+    B, N, Hq, d = q8.shape
+    Hkv = k8.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty((B, N, Hq, d), dtype=torch.bfloat16, device=q8.device)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q8.device) if want_lse else None
+    st = lib().ea_attn_fwd_mx8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale),
+                               _ptr(o), _ptr(lse), B, N, Hq, Hkv, d, int(bool(causal)), float(scale), _stream(q8))
+    _check(st, "ea_attn_fwd_mx8")
+    return o, lse
+
+
+def decode_workspace_size(B: int, Hq: int, Hkv: int, d: int, max_seqlen: int, page_size: int,
+                          num_splits: int = 0) -> int:
+    return int(lib().ea_decode_workspace_size(B, Hq, Hkv, d, max_seqlen, page_size, num_splits))
+
+
+def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, page_size: int | None = None,
+                      scale: float | None = None, *, num_splits: int = 0, workspace: torch.Tensor | None = None,
+                      want_lse: bool = True):
+    """Paged split-KV decode. q [B,Hq,d] bf16; k/v_cache [P,page,Hkv,d] bf16;
+    block_table int32 [B,max_pages]; seq_lens int32 [B]. Returns (o [B,Hq,d], lse [B,Hq])."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    B, Hq, d = q.shape
+    P, ps, Hkv, _ = k_cache.shape
+    if page_size is not None and page_size != ps:
+        raise ValueError("page_size does not match k_cache.shape[1]")
+    max_pages = block_table.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = decode_workspace_size(B, Hq, Hkv, d, max_pages * ps, ps, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if want_lse else None
+    st = lib().ea_attn_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+                                    _ptr(o), _ptr(lse), B, Hq, Hkv, d, ps, P, max_pages, float(scale),
+                                    int(num_splits), _ptr(workspace), workspace.numel(), _stream(q))
+    _check(st, "ea_attn_decode_paged")
+    return o, lse
+
+
+def test_exp2(x: torch.Tensor, mode: int) -> torch.Tensor:
+    """Test-only: 2^x with the kernels' exponential (EA_EXP_HW or EA_EXP_POLY)."""
+    _need(x, "x", torch.float32, 1)
+    y = torch.empty_like(x)
+    _check(lib().ea_test_exp2(_ptr(x), _ptr(y), x.numel(), int(mode), _stream(x)), "ea_test_exp2")
+    return y

@@ -1,0 +1,286 @@
+// C ABI of libexactattn.so: argument validation (host only, before any HIP
+// call), tuning defaults, work decomposition parameters and kernel dispatch.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "ea.h"
+#include "ea_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ea_status fail(ea_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+ea_status ok() {
+  g_err[0] = '\0';
+  return EA_OK;
+}
+
+ea_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(EA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool finite_pos(float x) { return std::isfinite(x) && x > 0.f; }
+
+ea_status check_tuning(const ea_fwd_tuning* t) {
+  if (t == nullptr) return EA_OK;
+  if (t->exp_mode < 0 || t->exp_mode > 2) return fail(EA_ERR_INVALID, "tuning.exp_mode must be 0, 1 or 2");
+  if (!(t->rescale_log2 >= 0.f && t->rescale_log2 <= 16.f))
+    return fail(EA_ERR_INVALID, "tuning.rescale_log2 must be in [0, 16]");
+  if (t->natural_order != 0 && t->natural_order != 1)
+    return fail(EA_ERR_INVALID, "tuning.natural_order must be 0 or 1");
+  return EA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ea_version(void) { return 1; }
+
+const char* ea_last_error(void) { return g_err; }
+
+void ea_fwd_tuning_default(ea_fwd_tuning* t) {
+  if (t == nullptr) return;
+  t->exp_mode = EA_EXP_HW;
+  t->rescale_log2 = 8.0f;
+  t->natural_order = 0;
+}
+
+ea_status ea_attn_fwd_tuned(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int Nq, int Nk, int Hq, int Hkv, int d, int causal,
+                            float scale, const ea_fwd_tuning* tuning, void* stream) {
+  if (!q || !k || !v || !o) return fail(EA_ERR_INVALID, "q, k, v and o must be non-null");
+  if (B <= 0 || Nq <= 0 || Nk <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0)
+    return fail(EA_ERR_INVALID, "B, Nq, Nk, Hq, Hkv and d must be positive");
+  if (Hq % Hkv) return fail(EA_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if (d != 64 && d != 128) return fail(EA_ERR_UNSUPPORTED, "head dim %d not supported (64 or 128)", d);
+  if (!finite_pos(scale)) return fail(EA_ERR_INVALID, "scale must be finite and positive");
+  if (causal != 0 && causal != 1) return fail(EA_ERR_INVALID, "causal must be 0 or 1");
+  if (ea_status st = check_tuning(tuning); st != EA_OK) return st;
+  if ((long long)B * Nq >= (1LL << 31) || (long long)B * Nk >= (1LL << 31))
+    return fail(EA_ERR_UNSUPPORTED, "B * N must be below 2^31");
+  const int n_mb = (Nq + ea::kFwdBlockM - 1) / ea::kFwdBlockM;
+  if ((long long)((B * (long long)Hq + 7) / 8) * 8 * n_mb >= (1LL << 31))
+    return fail(EA_ERR_UNSUPPORTED, "problem too large for one launch");
+  ea_fwd_tuning tt;
+  ea_fwd_tuning_default(&tt);
+  if (tuning) tt = *tuning;
+
+  ea::FwdArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.o = (uint16_t*)o;
+  a.lse = lse;
+  a.nseq = B;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.group = Hq / Hkv;
+  a.total_q = B * Nq;
+  a.n_mb = n_mb;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.tau = tt.rescale_log2;
+  a.natural = tt.natural_order;
+  return hip_status(ea::launch_fwd(a, d, causal != 0, false, tt.exp_mode, (hipStream_t)stream),
+                    "attention forward launch");
+}
+
+ea_status ea_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                      int Nq, int Nk, int Hq, int Hkv, int d, int causal, float scale,
+                      void* stream) {
+  return ea_attn_fwd_tuned(q, k, v, o, lse, B, Nq, Nk, Hq, Hkv, d, causal, scale, nullptr, stream);
+}
+
+ea_status ea_attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                             const int* cu_seqlens_q, const int* cu_seqlens_k, int num_seqs,
+                             int total_q, int total_k, int max_seqlen_q, int Hq, int Hkv, int d,
+                             int causal, float scale, const ea_fwd_tuning* tuning, void* stream) {
+  if (!q || !k || !v || !o || !cu_seqlens_q || !cu_seqlens_k)
+    return fail(EA_ERR_INVALID, "q, k, v, o and cu_seqlens must be non-null");
+  if (num_seqs <= 0 || total_q <= 0 || total_k <= 0 || max_seqlen_q <= 0 || Hq <= 0 || Hkv <= 0 ||
+      d <= 0)
+    return fail(EA_ERR_INVALID, "num_seqs, totals, max_seqlen_q, Hq, Hkv and d must be positive");
+  if (Hq % Hkv) return fail(EA_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if (d != 64 && d != 128) return fail(EA_ERR_UNSUPPORTED, "head dim %d not supported (64 or 128)", d);
+  if (!finite_pos(scale)) return fail(EA_ERR_INVALID, "scale must be finite and positive");
+  if (causal != 0 && causal != 1) return fail(EA_ERR_INVALID, "causal must be 0 or 1");
+  if (ea_status st = check_tuning(tuning); st != EA_OK) return st;
+  if (max_seqlen_q > total_q) return fail(EA_ERR_INVALID, "max_seqlen_q exceeds total_q");
+  const int n_mb = (max_seqlen_q + ea::kFwdBlockM - 1) / ea::kFwdBlockM;
+  if ((long long)((num_seqs * (long long)Hq + 7) / 8) * 8 * n_mb >= (1LL << 31))
+    return fail(EA_ERR_UNSUPPORTED, "problem too large for one launch");
+  ea_fwd_tuning tt;
+  ea_fwd_tuning_default(&tt);
+  if (tuning) tt = *tuning;
+
+  ea::FwdArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.o = (uint16_t*)o;
+  a.lse = lse;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.nseq = num_seqs;
+  a.Nq = 0;
+  a.Nk = 0;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.group = Hq / Hkv;
+  a.total_q = total_q;
+  a.n_mb = n_mb;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.tau = tt.rescale_log2;
+  a.natural = tt.natural_order;
+  return hip_status(ea::launch_fwd(a, d, causal != 0, true, tt.exp_mode, (hipStream_t)stream),
+                    "varlen attention forward launch");
+}
+
+ea_status ea_attn_fwd_mx8(const void* q8, const void* k8, const void* v8, const uint8_t* q_scale,
+                          const uint8_t* k_scale, const uint8_t* v_scale, void* o, float* lse,
+                          int B, int N, int Hq, int Hkv, int d, int causal, float scale,
+                          void* stream) {
+  if (!q8 || !k8 || !v8 || !q_scale || !k_scale || !v_scale || !o)
+    return fail(EA_ERR_INVALID, "tensor pointers must be non-null");
+  if (B <= 0 || N <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0)
+    return fail(EA_ERR_INVALID, "B, N, Hq, Hkv and d must be positive");
+  if (Hq % Hkv) return fail(EA_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if (d != 128) return fail(EA_ERR_UNSUPPORTED, "MX fp8 forward supports d = 128 only");
+  if (N % 32) return fail(EA_ERR_UNSUPPORTED, "MX fp8 forward needs N %% 32 == 0");
+  if (!finite_pos(scale)) return fail(EA_ERR_INVALID, "scale must be finite and positive");
+  if (causal != 0 && causal != 1) return fail(EA_ERR_INVALID, "causal must be 0 or 1");
+  if ((long long)B * N >= (1LL << 31)) return fail(EA_ERR_UNSUPPORTED, "B * N must be below 2^31");
+  ea::Mx8Args a{};
+  a.q = (const uint8_t*)q8;
+  a.k = (const uint8_t*)k8;
+  a.v = (const uint8_t*)v8;
+  a.qs = q_scale;
+  a.ks = k_scale;
+  a.vs = v_scale;
+  a.o = (uint16_t*)o;
+  a.lse = lse;
+  a.B = B;
+  a.N = N;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.group = Hq / Hkv;
+  a.n_mb = (N + ea::kFwdBlockM - 1) / ea::kFwdBlockM;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.tau = 8.0f;
+  return hip_status(ea::launch_fwd_mx8(a, causal != 0, (hipStream_t)stream), "MX fp8 forward launch");
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// paged decode
+// ---------------------------------------------------------------------------
+namespace {
+
+// Split length (tokens per workgroup). The split count is derived from the
+// maximum context so the grid is known without reading seq_lens on the host;
+// workgroups past a sequence's own length exit at once. Aim for at least two
+// workgroups per CU slot over the longest context, with splits of 256..4096
+// tokens (a heuristic from CU count and lengths; any choice gives the same
+// result up to rounding).
+int choose_split_len(int B, int Hkv, int max_seqlen, int page_size, int num_splits) {
+  // 32-token steps; 16 | page_size keeps every 16-token tile inside one page
+  (void)page_size;
+  const int unit = 32;
+  const int cus = 256;  // fixed so the workspace size does not depend on the device
+  if (num_splits > 0) {
+    int per = (max_seqlen + num_splits - 1) / num_splits;
+    per = ((per + unit - 1) / unit) * unit;
+    return per < unit ? unit : per;
+  }
+  long long pairs = (long long)B * Hkv;
+  long long target_wg = 4LL * cus;  // aim for a few workgroups per CU in total
+  long long splits = (target_wg + pairs - 1) / pairs;
+  if (splits < 1) splits = 1;
+  long long per = (max_seqlen + splits - 1) / splits;
+  if (per < 256) per = 256;
+  if (per > 4096) per = 4096;
+  per = ((per + unit - 1) / unit) * unit;
+  return (int)per;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ea_decode_workspace_size(int B, int Hq, int Hkv, int d, int max_seqlen, int page_size,
+                                int num_splits) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || max_seqlen < 0 || page_size <= 0 || num_splits < 0)
+    return 0;
+  const int split_len = choose_split_len(B, Hkv, max_seqlen, page_size, num_splits);
+  const int max_splits = max_seqlen > 0 ? (max_seqlen + split_len - 1) / split_len : 1;
+  return ea::decode_workspace_bytes(B, Hq, d, max_splits);
+}
+
+ea_status ea_attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                               const int* block_table, const int* seq_lens, void* o, float* lse,
+                               int B, int Hq, int Hkv, int d, int page_size, int num_pages,
+                               int max_pages_per_seq, float scale, int num_splits, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o)
+    return fail(EA_ERR_INVALID, "tensor pointers must be non-null");
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || page_size <= 0 || num_pages <= 0 ||
+      max_pages_per_seq <= 0)
+    return fail(EA_ERR_INVALID, "sizes must be positive");
+  if (Hq % Hkv) return fail(EA_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  const int group = Hq / Hkv;
+  if (d != 128) return fail(EA_ERR_UNSUPPORTED, "paged decode supports d = 128 only");
+  if (page_size % 16) return fail(EA_ERR_UNSUPPORTED, "page_size must be a multiple of 16");
+  if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16)
+    return fail(EA_ERR_UNSUPPORTED, "Hq / Hkv must be 1, 2, 4, 8 or 16");
+  if (!finite_pos(scale)) return fail(EA_ERR_INVALID, "scale must be finite and positive");
+  if (num_splits < 0) return fail(EA_ERR_INVALID, "num_splits must be >= 0");
+  if ((long long)max_pages_per_seq * page_size >= (1LL << 31))
+    return fail(EA_ERR_UNSUPPORTED, "max context too long");
+  if ((long long)num_pages * page_size * Hkv * d >= (1LL << 40))
+    return fail(EA_ERR_UNSUPPORTED, "KV pool too large");
+  const int max_seqlen = max_pages_per_seq * page_size;
+  const size_t need = ea_decode_workspace_size(B, Hq, Hkv, d, max_seqlen, page_size, num_splits);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(EA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  const int split_len = choose_split_len(B, Hkv, max_seqlen, page_size, num_splits);
+  ea::DecodeArgs a{};
+  a.q = (const uint16_t*)q;
+  a.kc = (const uint16_t*)k_cache;
+  a.vc = (const uint16_t*)v_cache;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.o = (uint16_t*)o;
+  a.lse = lse;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.group = group;
+  a.page_size = page_size;
+  a.max_pages = max_pages_per_seq;
+  a.num_pages = num_pages;
+  a.split_len = split_len;
+  a.max_splits = (max_seqlen + split_len - 1) / split_len;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  const size_t o_bytes = (size_t)B * Hq * a.max_splits * d * sizeof(float);
+  a.part_o = (float*)workspace;
+  a.part_lse = (float*)((char*)workspace + o_bytes);
+  return hip_status(ea::launch_decode(a, (hipStream_t)stream), "paged decode launch");
+}
+
+}  // extern "C"

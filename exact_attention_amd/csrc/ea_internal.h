@@ -1,0 +1,73 @@
+// Internal launcher interfaces between the C ABI (ea_api.cpp) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ea {
+
+// Forward (bf16). Dense inputs are BSHD, packed inputs THD with cu_seqlens.
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;          // may be null
+  const int* cu_q;     // packed sequences only
+  const int* cu_k;
+  int nseq;            // batch (dense) or number of packed sequences
+  int Nq, Nk;          // dense sequence lengths
+  int Hq, Hkv, group;  // group = Hq / Hkv
+  int total_q;         // packed: lse row stride per head
+  int n_mb;            // row blocks per sequence (dense) / upper bound (packed)
+  float scale_log2;    // softmax scale * log2(e)
+  float tau;           // lazy-rescale threshold in log2 units
+  int natural;         // 1: ascending row-block order
+};
+
+constexpr int kFwdBlockM = 128;  // query rows per workgroup (4 waves x 32)
+constexpr int kFwdBlockN = 64;   // keys per K/V tile
+
+// grid size for the forward (workgroups)
+int fwd_grid(const FwdArgs& a, bool varlen);
+hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, bool varlen, int exp_mode,
+                      hipStream_t s);
+
+// MX fp8 forward
+struct Mx8Args {
+  const uint8_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  const uint8_t* qs;
+  const uint8_t* ks;
+  const uint8_t* vs;
+  uint16_t* o;
+  float* lse;
+  int B, N, Hq, Hkv, group;
+  int n_mb;
+  float scale_log2;
+  float tau;
+};
+hipError_t launch_fwd_mx8(const Mx8Args& a, bool causal, hipStream_t s);
+
+// Paged split-KV decode
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint16_t* kc;
+  const uint16_t* vc;
+  const int* block_table;
+  const int* seq_lens;
+  uint16_t* o;
+  float* lse;
+  float* part_o;     // [B, Hkv, max_splits, group, d] fp32
+  float* part_lse;   // [B, Hkv, max_splits, group] fp32
+  int B, Hq, Hkv, group;
+  int page_size, max_pages;
+  int num_pages;     // pool size: page indices outside [0, num_pages) read as zeros
+  int split_len;     // tokens per split (multiple of 32 and of page_size)
+  int max_splits;
+  float scale_log2;
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+size_t decode_workspace_bytes(int B, int Hq, int d, int max_splits);
+
+}  // namespace ea

@@ -1,0 +1,172 @@
+/*
+ * ea.h -- C ABI of libexactattn.so, exact attention for AMD MI355X (gfx950).
+ *
+ * What is computed (cited by page title and section):
+ *   O = softmax(scale * Q K^T) V  and the per-row natural log-sum-exp
+ *   lse_i = log sum_j exp(scale * q_i . k_j), exactly (no approximation beyond
+ *   floating-point rounding order) -- "FlashAttention: not less compute, less
+ *   data movement", sections 01 (the formula), 02 (the online-softmax
+ *   recurrence the kernels use) and 03 (the forward keeps O and the row
+ *   log-sum-exp, never the N x N score matrix).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers allocated by the caller, who owns
+ *     them. The library allocates nothing and keeps no per-call state.
+ *   - bf16 tensors are raw IEEE bfloat16 bit patterns (uint16 storage).
+ *   - Dense Q/K/V/O are contiguous BSHD: element (b, n, h, c) lives at
+ *     ((b * N + n) * H + h) * d + c. Packed variable-length tensors are THD:
+ *     (t, h, c) at (t * H + h) * d + c.
+ *   - Grouped-query attention: Hq must be a multiple of Hkv; query head h reads
+ *     KV head h / (Hq / Hkv) (consecutive groups; "FlashAttention: not less
+ *     compute, less data movement", section 05 requires only divisibility).
+ *   - causal = 1 masks key j for query i when j > i + (Nk - Nq) (bottom-right
+ *     alignment; identical to j > i when Nq == Nk).
+ *   - A query row with no allowed key yields o = 0 and lse = -inf.
+ *   - stream is a hipStream_t (NULL = the default stream). Work is enqueued on
+ *     it; calls never synchronise. Device faults surface at the caller's next
+ *     synchronisation.
+ *   - Argument checks run on the host before any HIP call: on failure nothing
+ *     is launched, the status is returned and ea_last_error() describes it.
+ */
+#ifndef EXACT_ATTENTION_EA_H
+#define EXACT_ATTENTION_EA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  EA_OK = 0,
+  EA_ERR_INVALID = -1,      /* null pointer, non-positive size, Hq % Hkv, bad scale */
+  EA_ERR_UNSUPPORTED = -2,  /* valid but not built: head dim, page size, ... */
+  EA_ERR_HIP = -3,          /* a HIP launch failed */
+  EA_ERR_WORKSPACE = -4     /* caller's workspace too small */
+} ea_status;
+
+/* Softmax exponential used by the forward kernels.
+ *   EA_EXP_HW     the hardware v_exp_f32.
+ *   EA_EXP_POLY   range reduction 2^x = 2^floor(x) * 2^frac(x) with a cubic
+ *                 polynomial for 2^frac on [0,1) and the integer part added to
+ *                 the exponent field; inputs clamped at -127
+ *                 ("FlashAttention-4: algorithm-pipeline co-design for
+ *                 Blackwell", hybrid exponent section; "FlashAttention4 close
+ *                 reading", section 3.1.3).
+ *   EA_EXP_HYBRID a fixed fraction of each score tile takes the polynomial,
+ *                 the rest the hardware unit (same sections). */
+enum { EA_EXP_HW = 0, EA_EXP_POLY = 1, EA_EXP_HYBRID = 2 };
+
+/* Forward tuning knobs (results differ only by rounding). */
+typedef struct {
+  int exp_mode;            /* EA_EXP_*; default EA_EXP_HW */
+  float rescale_log2;      /* lazy rescale: rescale the accumulator only when the
+                              running row max grows by more than this many
+                              powers of two ("FlashAttention-4: ... co-design",
+                              conditional softmax rescaling section; reading: a
+                              factor of 256, i.e. 8.0). 0 = rescale on every
+                              increase. Must be in [0, 16]. Default 8.0. */
+  int natural_order;       /* 0 (default): causal tiles heaviest first; 1: tiles
+                              in ascending row-block order. */
+} ea_fwd_tuning;
+
+/* Default tuning values. */
+void ea_fwd_tuning_default(ea_fwd_tuning* t);
+
+/*
+ * ea_attn_fwd -- fused exact attention forward, bf16 in, bf16 O + fp32 LSE out.
+ *   q   [B, Nq, Hq, d] bf16        k, v [B, Nk, Hkv, d] bf16
+ *   o   [B, Nq, Hq, d] bf16 (written)
+ *   lse [B, Hq, Nq] fp32 (written; natural log, scale included), or NULL
+ *   d in {64, 128}; scale finite and > 0 (usually 1/sqrt(d)).
+ * One pass: each row block of queries streams over K/V tiles with the online
+ * softmax, so the N x N matrix never reaches HBM ("FlashAttention: not less
+ * compute, less data movement", sections 02-03).
+ */
+ea_status ea_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int Nq, int Nk, int Hq, int Hkv, int d, int causal,
+                      float scale, void* stream);
+
+/* ea_attn_fwd with explicit tuning (NULL = defaults). */
+ea_status ea_attn_fwd_tuned(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int Nq, int Nk, int Hq, int Hkv, int d, int causal,
+                            float scale, const ea_fwd_tuning* tuning, void* stream);
+
+/*
+ * ea_attn_fwd_varlen -- packed variable-length sequences (THD layout).
+ *   q [total_q, Hq, d], k/v [total_k, Hkv, d], o [total_q, Hq, d] bf16
+ *   lse [Hq, total_q] fp32 or NULL
+ *   cu_seqlens_q / cu_seqlens_k: device int32 [num_seqs + 1], nondecreasing,
+ *   starting at 0 and ending at total_q / total_k; sequence s owns rows
+ *   [cu[s], cu[s+1]); positions and the causal mask are local to each
+ *   sequence. max_seqlen_q must bound every query length (it sizes the grid).
+ *   Rows outside every sequence are neither read nor written.
+ * Packing without padding follows the unpadded-batch advice in "FlashAttention:
+ * not less compute, less data movement", section 05.
+ */
+ea_status ea_attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                             const int* cu_seqlens_q, const int* cu_seqlens_k, int num_seqs,
+                             int total_q, int total_k, int max_seqlen_q, int Hq, int Hkv, int d,
+                             int causal, float scale, const ea_fwd_tuning* tuning, void* stream);
+
+/*
+ * ea_attn_fwd_mx8 -- forward with MX-scaled FP8 (OCP e4m3) inputs.
+ *   q8, k8, v8     [B, N, H*, d] e4m3 codes (uint8)
+ *   q_scale, k_scale [B, N, H*, d/32] e8m0 scale bytes (2^(s-127)), one per 32
+ *                  consecutive elements along d;
+ *   v_scale        [B, N/32, Hkv, d] e8m0, one per 32 consecutive keys
+ *                  (the contraction dimension of P V) -- "Low-precision
+ *                  FlashAttention-4: end-to-end block-scaled attention for
+ *                  Blackwell", section 2.1.
+ *   P is re-quantised to e4m3 before the P V product (same page, 2.1.3).
+ *   o [B, N, Hq, d] bf16, lse [B, Hq, N] fp32 or NULL. N % 32 == 0, d == 128.
+ */
+ea_status ea_attn_fwd_mx8(const void* q8, const void* k8, const void* v8,
+                          const uint8_t* q_scale, const uint8_t* k_scale, const uint8_t* v_scale,
+                          void* o, float* lse, int B, int N, int Hq, int Hkv, int d, int causal,
+                          float scale, void* stream);
+
+/*
+ * Paged split-KV decode ("Faster, more flexible FlashAttention-4 for LLM
+ * inference": PR 1999/2104 for KV pages of any size, PR 1940 for splitting the
+ * KV sequence over workgroups plus a combine kernel, PR 1993 for one query tile
+ * per workgroup, PR 2186 for packing the query heads of one KV head together).
+ *
+ *   q      [B, Hq, d] bf16 (one query token per sequence)
+ *   k_cache, v_cache [num_pages, page_size, Hkv, d] bf16
+ *   block_table [B, max_pages_per_seq] int32: token t of sequence b lives in
+ *          page block_table[b, t / page_size], slot t % page_size; entries past
+ *          the sequence's last page are never read; an entry outside
+ *          [0, num_pages) reads as zeros (no fault).
+ *   seq_lens [B] int32, each in [0, max_pages_per_seq * page_size] (larger
+ *          values are clamped to that capacity)
+ *   o      [B, Hq, d] bf16 (written); lse [B, Hq] fp32 or NULL
+ *   page_size a multiple of 16; d == 128; Hq / Hkv in {1, 2, 4, 8, 16}.
+ *   num_splits: 0 = choose from the CU count and lengths; otherwise the number
+ *          of KV splits per sequence (>= 1).
+ *   workspace: device memory of at least ea_decode_workspace_size(B, Hq, Hkv,
+ *          d, max_pages_per_seq * page_size, page_size, num_splits) bytes,
+ *          owned by the caller; contents on entry are ignored.
+ * The decode attends to all seq_lens[b] tokens (no mask).
+ */
+size_t ea_decode_workspace_size(int B, int Hq, int Hkv, int d, int max_seqlen, int page_size,
+                                int num_splits);
+
+ea_status ea_attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                               const int* block_table, const int* seq_lens, void* o, float* lse,
+                               int B, int Hq, int Hkv, int d, int page_size, int num_pages,
+                               int max_pages_per_seq, float scale, int num_splits,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable description of the last failure on the calling thread
+ * (thread-local; valid until the next library call on that thread). */
+const char* ea_last_error(void);
+
+/* Library ABI version (this header: 1). */
+int ea_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EXACT_ATTENTION_EA_H */

@@ -1,0 +1,29 @@
+/*
+ * ea_test.h -- test-only entry points of libexactattn.so.
+ *
+ * They run the library's own device functions on caller data so unit tests can
+ * check them in isolation. Not part of the attention API; no stability promise.
+ */
+#ifndef EXACT_ATTENTION_EA_TEST_H
+#define EXACT_ATTENTION_EA_TEST_H
+
+#include <stddef.h>
+
+#include "ea.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * ea_test_exp2 -- y[i] = 2^x[i] with the forward kernels' exponential:
+ *   mode EA_EXP_HW (v_exp_f32) or EA_EXP_POLY (range reduction + cubic, inputs
+ *   clamped at -127; "FlashAttention4 close reading", section 3.1.3).
+ *   x, y: device float arrays of n elements (n >= 0). stream: hipStream_t.
+ */
+ea_status ea_test_exp2(const float* x, float* y, int n, int mode, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EXACT_ATTENTION_EA_TEST_H */

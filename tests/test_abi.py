@@ -1,0 +1,112 @@
+"""C ABI checks that need no GPU: the library builds, loads and exports every
+function include/ea.h declares, and invalid arguments come back as error codes
+from the host-side checks (no HIP call is reached)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from _helpers import ROOT
+
+HEADERS = [os.path.join(ROOT, "include", f) for f in ("ea.h", "ea_test.h")]
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import exact_attention_amd as ea
+    if not os.path.exists(ea.LIB_PATH):
+        from exact_attention_amd import build
+        build.build()
+    return ea.lib()
+
+
+def declared_functions():
+    text = "".join(open(h).read() for h in HEADERS)
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ea_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("ea_attn_fwd", "ea_attn_fwd_varlen", "ea_attn_fwd_mx8", "ea_attn_decode_paged",
+              "ea_decode_workspace_size", "ea_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} missing from libexactattn.so"
+    assert lib.ea_version() == 1
+
+
+def _err(lib):
+    return lib.ea_last_error().decode()
+
+
+P = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def test_fwd_argument_errors(lib):
+    f = lib.ea_attn_fwd
+    assert f(None, P, P, P, None, 1, 8, 8, 2, 2, 128, 0, 0.1, None) == -1 and "non-null" in _err(lib)
+    assert f(P, P, P, P, None, 0, 8, 8, 2, 2, 128, 0, 0.1, None) == -1
+    assert f(P, P, P, P, None, 1, 8, 8, 3, 2, 128, 0, 0.1, None) == -1 and "multiple" in _err(lib)
+    assert f(P, P, P, P, None, 1, 8, 8, 2, 2, 96, 0, 0.1, None) == -2
+    assert f(P, P, P, P, None, 1, 8, 8, 2, 2, 128, 0, float("nan"), None) == -1
+    assert f(P, P, P, P, None, 1, 8, 8, 2, 2, 128, 0, -1.0, None) == -1
+    assert f(P, P, P, P, None, 1, 8, 8, 2, 2, 128, 2, 0.1, None) == -1
+
+
+def test_tuning_errors(lib):
+    import exact_attention_amd as ea
+    t = ea.tuning(exp_mode=7)
+    assert lib.ea_attn_fwd_tuned(P, P, P, P, None, 1, 8, 8, 2, 2, 128, 0, 0.1, ctypes.byref(t), None) == -1
+    t = ea.tuning(rescale_log2=-1.0)
+    assert lib.ea_attn_fwd_tuned(P, P, P, P, None, 1, 8, 8, 2, 2, 128, 0, 0.1, ctypes.byref(t), None) == -1
+    d = ea.default_tuning()
+    assert d.exp_mode == 0 and d.rescale_log2 == 8.0 and d.natural_order == 0
+
+
+def test_varlen_argument_errors(lib):
+    f = lib.ea_attn_fwd_varlen
+    assert f(P, P, P, P, None, None, P, 2, 10, 10, 5, 2, 2, 128, 1, 0.1, None, None) == -1
+    assert f(P, P, P, P, None, P, P, 2, 10, 10, 50, 2, 2, 128, 1, 0.1, None, None) == -1  # max > total
+    assert f(P, P, P, P, None, P, P, 2, 10, 10, 5, 2, 2, 80, 1, 0.1, None, None) == -2
+
+
+def test_mx8_argument_errors(lib):
+    f = lib.ea_attn_fwd_mx8
+    assert f(P, P, P, P, P, None, P, None, 1, 64, 2, 2, 128, 1, 0.1, None) == -1
+    assert f(P, P, P, P, P, P, P, None, 1, 48, 2, 2, 128, 1, 0.1, None) == -2   # N % 32
+    assert f(P, P, P, P, P, P, P, None, 1, 64, 2, 2, 64, 1, 0.1, None) == -2    # d
+
+
+def test_decode_argument_errors(lib):
+    f = lib.ea_attn_decode_paged
+    ws = lib.ea_decode_workspace_size(4, 8, 2, 128, 1024, 16, 0)
+    assert ws > 0
+    ok_args = dict(B=4, Hq=8, Hkv=2, d=128, ps=16, P=100, mp=64)
+
+    def call(q=P, B=4, Hq=8, Hkv=2, d=128, ps=16, npages=100, mp=64, scale=0.1, ns=0, wsp=P, wsb=ws):
+        return f(q, P, P, P, P, P, None, B, Hq, Hkv, d, ps, npages, mp, scale, ns, wsp, wsb, None)
+
+    assert call(q=None) == -1
+    assert call(Hq=6, Hkv=4) == -1
+    assert call(d=64) == -2
+    assert call(ps=8) == -2
+    assert call(Hq=6, Hkv=2) == -2          # group 3 not built
+    assert call(scale=0.0) == -1
+    assert call(ns=-1) == -1
+    assert call(wsb=ws - 1) == -4 and "workspace" in _err(lib)
+    assert call(wsp=None) == -4
+    # more splits need more workspace
+    assert lib.ea_decode_workspace_size(4, 8, 2, 128, 1024, 16, 8) >= lib.ea_decode_workspace_size(4, 8, 2, 128, 1024, 16, 1)
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    import exact_attention_amd as ea
+    q = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ea.attn_fwd(q, q, q)

@@ -293,9 +293,82 @@ def decode_lengths(B: int, lo: int, hi: int, seed: int) -> np.ndarray:
 
 def paged_decode() -> Paged:
     """Workload 3: B=64, Hq=32, Hkv=8, d=128, context ~ U{512..32768}, page 16,
-    block table = seeded permutation of the page pool; max_pages = 2048."""
+    block table = seeded permutation of the page pool; max_pages = 2048.
+    Host-generated (slow for the full pool: prefer paged_decode_device)."""
     L = decode_lengths(64, 512, 32768, seed=1003)
     return paged(64, 32, 8, 128, 16, L, seed=1003, max_pages=32768 // 16)
+
+
+def normal_bf16_device(seed: int, stream: int, shape, device, chunk: int = 1 << 28):
+    """iid N(0,1) draws rounded (RNE) to bf16 on a GPU: torch's seeded
+    Philox generator on ``device``, drawn in chunks of ``chunk`` elements
+    (chunk c seeded with (seed, stream, c)). Returns a torch bf16 tensor."""
+    import torch
+    n = int(np.prod(shape))
+    out = torch.empty(n, dtype=torch.bfloat16, device=device)
+    for c, lo in enumerate(range(0, n, chunk)):
+        hi = min(n, lo + chunk)
+        g = torch.Generator(device=device)
+        g.manual_seed((seed * 1_000_003 + stream * 10_007 + c) & 0x7FFFFFFFFFFFFFFF)
+        out[lo:hi] = torch.randn(hi - lo, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+    return out.view(*shape)
+
+
+def paged_decode_device(device="cuda", seed: int = 1003) -> Paged:
+    """Workload 3 with the KV pool drawn on the GPU (same lengths, block table,
+    q and NaN-poisoned tails as the host recipe; cache values from
+    ``normal_bf16_device``). k_cache / v_cache are torch bf16 tensors on
+    ``device``; q, block_table and seq_lens stay numpy."""
+    import torch
+    B, Hq, Hkv, d, ps = 64, 32, 8, 128, 16
+    L = decode_lengths(B, 512, 32768, seed=seed)
+    npages_seq = (L + ps - 1) // ps
+    P = int(npages_seq.sum())
+    rng = meta_rng(seed)
+    phys = rng.permutation(P).astype(np.int32)
+    max_pages = 32768 // ps
+    bt = np.full((B, max_pages), -1, dtype=np.int32)
+    off = 0
+    for b in range(B):
+        n = int(npages_seq[b])
+        bt[b, :n] = phys[off:off + n]
+        off += n
+    q = normal_bf16_bits(seed, STREAM_Q, (B, Hq, d))
+    kc = normal_bf16_device(seed, STREAM_KC, (P, ps, Hkv, d), device)
+    vc = normal_bf16_device(seed, STREAM_VC, (P, ps, Hkv, d), device)
+    nan = torch.tensor(float("nan"), dtype=torch.bfloat16, device=device)
+    for b in range(B):
+        n = int(npages_seq[b])
+        used = int(L[b] - (n - 1) * ps)
+        if used < ps:
+            pg = int(bt[b, n - 1])
+            kc[pg, used:] = nan
+            vc[pg, used:] = nan
+    return Paged(q, kc, vc, bt, L.astype(np.int32), ps, float(1.0 / np.sqrt(d)))
+
+
+def host_subpool(pg: Paged, batches):
+    """Copy the pages of the listed sequences of a device-resident pool to the
+    host (bf16 bits) with a remapped block table, for oracle checks. Returns a
+    host Paged holding only those sequences (in the given order)."""
+    import torch
+    ps = pg.page_size
+    rows, tables, lens, qs = [], [], [], []
+    off = 0
+    mp = pg.block_table.shape[1]
+    for b in batches:
+        n = -(-int(pg.seq_lens[b]) // ps)
+        idx = torch.from_numpy(pg.block_table[b, :n].astype(np.int64)).to(pg.k_cache.device)
+        rows.append((pg.k_cache.index_select(0, idx), pg.v_cache.index_select(0, idx)))
+        t = np.full(mp, -1, np.int32)
+        t[:n] = np.arange(off, off + n)
+        tables.append(t)
+        lens.append(pg.seq_lens[b])
+        qs.append(pg.q[b])
+        off += n
+    kc = torch.cat([r[0] for r in rows]).view(torch.int16).cpu().numpy().view(np.uint16)
+    vc = torch.cat([r[1] for r in rows]).view(torch.int16).cpu().numpy().view(np.uint16)
+    return Paged(np.stack(qs), kc, vc, np.stack(tables), np.array(lens, np.int32), ps, pg.scale)
 
 
 @dataclass
