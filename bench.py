@@ -48,7 +48,22 @@ def parse():
                    help="time one kernel family only (profiling runs)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle time budget per leg")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB device-to-device copy (calibrates HBM byte counters)")
     return p.parse_args()
+
+
+def copy_calibration():
+    """A plain copy of 1 GiB (reads 1 GiB, writes 1 GiB), repeated 3 times, so
+    rocprofv3 FETCH_SIZE / WRITE_SIZE per dispatch can be scaled to bytes."""
+    import torch
+    x = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    x.fill_(1)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": 1 << 30, "calls": 3}))
 
 
 def prefill_flops(B, H, N, d):
@@ -111,6 +126,9 @@ def _f64(bits):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the library has no "
               "multi-GPU path: the per-GPU kernels are each GPU's share.", file=sys.stderr)

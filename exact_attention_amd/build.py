@@ -24,6 +24,8 @@ COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # packed fp32 VALU ops are kept out of the generated code on purpose
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # IEEE mode off: min/max need no NaN quieting (the kernels use -inf, never NaN)
+    "-mno-amdgpu-ieee", "-fno-honor-nans",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

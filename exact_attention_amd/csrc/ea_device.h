@@ -106,21 +106,41 @@ __device__ __forceinline__ float add_bf16x2(uint32_t packed, float acc) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS tiles: rows of D bf16, stored in 16-byte chunks permuted per row so that
-// (a) 8 consecutive rows read at the same chunk (MFMA A/B operand reads) and
-// (b) 4 consecutive rows x 2 adjacent chunks (transposed reads) fall on
-// distinct bank groups. chunk position = chunk ^ swz(row).
+// LDS tiles: rows of D bf16, stored in 16-byte chunks permuted per row:
+// chunk position = chunk ^ swz(row). For D = 128 (16 chunks per row)
+// swz(row) = ((row & 3) << 2) | ((row >> 2) & 3), which is a bijection on
+// row % 16, so
+//  (a) 16 consecutive rows read at one chunk (MFMA A/B operand reads) hit 16
+//      distinct 16-byte bank groups, and
+//  (b) 4 consecutive rows x 4 consecutive chunks (32 lanes of a transposed
+//      read) also hit 16 distinct bank groups: the row picks bits 2-3 of the
+//      position, the chunk bits 0-1.
+// swz depends on row % 16 only, so moving 16 rows (or 32) is a constant
+// address offset. D = 64 rows have 8 chunks: swz(row) = ((row & 3) << 1) |
+// ((row >> 2) & 1).
 // ---------------------------------------------------------------------------
 template <int D>
 __device__ __forceinline__ int swz(int row) {
-  int s = ((row & 3) << 1) | ((row >> 2) & 1);
-  if constexpr (D >= 128) s |= ((row >> 3) & 1) << 3;
-  return s;
+  if constexpr (D >= 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  return ((row & 3) << 1) | ((row >> 2) & 1);
 }
 // element offset (in bf16 units) of (row, col) in a swizzled tile
 template <int D>
 __device__ __forceinline__ int tile_off(int row, int col) {
   return row * D + (((col >> 3) ^ swz<D>(row)) << 3) + (col & 7);
+}
+
+// Workgroup-uniform integer pinned to a scalar register (the compiler cannot
+// always prove uniformity through divisions done on the vector unit).
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Buffer resource over [base, base + nbytes) (raw, stride 0): loads at offsets
+// >= nbytes return zeros. The range check covers the VGPR offset only.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, 0x00020000);
+}
+__device__ __forceinline__ i32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
 }
 
 __device__ __forceinline__ i16x4 ds_read_tr16(const EA_LDS uint16_t* p) {

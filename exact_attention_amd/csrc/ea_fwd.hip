@@ -47,12 +47,13 @@ __device__ __forceinline__ float softmax_exp2(float x, int i) {
   }
 }
 
-template <int D, bool CAUSAL, bool VARLEN, int EXPMODE>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
-  constexpr int BM = kFwdBlockM, BN = kFwdBlockN;
+template <int D, bool CAUSAL, bool VARLEN, int EXPMODE, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
+  constexpr int BM = 32 * NW, BN = kFwdBlockN;
+  constexpr int NT = 64 * NW;              // threads per workgroup
   constexpr int KCH = D / 8;               // 16-byte chunks per row
   constexpr int TILE = BN * D;             // bf16 elements per K or V tile
-  constexpr int CPT = BN * KCH / 256;      // chunks per thread per tile
+  constexpr int CPT = BN * KCH / NT;       // chunks per thread per tile
   constexpr int NDT = D / 32;              // 32-wide d tiles of O^T
   __shared__ __attribute__((aligned(16))) uint16_t smem_raw[2 * 2 * TILE];
   EA_LDS uint16_t* sm = (EA_LDS uint16_t*)smem_raw;
@@ -96,13 +97,20 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
     k0 = seq * a.Nk;
     lk = a.Nk;
   }
-  const int hk = h / a.group;
+  seq = uniform(seq);
+  h = uniform(h);
+  mb = uniform(mb);
+  q0 = uniform(q0);
+  lq = uniform(lq);
+  k0 = uniform(k0);
+  lk = uniform(lk);
+  const int hk = uniform(h / a.group);
   const int off = lk - lq;  // bottom-right causal alignment
   const int row_lo = mb * BM;
   int nkeys = lk;
   if constexpr (CAUSAL) nkeys = min(lk, row_lo + BM + off);
   if (nkeys < 0) nkeys = 0;
-  const int nkb = (nkeys + BN - 1) / BN;
+  const int nkb = uniform((nkeys + BN - 1) / BN);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, hh = lane >> 5, c = lane & 31;
@@ -124,22 +132,31 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   }
 
   // ---------------- K/V tile staging (global -> VGPR -> swizzled LDS)
+  // Buffer loads: the resource of tile kb starts at its first row and ends
+  // after the sequence's last valid row, so rows past the end read as zeros
+  // with no branch, and the per-lane byte offsets are loop-invariant.
   const uint16_t* kg_base = a.k + (size_t)k0 * kstride + (size_t)hk * D;
   const uint16_t* vg_base = a.v + (size_t)k0 * kstride + (size_t)hk * D;
+  uint32_t g_off[CPT];
+  int s_off[CPT];
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    const int ci = tid + NT * u;
+    const int row = ci / KCH, ch = ci % KCH;
+    g_off[u] = (uint32_t)((row * (int)kstride + ch * 8) * 2);
+    s_off[u] = row * D + ((ch ^ swz<D>(row)) << 3);
+  }
   i32x4 rk[CPT], rv[CPT];
   auto gload = [&](int kb) {
+    const int rows = min(lk - kb * BN, BN);
+    const uint32_t nrec = (uint32_t)((rows - 1) * (int)kstride * 2 + D * 2);
+    const size_t t0 = (size_t)kb * BN * kstride;
+    const __amdgpu_buffer_rsrc_t rsk = make_rsrc(kg_base + t0, nrec);
+    const __amdgpu_buffer_rsrc_t rsv = make_rsrc(vg_base + t0, nrec);
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      const int ci = tid + 256 * u;
-      const int row = ci / KCH, ch = ci % KCH;
-      const int key = kb * BN + row;
-      if (key < lk) {
-        rk[u] = *(const i32x4*)(kg_base + (size_t)key * kstride + ch * 8);
-        rv[u] = *(const i32x4*)(vg_base + (size_t)key * kstride + ch * 8);
-      } else {
-        rk[u] = i32x4{0, 0, 0, 0};  // rows past the end: zeros (never NaN)
-        rv[u] = i32x4{0, 0, 0, 0};
-      }
+      rk[u] = buffer_load16(rsk, g_off[u]);
+      rv[u] = buffer_load16(rsv, g_off[u]);
     }
   };
   auto sstore = [&](int buf) {
@@ -147,11 +164,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
     EA_LDS uint16_t* vs = ks + TILE;
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      const int ci = tid + 256 * u;
-      const int row = ci / KCH, ch = ci % KCH;
-      const int o = row * D + ((ch ^ swz<D>(row)) << 3);
-      lds_store<i32x4>(ks + o, rk[u]);
-      lds_store<i32x4>(vs + o, rv[u]);
+      lds_store<i32x4>(ks + s_off[u], rk[u]);
+      lds_store<i32x4>(vs + s_off[u], rv[u]);
     }
   };
 
@@ -165,104 +179,122 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
     gload(0);
     sstore(0);
   }
+  // nothing outstanding when the loop starts (Q and tile 0 have landed)
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // transposed-read lane geometry (see ea_device.h for the instruction's layout)
+  // loop-invariant LDS element offsets of this lane's operand reads:
+  //   K (A of S^T): rows c and c + 32 (+32 rows = +32*D), chunk 2*kk + hh
+  //   V^T (A of O^T, transposed reads): rows 16*st + 8*r + tr_row (+16 rows =
+  //   +16*D), columns 32*dt + tr_col
+  int k_off[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) k_off[kk] = tile_off<D>(c, 16 * kk + 8 * hh);
   const int tr_row = 4 * hh + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  int v_off[NDT][2];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    v_off[dt][0] = tile_off<D>(tr_row, 32 * dt + tr_col);
+    v_off[dt][1] = tile_off<D>(tr_row + 8, 32 * dt + tr_col);
+  }
   const int wave_last_q = row_lo + w * 32 + 31;
+  const int wave_first_q = row_lo + w * 32;
 
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int cur = kb & 1;
-    if (kb + 1 < nkb) gload(kb + 1);
-    const EA_LDS uint16_t* ks = sm + cur * 2 * TILE;
+  auto compute = [&](int kb) {
+    const EA_LDS uint16_t* ks = sm + (kb & 1) * 2 * TILE;
     const EA_LDS uint16_t* vs = ks + TILE;
     const int kbase = kb * BN;
-    bool active = true;
-    if constexpr (CAUSAL) active = kbase <= wave_last_q + off;
-    if (active) {
-      // ---- S^T = K Q^T (two 32-key tiles)
-      f32x16 s0 = f32x16{}, s1 = f32x16{};
+    if (CAUSAL && kbase > wave_last_q + off) return;  // wave-uniform: fully masked
+    // ---- S^T = K Q^T (two 32-key tiles)
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const bf16x8 ka0 = lds_load<bf16x8>(ks + tile_off<D>(c, 16 * kk + 8 * hh));
-        const bf16x8 ka1 = lds_load<bf16x8>(ks + tile_off<D>(32 + c, 16 * kk + 8 * hh));
-        s0 = mfma32x32x16(ka0, qf[kk], s0);
-        s1 = mfma32x32x16(ka1, qf[kk], s1);
-      }
-      // ---- mask: keys past the sequence end, and above the causal diagonal
-      bool need_mask = kbase + BN > lk;
-      if constexpr (CAUSAL) need_mask = need_mask || (kbase + BN - 1 > row_lo + w * 32 + off);
-      if (need_mask) {
-        int lim = lk;
-        if constexpr (CAUSAL) lim = min(lk, qi + off + 1);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kbase + 8 * (i >> 2) + 4 * hh + (i & 3);
-          if (key >= lim) s0[i] = kNegInf;
-          if (key + 32 >= lim) s1[i] = kNegInf;
-        }
-      }
-      // ---- row max (raw scores; scale > 0 commutes with max)
-      float mx = kNegInf;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, __builtin_fmaxf(s0[i], s1[i]));
-      mx = max_with_partner32(mx);
-      const float m_new = __builtin_fmaxf(m_run, mx * sl);
-      // ---- lazy rescale, wave-uniform
-      if (__ballot(m_new > m_run + a.tau)) {
-        const float alpha = (m_run == kNegInf) ? 0.f : exp2_hw(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
-        m_run = m_new;
-      }
-      const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
-      // ---- P = 2^(s*scale*log2e - m) in fp32; the row sum is taken before the
-      //      bf16 rounding (keeps the log-sum-exp accurate on short rows)
-      float p0[16], p1[16];
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const bf16x8 ka0 = lds_load<bf16x8>(ks + k_off[kk]);
+      const bf16x8 ka1 = lds_load<bf16x8>(ks + k_off[kk] + 32 * D);
+      s0 = mfma32x32x16(ka0, qf[kk], s0);
+      s1 = mfma32x32x16(ka1, qf[kk], s1);
+    }
+    __builtin_amdgcn_s_setprio(0);
+    // ---- mask: keys past the sequence end, and above the causal diagonal
+    bool need_mask = kbase + BN > lk;
+    if constexpr (CAUSAL) need_mask = need_mask || (kbase + BN - 1 > wave_first_q + off);
+    if (need_mask) {
+      int lim = lk;
+      if constexpr (CAUSAL) lim = min(lk, qi + off + 1);
+      const int rel = lim - kbase - 4 * hh;  // element i is valid iff its key offset < rel
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        p0[i] = softmax_exp2<D, EXPMODE>(__builtin_fmaf(s0[i], sl, neg_m), i);
-        p1[i] = softmax_exp2<D, EXPMODE>(__builtin_fmaf(s1[i], sl, neg_m), i);
-      }
-      float ls0 = 0.f, ls1 = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        ls0 += p0[i];
-        ls1 += p1[i];
-      }
-      l_run += ls0 + ls1;
-      uint32_t pk[16];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pk[i] = pack_bf16x2(p0[2 * i], p0[2 * i + 1]);
-        pk[8 + i] = pack_bf16x2(p1[2 * i], p1[2 * i + 1]);
-      }
-      bf16x8 pb[4];
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        i32x4 t = {(int)pk[4 * st], (int)pk[4 * st + 1], (int)pk[4 * st + 2], (int)pk[4 * st + 3]};
-        pb[st] = __builtin_bit_cast(bf16x8, t);
-      }
-      // ---- O^T += V^T P^T
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          const int r0 = 16 * st + tr_row;
-          const int col = 32 * dt + tr_col;
-          const i16x4 lo = ds_read_tr16(vs + tile_off<D>(r0, col));
-          const i16x4 hi = ds_read_tr16(vs + tile_off<D>(r0 + 8, col));
-          i32x4 t = {__builtin_bit_cast(i32x2, lo)[0], __builtin_bit_cast(i32x2, lo)[1],
-                     __builtin_bit_cast(i32x2, hi)[0], __builtin_bit_cast(i32x2, hi)[1]};
-          oacc[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, t), pb[st], oacc[dt]);
-        }
+        const int ko = 8 * (i >> 2) + (i & 3);
+        s0[i] = (ko < rel) ? s0[i] : kNegInf;
+        s1[i] = (ko + 32 < rel) ? s1[i] : kNegInf;
       }
     }
-    if (kb + 1 < nkb) sstore(cur ^ 1);
+    // ---- row max (raw scores; scale > 0 commutes with max)
+    float mx = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, __builtin_fmaxf(s0[i], s1[i]));
+    mx = max_with_partner32(mx);
+    const float m_new = __builtin_fmaxf(m_run, mx * sl);
+    // ---- lazy rescale, wave-uniform
+    if (__ballot(m_new > m_run + a.tau)) {
+      const float alpha = (m_run == kNegInf) ? 0.f : exp2_hw(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+      m_run = m_new;
+    }
+    const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
+    // ---- P = 2^(s*scale*log2e - m) in fp32; the row sum is taken before the
+    //      bf16 rounding (keeps the log-sum-exp accurate on short rows)
+    float p0[16], p1[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      p0[i] = softmax_exp2<D, EXPMODE>(__builtin_fmaf(s0[i], sl, neg_m), i);
+      p1[i] = softmax_exp2<D, EXPMODE>(__builtin_fmaf(s1[i], sl, neg_m), i);
+    }
+    float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      ls0 += p0[i];
+      ls1 += p1[i];
+    }
+    l_run += ls0 + ls1;
+    bf16x8 pb[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const float* src = (st < 2) ? p0 : p1;
+      const int base = 8 * (st & 1);
+      i32x4 t = {(int)pack_bf16x2(src[base + 0], src[base + 1]), (int)pack_bf16x2(src[base + 2], src[base + 3]),
+                 (int)pack_bf16x2(src[base + 4], src[base + 5]), (int)pack_bf16x2(src[base + 6], src[base + 7])};
+      pb[st] = __builtin_bit_cast(bf16x8, t);
+    }
+    // ---- O^T += V^T P^T
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const i16x4 lo = ds_read_tr16(vs + v_off[dt][0] + 16 * st * D);
+        const i16x4 hi = ds_read_tr16(vs + v_off[dt][1] + 16 * st * D);
+        i32x4 t = {__builtin_bit_cast(i32x2, lo)[0], __builtin_bit_cast(i32x2, lo)[1],
+                   __builtin_bit_cast(i32x2, hi)[0], __builtin_bit_cast(i32x2, hi)[1]};
+        oacc[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, t), pb[st], oacc[dt]);
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // main loop: prefetch tile kb+1 into VGPRs, compute tile kb, park kb+1 in the
+  // other LDS buffer; one barrier per tile. The last tile is peeled.
+  for (int kb = 0; kb + 1 < nkb; ++kb) {
+    gload(kb + 1);
+    compute(kb);
+    sstore((kb + 1) & 1);
     __syncthreads();
   }
+  if (nkb > 0) compute(nkb - 1);
 
   // ---------------- epilogue: O = acc / l (bf16), lse = ln2 * (m + log2 l)
   const float l_tot = sum_with_partner32(l_run);
@@ -303,7 +335,8 @@ int fwd_grid(const FwdArgs& a, bool varlen) {
 template <int D, bool CAUSAL, bool VARLEN, int EXPMODE>
 static hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
   const int grid = fwd_grid(a, VARLEN);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, VARLEN, EXPMODE>), dim3(grid), dim3(256), 0, s, a);
+  constexpr int NW = kFwdBlockM / 32;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, VARLEN, EXPMODE, NW>), dim3(grid), dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
 
