@@ -3,15 +3,18 @@
 One step = one pass of the whole path over one batch of synthetic input:
   * the fused causal prefill forward at B=4, H=16, N=8192, d=128 (bf16),
   * the paged split-KV decode at B=64, Hq=32, Hkv=8, d=128, contexts
-    U{512..32768}, page 16 (bf16), including its combine kernel.
+    U{512..32768}, page 16 (bf16), including its combine kernel,
+  * the MX fp8 causal prefill forward at B=2, H=16, N=16384, d=128 (e4m3
+    inputs with e8m0 block scales, P re-quantised to e4m3).
 Inputs are resident in HBM before timing starts. Each kernel launch is timed
 with HIP events recorded on the stream the kernels run on; the step time is the
 wall clock over K steps between device synchronisations.
 
 Printed: one JSON line. ``value`` is the prefill throughput in TFLOP/s (causal
 FLOPs counted as 4*B*H*N^2*d/2); the decode rate in GB/s of algorithmic HBM
-bytes sits under ``decode``. ``roofline`` describes the dominant kernel (the
-prefill forward, MFMA-bound); ``roofline_decode`` the decode (HBM-bound).
+bytes sits under ``decode``, the fp8 forward under ``fp8``. ``roofline``
+describes the dominant kernel (the bf16 prefill forward, MFMA-bound);
+``roofline_decode`` the decode (HBM-bound), ``roofline_fp8`` the fp8 forward.
 ``cpu_baseline`` times the CPU fp64 oracle on a bounded sample of the same
 workload on this host's cores.
 """
@@ -32,6 +35,7 @@ if ROOT not in sys.path:
 METRIC = "attn fwd TFLOP/s (bf16 d=128 8K causal) + paged decode HBM GB/s"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 # HBM bytes measured by rocprofv3 (FETCH_SIZE + WRITE_SIZE) per launch, scaled by
 # the copy-kernel calibration factor; None until measured for the current kernels.
 TRAFFIC_PREFILL = None
@@ -44,7 +48,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--exp-mode", type=int, default=0)
-    p.add_argument("--only", choices=["prefill", "decode"], default=None,
+    p.add_argument("--only", choices=["prefill", "decode", "fp8"], default=None,
                    help="time one kernel family only (profiling runs)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle time budget per leg")
@@ -147,6 +151,7 @@ def main():
 
     run_prefill = args.only in (None, "prefill")
     run_decode = args.only in (None, "decode")
+    run_fp8 = args.only in (None, "fp8")
     t_gen = time.perf_counter()
     if run_prefill:
         inp = W.prefill(True)
@@ -174,6 +179,13 @@ def main():
         pools = [(pg.k_cache, pg.v_cache, bt), (kc2, vc2, bt2)]
         do = torch.empty_like(dq)
         dlse = torch.empty((Bd, Hq), dtype=torch.float32, device=dev)
+    if run_fp8:
+        m8 = W.fp8_prefill()
+        t8 = [torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+              for x in (m8.q8, m8.k8, m8.v8, m8.q_scale, m8.k_scale, m8.v_scale)]
+        B8, N8, H8, d8 = m8.q8.shape
+        o8 = torch.empty((B8, N8, H8, d8), dtype=torch.bfloat16, device=dev)
+        lse8 = torch.empty((B8, H8, N8), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     t_gen = time.perf_counter() - t_gen
 
@@ -191,9 +203,15 @@ def main():
                                             stream.cuda_stream)
             ea._check(r, "ea_attn_decode_paged")
             ev[3].record(stream)
+        if run_fp8:
+            ev[4].record(stream)
+            r = ea.lib().ea_attn_fwd_mx8(*[ea._ptr(x) for x in t8], ea._ptr(o8), ea._ptr(lse8), B8, N8, H8, H8, d8,
+                                        1, m8.scale, stream.cuda_stream)
+            ea._check(r, "ea_attn_fwd_mx8")
+            ev[5].record(stream)
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    wev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    wev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
     for i in range(args.warmup):
         step(i, wev)
     torch.cuda.synchronize()
@@ -231,6 +249,18 @@ def main():
                                   "kernel": "ea::decode_split_kernel<4> + decode_combine_kernel"}
         if not run_prefill:
             out["value"], out["unit"] = gbs, "GB/s"
+    if run_fp8:
+        t_8 = np.array([e[4].elapsed_time(e[5]) for e in evs])
+        flops8 = prefill_flops(B8, H8, N8, d8)
+        tf8 = flops8 / (t_8.mean() * 1e-3) / 1e12
+        out["fp8"] = {"value": tf8, "unit": "TFLOP/s", "ms_mean": float(t_8.mean()), "ms_min": float(t_8.min()),
+                      "flop_per_launch": flops8, "workload": "B=2 H=16 N=16384 d=128 causal MX e4m3"}
+        if run_prefill:
+            out["fp8"]["ratio_to_bf16"] = tf8 / out["value"]
+        out["roofline_fp8"] = {"bound": "mfma", "achieved": tf8, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                               "frac": tf8 / PEAK_FP8_TFLOPS, "traffic": None, "kernel": "ea::fwd_mx8_kernel<causal>"}
+        if not (run_prefill or run_decode):
+            out["value"], out["unit"], out["dtype"] = tf8, "TFLOP/s", "fp8_e4m3"
     props = torch.cuda.get_device_properties(dev)
     cfg["device"] = props.name
     cfg["cus"] = props.multi_processor_count

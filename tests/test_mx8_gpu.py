@@ -1,0 +1,99 @@
+"""GPU parity of the MX fp8 forward against the fp64 oracle on the dequantised
+inputs (e4m3 value x 2^(e8m0 - 127), exact in fp64).
+
+The kernel re-quantises P to e4m3 before P V, which the oracle does not mirror
+(the kernel's P depends on its running max and tiling), so the contract is
+normwise: per (batch, head), ||O - O_ref||_F / ||O_ref||_F <= 5e-2, and the
+log-sum-exp within 5e-2 (the scores themselves are exact products of the
+dequantised inputs accumulated in fp32). max|dO| / max|O_ref| is logged too.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from _helpers import f64, host_bits, log
+
+pytestmark = pytest.mark.gpu
+
+NORM_TOL = 5e-2
+LSE_TOL = 5e-2
+
+
+def run_mx8(m):
+    import exact_attention_amd as ea
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    o, lse = ea.attn_fwd_mx8(t(m.q8), t(m.k8), t(m.v8), t(m.q_scale), t(m.k_scale), t(m.v_scale),
+                             m.causal, m.scale)
+    torch.cuda.synchronize()
+    return f64(host_bits(o)), lse.cpu().numpy().astype(np.float64)
+
+
+def deq(m):
+    return (oracle.dequant_mx(m.q8, m.q_scale, axis=3), oracle.dequant_mx(m.k8, m.k_scale, axis=3),
+            oracle.dequant_mx(m.v8, m.v_scale, axis=1))
+
+
+def check_normwise(o, ro, lse, rl, what):
+    B, N, H, d = ro.shape
+    worst = 0.0
+    for b in range(B):
+        for h in range(H):
+            num = np.linalg.norm(o[b, :, h] - ro[b, :, h])
+            den = np.linalg.norm(ro[b, :, h])
+            worst = max(worst, num / den)
+    dl = np.abs(lse - rl)
+    mx = np.abs(o - ro).max() / np.abs(ro).max()
+    log(f"  {what}: normwise {worst:.3e}  max|dO|/max|O| {mx:.3e}  max|dlse| {dl.max():.3e}")
+    assert np.isfinite(o).all()
+    assert worst <= NORM_TOL, f"{what}: normwise error {worst:.3e}"
+    assert dl.max() <= LSE_TOL, f"{what}: lse error {dl.max():.3e}"
+
+
+@pytest.mark.parametrize("shape", [
+    (1, 256, 2, 2, True), (1, 256, 2, 2, False),
+    (2, 320, 4, 2, True),      # N % 64 != 0 (ragged tail tile), GQA 2:1
+    (1, 96, 1, 1, False), (1, 1024, 2, 1, True)])
+def test_mx8_small(shape):
+    B, N, Hq, Hkv, causal = shape
+    log(f"mx8 shape {shape}")
+    # quantise Q with Hq heads and K/V with Hkv heads
+    qf = W.normal_f32(300 + N, W.STREAM_Q, B * N * Hq * 128).reshape(B, N, Hq, 128)
+    kf = W.normal_f32(300 + N, W.STREAM_K, B * N * Hkv * 128).reshape(B, N, Hkv, 128)
+    vf = W.normal_f32(300 + N, W.STREAM_V, B * N * Hkv * 128).reshape(B, N, Hkv, 128)
+    q8, qs = W.mx_quantize_e4m3(qf, axis=3)
+    k8, ks = W.mx_quantize_e4m3(kf, axis=3)
+    v8, vs = W.mx_quantize_e4m3(vf, axis=1)
+    m = W.MX8(q8, k8, v8, qs, ks, vs, causal, 1 / np.sqrt(128))
+    o, lse = run_mx8(m)
+    q, k, v = deq(m)
+    ro, rl = oracle.attention(q, k, v, causal, m.scale)
+    check_normwise(o, ro, lse, rl, f"shape {shape}")
+
+
+def test_mx8_determinism():
+    m = W.mx8(1, 512, 2, 128, True, seed=310)
+    o1, l1 = run_mx8(m)
+    o2, l2 = run_mx8(m)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_fp8_workload_sampled():
+    m = W.fp8_prefill()
+    log(f"mx8 workload shape={m.q8.shape}")
+    o, lse = run_mx8(m)
+    B, N, H, d = m.q8.shape
+    rng = np.random.default_rng(8)
+    rows = sorted(set([0, 1, 63, 64, 127, 128, N // 2, N - 65, N - 1] + rng.integers(0, N, 20).tolist()))
+    for (b, h) in [(0, 0), (1, 15), (0, 9)]:
+        q = oracle.dequant_mx(m.q8[b:b + 1, :, h:h + 1], m.q_scale[b:b + 1, :, h:h + 1], axis=3)
+        k = oracle.dequant_mx(m.k8[b:b + 1, :, h:h + 1], m.k_scale[b:b + 1, :, h:h + 1], axis=3)
+        v = oracle.dequant_mx(m.v8[b:b + 1, :, h:h + 1], m.v_scale[b:b + 1, :, h:h + 1], axis=1)
+        ro, rl = oracle.attention_rows(q, k, v, 0, 0, rows, True, m.scale)
+        got = o[b, rows, h, :]
+        nrm = np.linalg.norm(got - ro) / np.linalg.norm(ro)
+        dl = np.abs(lse[b, h, rows] - rl).max()
+        log(f"  (b={b},h={h}) sampled rows: normwise {nrm:.3e} max|dlse| {dl:.3e}")
+        assert nrm <= NORM_TOL and dl <= LSE_TOL
+    assert np.isfinite(o).all() and np.isfinite(lse).all()

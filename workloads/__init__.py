@@ -67,26 +67,39 @@ E4M3_MAX = 448.0
 
 def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
     """Encode finite values as OCP FP8 E4M3 (bias 7, no infinities), round to
-    nearest even, saturating to +-448. Returns uint8 codes."""
-    x = np.asarray(x, dtype=np.float64)
+    nearest even, saturating to +-448. Returns uint8 codes. Works in float32:
+    every step (power-of-two scaling, rounding to an integer) is exact there."""
+    x = np.asarray(x, dtype=np.float32)
     a = np.abs(x)
     sign = np.signbit(x).astype(np.uint8)
     # quantisation step: 2^(floor(log2 a) - 3) for normals, 2^-9 below 2^-6
-    _, e = np.frexp(np.maximum(a, 2.0 ** -6))          # a = f * 2^e, f in [0.5, 1)
-    step = np.ldexp(1.0, (e - 1) - 3)
-    q = np.round(a / step) * step                        # ties to even
-    q = np.minimum(q, E4M3_MAX)
-    _, e2 = np.frexp(np.maximum(q, 2.0 ** -6))
-    E = e2 - 1                                           # floor(log2 q) for normals
-    normal = q >= 2.0 ** -6
-    exp_field = np.where(normal, E + 7, 0)
-    mant = np.where(normal, q / np.ldexp(1.0, E) - 1.0, q / 2.0 ** -9)
-    mant = np.where(normal, mant * 8.0, mant)
-    code = (sign << 7) | (exp_field.astype(np.uint8) << 3) | np.rint(mant).astype(np.uint8)
+    _, e = np.frexp(np.maximum(a, np.float32(2.0 ** -6)))   # a = f * 2^e, f in [0.5, 1)
+    step = np.ldexp(np.float32(1.0), (e - 4).astype(np.int32))
+    q = np.round(a / step) * step                             # ties to even
+    q = np.minimum(q, np.float32(E4M3_MAX))
+    _, e2 = np.frexp(np.maximum(q, np.float32(2.0 ** -6)))
+    E = (e2 - 1).astype(np.int32)                             # floor(log2 q) for normals
+    normal = q >= np.float32(2.0 ** -6)
+    exp_field = np.where(normal, E + 7, 0).astype(np.uint8)
+    mant = np.where(normal, (q / np.ldexp(np.float32(1.0), E) - np.float32(1.0)) * np.float32(8.0),
+                    q / np.float32(2.0 ** -9))
+    code = (sign << 7) | (exp_field << 3) | np.rint(mant).astype(np.uint8)
     return code.astype(np.uint8)
 
 
-def mx_quantize_e4m3(x: np.ndarray, axis: int, block: int = 32):
+def _mx_rows(blk: np.ndarray):
+    """MX quantisation of rows of 32-element blocks: blk [..., 32] float32."""
+    amax = np.abs(blk).max(axis=-1).astype(np.float64)
+    ratio = amax / E4M3_MAX
+    f, e = np.frexp(np.where(ratio > 0, ratio, 1.0))      # ratio = f * 2^e, f in [0.5,1)
+    E = np.where(f == 0.5, e - 1, e)                       # ceil(log2 ratio)
+    E = np.where(amax > 0, E, -127)
+    E = np.clip(E, -127, 127).astype(np.int32)
+    scaled = blk * np.ldexp(np.float32(1.0), -E)[..., None].astype(np.float32)
+    return f32_to_e4m3_bits(scaled), (E + 127).astype(np.uint8)
+
+
+def mx_quantize_e4m3(x: np.ndarray, axis: int, block: int = 32, threads: int | None = None):
     """Quantise float data to e4m3 codes with one e8m0 scale per ``block``
     consecutive elements along ``axis``.
 
@@ -103,18 +116,29 @@ def mx_quantize_e4m3(x: np.ndarray, axis: int, block: int = 32):
     n = x.shape[axis]
     if n % block:
         raise ValueError("length along the scaled axis must be a multiple of the block")
-    xs = np.moveaxis(x, axis, -1)
-    blk = xs.reshape(xs.shape[:-1] + (n // block, block)).astype(np.float64)
-    amax = np.abs(blk).max(axis=-1)
-    ratio = amax / E4M3_MAX
-    f, e = np.frexp(np.where(ratio > 0, ratio, 1.0))      # ratio = f * 2^e, f in [0.5,1)
-    E = np.where(f == 0.5, e - 1, e)                       # ceil(log2 ratio)
-    E = np.where(amax > 0, E, -127)
-    E = np.clip(E, -127, 127).astype(np.int32)
-    scaled = blk / np.ldexp(1.0, E)[..., None]
-    codes = f32_to_e4m3_bits(scaled).reshape(xs.shape)
-    codes = np.moveaxis(codes, -1, axis)
-    scales = np.moveaxis((E + 127).astype(np.uint8), -1, axis)
+    xs = np.ascontiguousarray(np.moveaxis(x, axis, -1))
+    lead = xs.shape[:-1]
+    blk = xs.reshape(-1, n // block, block)
+    codes = np.empty(blk.shape, np.uint8)
+    scales = np.empty(blk.shape[:2], np.uint8)
+    rows = blk.shape[0]
+    step = max(1, (1 << 20) // max(1, n))
+
+    def run(lo):
+        hi = min(rows, lo + step)
+        c, s_ = _mx_rows(blk[lo:hi])
+        codes[lo:hi] = c
+        scales[lo:hi] = s_
+
+    starts = list(range(0, rows, step))
+    if len(starts) <= 1:
+        for lo in starts:
+            run(lo)
+    else:
+        with ThreadPoolExecutor(threads or _threads()) as ex:
+            list(ex.map(run, starts))
+    codes = np.moveaxis(codes.reshape(lead + (n,)), -1, axis)
+    scales = np.moveaxis(scales.reshape(lead + (n // block,)), -1, axis)
     return np.ascontiguousarray(codes), np.ascontiguousarray(scales)
 
 
