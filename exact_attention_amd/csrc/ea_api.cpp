@@ -191,31 +191,15 @@ ea_status ea_attn_fwd_mx8(const void* q8, const void* k8, const void* v8, const 
 // ---------------------------------------------------------------------------
 namespace {
 
-// Split length (tokens per workgroup). The split count is derived from the
-// maximum context so the grid is known without reading seq_lens on the host;
-// workgroups past a sequence's own length exit at once. Aim for at least two
-// workgroups per CU slot over the longest context, with splits of 256..4096
-// tokens (a heuristic from CU count and lengths; any choice gives the same
-// result up to rounding).
-int choose_split_len(int B, int Hkv, int max_seqlen, int page_size, int num_splits) {
-  // 32-token steps; 16 | page_size keeps every 16-token tile inside one page
-  (void)page_size;
-  const int unit = 32;
-  const int cus = 256;  // fixed so the workspace size does not depend on the device
-  if (num_splits > 0) {
-    int per = (max_seqlen + num_splits - 1) / num_splits;
-    per = ((per + unit - 1) / unit) * unit;
-    return per < unit ? unit : per;
-  }
-  long long pairs = (long long)B * Hkv;
-  long long target_wg = 4LL * cus;  // aim for a few workgroups per CU in total
-  long long splits = (target_wg + pairs - 1) / pairs;
-  if (splits < 1) splits = 1;
-  long long per = (max_seqlen + splits - 1) / splits;
-  if (per < 256) per = 256;
-  if (per > 4096) per = 4096;
-  per = ((per + unit - 1) / unit) * unit;
-  return (int)per;
+// Number of equal shares W the batch's KV chunks are cut into (one workgroup
+// of 8 KV heads each). By default one workgroup per CU: 256 CUs over the
+// groups of 8 KV heads, fixed so the workspace size does not depend on the
+// device. Any W gives the same result up to rounding.
+int choose_ranges(int Hkv, int num_splits) {
+  if (num_splits > 0) return num_splits;
+  const int head_groups = (Hkv + 7) / 8;
+  const int w = (256 + head_groups - 1) / head_groups;
+  return w < 1 ? 1 : w;
 }
 
 }  // namespace
@@ -226,9 +210,9 @@ size_t ea_decode_workspace_size(int B, int Hq, int Hkv, int d, int max_seqlen, i
                                 int num_splits) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || max_seqlen < 0 || page_size <= 0 || num_splits < 0)
     return 0;
-  const int split_len = choose_split_len(B, Hkv, max_seqlen, page_size, num_splits);
-  const int max_splits = max_seqlen > 0 ? (max_seqlen + split_len - 1) / split_len : 1;
-  return ea::decode_workspace_bytes(B, Hq, d, max_splits);
+  (void)max_seqlen;
+  (void)page_size;
+  return ea::decode_workspace_bytes(B, Hq, d, choose_ranges(Hkv, num_splits));
 }
 
 ea_status ea_attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
@@ -249,6 +233,9 @@ ea_status ea_attn_decode_paged(const void* q, const void* k_cache, const void* v
     return fail(EA_ERR_UNSUPPORTED, "Hq / Hkv must be 1, 2, 4, 8 or 16");
   if (!finite_pos(scale)) return fail(EA_ERR_INVALID, "scale must be finite and positive");
   if (num_splits < 0) return fail(EA_ERR_INVALID, "num_splits must be >= 0");
+  if (num_splits > 65536) return fail(EA_ERR_UNSUPPORTED, "num_splits above 65536");
+  if ((long long)B * max_pages_per_seq * page_size / 32 >= (1LL << 31))
+    return fail(EA_ERR_UNSUPPORTED, "batch context too long (2^31 32-token chunks)");
   if ((long long)max_pages_per_seq * page_size >= (1LL << 31))
     return fail(EA_ERR_UNSUPPORTED, "max context too long");
   if ((long long)num_pages * page_size * Hkv * d >= (1LL << 40))
@@ -258,7 +245,6 @@ ea_status ea_attn_decode_paged(const void* q, const void* k_cache, const void* v
   if (workspace == nullptr || workspace_bytes < need)
     return fail(EA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                 workspace == nullptr ? (size_t)0 : workspace_bytes);
-  const int split_len = choose_split_len(B, Hkv, max_seqlen, page_size, num_splits);
   ea::DecodeArgs a{};
   a.q = (const uint16_t*)q;
   a.kc = (const uint16_t*)k_cache;
@@ -274,12 +260,9 @@ ea_status ea_attn_decode_paged(const void* q, const void* k_cache, const void* v
   a.page_size = page_size;
   a.max_pages = max_pages_per_seq;
   a.num_pages = num_pages;
-  a.split_len = split_len;
-  a.max_splits = (max_seqlen + split_len - 1) / split_len;
+  a.num_ranges = choose_ranges(Hkv, num_splits);
   a.scale_log2 = scale * 1.4426950408889634f;
-  const size_t o_bytes = (size_t)B * Hq * a.max_splits * d * sizeof(float);
-  a.part_o = (float*)workspace;
-  a.part_lse = (float*)((char*)workspace + o_bytes);
+  ea::decode_bind_workspace(a, workspace);
   return hip_status(ea::launch_decode(a, (hipStream_t)stream), "paged decode launch");
 }
 

@@ -2,26 +2,37 @@
 //
 // Method ("Faster, more flexible FlashAttention-4 for LLM inference"):
 //  * split-KV (section on PR 1940): the KV sequence of every (sequence, KV head)
-//    is cut into splits of split_len tokens, one workgroup per split, each
-//    producing a normalised partial output and its log-sum-exp; a second
-//    kernel merges the splits (lse = log sum exp lse_s, o = sum
-//    exp(lse_s - lse) o_s) in fp32;
+//    is cut into pieces, one workgroup per piece, each producing a normalised
+//    partial output and its log-sum-exp; a second kernel merges the pieces
+//    (lse = log sum exp lse_s, o = sum exp(lse_s - lse) o_s) in fp32;
 //  * paged KV of any page size (sections on PR 1999/2104): token t of sequence
 //    b is read from page block_table[b, t / page_size], slot t % page_size;
 //  * one query tile per workgroup (PR 1993) and all query heads of one KV head
 //    packed into that tile (PR 2186), so every KV byte is read once.
 //
-// gfx950 mapping (this file's design): 4 waves per workgroup take 32-token
-// chunks in turn. A chunk is two 16-token tiles; 16 divides page_size, so a
-// tile lies in one page and its page index is wave-uniform (a scalar load), and
-// only 32-bit row offsets are formed per lane. Each wave copies its chunk's K
-// and V rows (256 contiguous bytes per row) into its own LDS region (no
-// workgroup barrier in the loop), prefetching the next chunk into VGPRs while
-// it computes the current one. S^T = K Q^T and O^T = V^T P^T use
-// v_mfma_f32_16x16x32_bf16 with the packed query heads as the 16-wide column
-// block; V^T operands come from ds_read_b64_tr_b16. Tokens at or past the
-// sequence length are never loaded (zero-filled), so stale or poisoned slots of
-// a last page cannot leak.
+// gfx950 mapping (this file's design):
+//  * Balanced pieces. Every sequence's context is a run of 32-token chunks;
+//    laid end to end over the batch they form Tc chunks, which are cut into W
+//    equal ranges, one per workgroup (W = gridDim.x, one workgroup per CU by
+//    default). A range meets one or more sequences; for each of them the
+//    workgroup runs the online-softmax loop over its chunks and writes one
+//    partial into slot w + b. Walking the pieces in order, each step moves to
+//    the next workgroup, the next sequence or both, so w + b never repeats and
+//    W + B slots suffice whatever the lengths. Every workgroup gets the same
+//    work up to one chunk, so there is no tail of long splits.
+//  * A workgroup of 8 waves serves 8 KV heads, one wave per head, all walking
+//    the same chunks. In the [pages, page_size, Hkv, d] cache a token's rows for
+//    all KV heads are adjacent, so the workgroup streams whole contiguous rows.
+//  * A chunk is two 16-token tiles; 16 divides page_size, so a tile lies in one
+//    page. Page indices are loaded 128 tiles at a time (two per lane) and read
+//    with v_readlane in the loop; each tile is a buffer resource bounded by the
+//    sequence length, so tokens at or past it (stale or poisoned slots of a
+//    last page) and page indices outside the pool read as zeros, no branch.
+//  * Each wave copies its chunk's K and V rows into its own LDS region (no
+//    workgroup barrier anywhere), prefetching the next chunk into VGPRs while
+//    it computes the current one. S^T = K Q^T and O^T = V^T P^T use
+//    v_mfma_f32_16x16x32_bf16 with the packed query heads as the 16-wide
+//    column block; V^T operands come from ds_read_b64_tr_b16.
 #include "ea_device.h"
 #include "ea_internal.h"
 
@@ -30,7 +41,7 @@ namespace ea {
 namespace {
 constexpr int kD = 128;
 constexpr int kChunk = 32;  // tokens per wave step
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;  // one wave per KV head of a group of 8
 }  // namespace
 
 __device__ __forceinline__ float xor16_max(float x) {
@@ -38,206 +49,283 @@ __device__ __forceinline__ float xor16_max(float x) {
 }
 __device__ __forceinline__ float xor16_sum(float x) { return x + __shfl_xor(x, 16); }
 
+// Chunks of sequence b: its length clamped to [0, block-table capacity].
+__device__ __forceinline__ int seq_len_clamped(const DecodeArgs& a, int b) {
+  return min(max(a.seq_lens[b], 0), a.max_pages * a.page_size);
+}
+__device__ __forceinline__ int seq_chunks(const DecodeArgs& a, int b) {
+  return (seq_len_clamped(a, b) + kChunk - 1) / kChunk;
+}
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+__device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+// Total chunks over the batch (every lane gets the same value).
+__device__ __forceinline__ int total_chunks(const DecodeArgs& a, int lane) {
+  int t = 0;
+  for (int base = 0; base < a.B; base += 64)
+    if (base + lane < a.B) t += seq_chunks(a, base + lane);
+  return uniform(wave_sum(t));
+}
+// First chunk of workgroup w's range: floor(w * Tc / W).
+__device__ __forceinline__ int range_start(int w, int Tc, int W) {
+  return (int)(((long long)w * Tc) / W);
+}
+
 template <int G>
-__global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(DecodeArgs a) {
   constexpr int D = kD;
   constexpr int TILE = kChunk * D;  // bf16 elements per K or V chunk
   __shared__ __attribute__((aligned(16))) uint16_t smem_raw[kWaves * 2 * TILE];
   EA_LDS uint16_t* sm = (EA_LDS uint16_t*)smem_raw;
 
-  const int split = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
-  // lengths beyond the block table's capacity are clamped (never index past it)
-  const int L = min(a.seq_lens[b], a.max_pages * a.page_size);
-  const int t_begin = split * a.split_len;
-  if (t_begin >= L && !(split == 0 && L <= 0)) return;
-  const int t_end = min(L, t_begin + a.split_len);
+  // grid: x = workgroup range w of W, y = group of kWaves KV heads; wave i
+  // owns KV head kWaves*y + i.
+  const int wg = blockIdx.x, W = gridDim.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = uniform(tid >> 6);
+  const int hkv = uniform(kWaves * (int)blockIdx.y + wv);
+  if (hkv >= a.Hkv) return;  // no barriers below: idle waves may leave
+  const int Tc = total_chunks(a, lane);
+  // lane 0 of the first wave of head group 0 records Tc (workgroup 0, whose
+  // range may be empty) and which ranges hold each sequence's first and last
+  // chunk, for the combine
+  const bool record = blockIdx.y == 0 && wv == 0 && lane == 0;
+  if (record && wg == 0) a.plan[2 * a.B] = Tc;
+  const int g0 = uniform(range_start(wg, Tc, W)), g1 = uniform(range_start(wg + 1, Tc, W));
+  if (g0 >= g1) return;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int grp = lane >> 4, col = lane & 15;
   const int ps = a.page_size;
-  const size_t row_stride = (size_t)a.Hkv * D;  // elements between consecutive slots
-  const int* bt = a.block_table + (size_t)b * a.max_pages;
-  const uint16_t* kbase = a.kc + (size_t)hkv * D;
-  const uint16_t* vbase = a.vc + (size_t)hkv * D;
-
-  // Q^T operand (B of S^T = K Q^T): column = packed query head, k = d
-  bf16x8 qf[D / 32];
-  {
-    const int head = col;
-    const uint16_t* qp = a.q + ((size_t)b * a.Hq + (size_t)hkv * G + head) * D + 8 * grp;
-#pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) qf[kk] = (head < G) ? *(const bf16x8*)(qp + 32 * kk) : bf16x8{};
-  }
-
-  EA_LDS uint16_t* ks = sm + w * 2 * TILE;
+  const int row_bytes = a.Hkv * D * 2;  // bytes between consecutive slots of a page
+  EA_LDS uint16_t* ks = sm + wv * 2 * TILE;
   EA_LDS uint16_t* vs = ks + TILE;
 
-  // chunk staging: lane handles rows 4u + grp (u = 0..7), 16-byte column chunk `col`
-  i32x4 rk[8], rv[8];
-  auto gload = [&](int t0) {
-    const int p0 = (t0 < t_end) ? bt[t0 / ps] : 0;
-    const int p1 = (t0 + 16 < t_end) ? bt[(t0 + 16) / ps] : 0;
+  // loop-invariant LDS offsets
+  const uint32_t voff0 = (uint32_t)(grp * row_bytes + col * 16);
+  int st_off[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int row = 4 * u + grp;
-      const int tok = t0 + row;
-      const int page = (u < 4) ? p0 : p1;
-      if (tok < t_end && (unsigned)page < (unsigned)a.num_pages) {
-        const size_t off = ((size_t)page * ps + (tok % ps)) * row_stride + col * 8;
-        rk[u] = *(const i32x4*)(kbase + off);
-        rv[u] = *(const i32x4*)(vbase + off);
-      } else {
-        rk[u] = i32x4{0, 0, 0, 0};
-        rv[u] = i32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto sstore = [&]() {
+  for (int u = 0; u < 8; ++u) {
+    const int row = 4 * u + grp;
+    st_off[u] = row * D + ((col ^ swz<D>(row)) << 3);
+  }
+  int k_off[2][D / 32];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int row = 4 * u + grp;
-      const int o = row * D + ((col ^ swz<D>(row)) << 3);
-      lds_store<i32x4>(ks + o, rk[u]);
-      lds_store<i32x4>(vs + o, rv[u]);
-    }
-  };
-
-  float m_run = kNegInf, l_run = 0.f;
-  f32x4 oacc[D / 16];
+  for (int tl = 0; tl < 2; ++tl)
 #pragma unroll
-  for (int mt = 0; mt < D / 16; ++mt) oacc[mt] = f32x4{};
+    for (int kk = 0; kk < D / 32; ++kk) k_off[tl][kk] = tile_off<D>(16 * tl + col, 32 * kk + 8 * grp);
+  const int tr_row = 4 * grp + ((lane >> 2) & 3);
+  const int tr_col = 4 * (lane & 3);
+  int v_off[D / 16][2];
+#pragma unroll
+  for (int mt = 0; mt < D / 16; ++mt) {
+    v_off[mt][0] = tile_off<D>(tr_row, 16 * mt + tr_col);
+    v_off[mt][1] = tile_off<D>(16 + tr_row, 16 * mt + tr_col);
+  }
   const float sl = a.scale_log2;
   const float tau = 8.0f;
 
-  int t0 = t_begin + kChunk * w;
-  if (t0 < t_end) {
-    gload(t0);
-    sstore();
-  }
-  for (; t0 < t_end; t0 += kChunk * kWaves) {
-    const int tn = t0 + kChunk * kWaves;
-    if (tn < t_end) gload(tn);
-    // ---- S^T = K Q^T for two 16-token tiles
-    f32x4 s[2];
+  // ---- one piece: chunks [c0, c1) of sequence b, partial into slot wg + b
+  auto run_piece = [&](int b, int c0, int c1) {
+    const int L = uniform(seq_len_clamped(a, b));
+    const int t_begin = uniform(kChunk * c0);
+    const int t_end = uniform(min(L, kChunk * c1));
+    const int nck = uniform(c1 - c0);
+    const int* bt = uniform_ptr(a.block_table + (size_t)b * a.max_pages);
+
+    // Q^T operand (B of S^T = K Q^T): column = packed query head, k = d
+    bf16x8 qf[D / 32];
+    {
+      const uint16_t* qp = a.q + ((size_t)b * a.Hq + (size_t)hkv * G + col) * D + 8 * grp;
 #pragma unroll
-    for (int tl = 0; tl < 2; ++tl) {
-      s[tl] = f32x4{};
-#pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk) {
-        const bf16x8 ka = lds_load<bf16x8>(ks + tile_off<D>(16 * tl + col, 32 * kk + 8 * grp));
-        s[tl] = mfma16x16x32(ka, qf[kk], s[tl]);
-      }
+      for (int kk = 0; kk < D / 32; ++kk) qf[kk] = (col < G) ? *(const bf16x8*)(qp + 32 * kk) : bf16x8{};
     }
-    if (t0 + kChunk > t_end) {
+
+    // Page indices of 128 consecutive 16-token tiles (64 chunks), two per lane;
+    // in the loop they come from v_readlane, so no memory access there has a
+    // wait that would also wait for the K/V loads in flight.
+    int lane_page[2];
+    auto load_pages = [&](int ci0) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int tt = t_begin + kChunk * ci0 + 16 * (64 * r + lane);
+        lane_page[r] = (tt < t_end) ? bt[tt / ps] : -1;
+      }
+    };
+    // A tile's buffer resource starts at its first slot for this KV head and
+    // ends after the last valid token.
+    auto tile_rsrc = [&](const uint16_t* cache, int tt, int page) {
+      const int slot = uniform(tt % ps);
+      const bool ok = (unsigned)page < (unsigned)a.num_pages && tt < t_end;
+      const int nvalid = ok ? min(16, t_end - tt) : 0;
+      const uint16_t* base = uniform_ptr(cache + (((size_t)(ok ? page : 0) * ps + slot) * a.Hkv + hkv) * D);
+      return make_rsrc(base, nvalid > 0 ? (uint32_t)((nvalid - 1) * row_bytes + D * 2) : 0u);
+    };
+    // chunk staging: lane handles rows 4u + grp (u = 0..7), 16-byte column chunk col.
+    // Both tiles' page indices are read before the chunk's first load, where no
+    // load is in flight, so their waits cost nothing.
+    i32x4 rk[8], rv[8];
+    auto gload = [&](int ci) {
+      const int idx = 2 * (ci & 31);
+      const int lp = (ci & 32) ? lane_page[1] : lane_page[0];
+      const int page0 = __builtin_amdgcn_readlane(lp, idx), page1 = __builtin_amdgcn_readlane(lp, idx + 1);
+      const int tt = uniform(t_begin + kChunk * ci);
+      const __amdgpu_buffer_rsrc_t rs[2][2] = {{tile_rsrc(a.kc, tt, page0), tile_rsrc(a.vc, tt, page0)},
+                                               {tile_rsrc(a.kc, tt + 16, page1), tile_rsrc(a.vc, tt + 16, page1)}};
 #pragma unroll
       for (int tl = 0; tl < 2; ++tl)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (t0 + 16 * tl + 4 * grp + i >= t_end) s[tl][i] = kNegInf;
-    }
-    float mx = kNegInf;
+        for (int u = 0; u < 4; ++u) {
+          rk[4 * tl + u] = buffer_load16(rs[tl][0], voff0 + 4 * u * row_bytes);
+          rv[4 * tl + u] = buffer_load16(rs[tl][1], voff0 + 4 * u * row_bytes);
+        }
+    };
+    auto sstore = [&]() {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) mx = __builtin_fmaxf(mx, __builtin_fmaxf(s[0][i], s[1][i]));
-    mx = xor16_max(mx);
-    mx = max_with_partner32(mx);
-    const float m_new = __builtin_fmaxf(m_run, mx * sl);
-    if (__ballot(m_new > m_run + tau)) {
-      const float alpha = (m_run == kNegInf) ? 0.f : exp2_hw(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int mt = 0; mt < D / 16; ++mt) oacc[mt] *= alpha;
-      m_run = m_new;
-    }
-    const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
-    float pv[2][4];
-#pragma unroll
-    for (int tl = 0; tl < 2; ++tl)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pv[tl][i] = exp2_hw(__builtin_fmaf(s[tl][i], sl, neg_m));
-    l_run += (pv[0][0] + pv[0][1]) + (pv[0][2] + pv[0][3]) + (pv[1][0] + pv[1][1]) + (pv[1][2] + pv[1][3]);
-    uint32_t pk[4];
-    pk[0] = pack_bf16x2(pv[0][0], pv[0][1]);
-    pk[1] = pack_bf16x2(pv[0][2], pv[0][3]);
-    pk[2] = pack_bf16x2(pv[1][0], pv[1][1]);
-    pk[3] = pack_bf16x2(pv[1][2], pv[1][3]);
-    const i32x4 pt = {(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
-    const bf16x8 pb = __builtin_bit_cast(bf16x8, pt);
-    // ---- O^T += V^T P^T (k = 32 tokens: tile-0 tokens 4*grp+0..3, tile-1 tokens 16+4*grp+0..3)
-    const int tr_row = 4 * grp + ((lane >> 2) & 3);
-    const int tr_col = 4 * (lane & 3);
-#pragma unroll
-    for (int mt = 0; mt < D / 16; ++mt) {
-      const i16x4 lo = ds_read_tr16(vs + tile_off<D>(tr_row, 16 * mt + tr_col));
-      const i16x4 hi = ds_read_tr16(vs + tile_off<D>(16 + tr_row, 16 * mt + tr_col));
-      const i32x4 t = {__builtin_bit_cast(i32x2, lo)[0], __builtin_bit_cast(i32x2, lo)[1],
-                       __builtin_bit_cast(i32x2, hi)[0], __builtin_bit_cast(i32x2, hi)[1]};
-      oacc[mt] = mfma16x16x32(__builtin_bit_cast(bf16x8, t), pb, oacc[mt]);
-    }
-    if (tn < t_end) sstore();
-  }
+      for (int u = 0; u < 8; ++u) {
+        lds_store<i32x4>(ks + st_off[u], rk[u]);
+        lds_store<i32x4>(vs + st_off[u], rv[u]);
+      }
+    };
 
-  // ---- merge the four waves of this split through LDS
-  float l_tot = xor16_sum(l_run);
-  l_tot = sum_with_partner32(l_tot);
-  __syncthreads();  // all waves done with their K/V regions
-  float* red = (float*)smem_raw;                   // [4 waves][16 heads][D]
-  float* red_m = red + kWaves * 16 * D;            // [4][16]
-  float* red_l = red_m + kWaves * 16;              // [4][16]
+    float m_run = kNegInf, l_run = 0.f;
+    f32x4 oacc[D / 16];
 #pragma unroll
-  for (int mt = 0; mt < D / 16; ++mt)
+    for (int mt = 0; mt < D / 16; ++mt) oacc[mt] = f32x4{};
+
+    load_pages(0);
+    gload(0);
+    sstore();
+    __builtin_amdgcn_s_waitcnt(0);
+    for (int ci = 0; ci < nck; ++ci) {
+      const int t0 = t_begin + kChunk * ci;
+      if (ci + 1 < nck) {
+        if (((ci + 1) & 63) == 0) load_pages(ci + 1);
+        gload(ci + 1);
+      }
+      // ---- S^T = K Q^T for two 16-token tiles
+      f32x4 s[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red[(w * 16 + col) * D + 16 * mt + 4 * grp + i] = oacc[mt][i];
-  if (grp == 0) {
-    red_m[w * 16 + col] = m_run;
-    red_l[w * 16 + col] = l_tot;
-  }
-  __syncthreads();
-  // 256 threads: thread -> (head, 8 consecutive d)
-  for (int idx = tid; idx < G * (D / 8); idx += 256) {
-    const int head = idx / (D / 8), d0 = (idx % (D / 8)) * 8;
-    float mstar = kNegInf;
+      for (int tl = 0; tl < 2; ++tl) {
+        s[tl] = f32x4{};
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) mstar = __builtin_fmaxf(mstar, red_m[ww * 16 + head]);
-    float wt[kWaves], lsum = 0.f;
+        for (int kk = 0; kk < D / 32; ++kk)
+          s[tl] = mfma16x16x32(lds_load<bf16x8>(ks + k_off[tl][kk]), qf[kk], s[tl]);
+      }
+      if (t0 + kChunk > t_end) {
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
-      const float mw = red_m[ww * 16 + head];
-      wt[ww] = (mw == kNegInf) ? 0.f : exp2_hw(mw - mstar);
-      lsum += wt[ww] * red_l[ww * 16 + head];
+        for (int tl = 0; tl < 2; ++tl)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (t0 + 16 * tl + 4 * grp + i >= t_end) s[tl][i] = kNegInf;
+      }
+      float mx = kNegInf;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = __builtin_fmaxf(mx, __builtin_fmaxf(s[0][i], s[1][i]));
+      mx = xor16_max(mx);
+      mx = max_with_partner32(mx);
+      const float m_new = __builtin_fmaxf(m_run, mx * sl);
+      if (__ballot(m_new > m_run + tau)) {
+        const float alpha = (m_run == kNegInf) ? 0.f : exp2_hw(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < D / 16; ++mt) oacc[mt] *= alpha;
+        m_run = m_new;
+      }
+      const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
+      float pv[2][4];
+#pragma unroll
+      for (int tl = 0; tl < 2; ++tl)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pv[tl][i] = exp2_hw(__builtin_fmaf(s[tl][i], sl, neg_m));
+      l_run += (pv[0][0] + pv[0][1]) + (pv[0][2] + pv[0][3]) + (pv[1][0] + pv[1][1]) + (pv[1][2] + pv[1][3]);
+      const i32x4 pt = {(int)pack_bf16x2(pv[0][0], pv[0][1]), (int)pack_bf16x2(pv[0][2], pv[0][3]),
+                        (int)pack_bf16x2(pv[1][0], pv[1][1]), (int)pack_bf16x2(pv[1][2], pv[1][3])};
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, pt);
+      // ---- O^T += V^T P^T (k = 32 tokens: tile-0 tokens 4*grp+0..3, tile-1 tokens 16+4*grp+0..3)
+#pragma unroll
+      for (int mt = 0; mt < D / 16; ++mt) {
+        const i16x4 lo = ds_read_tr16(vs + v_off[mt][0]);
+        const i16x4 hi = ds_read_tr16(vs + v_off[mt][1]);
+        const i32x4 t = {__builtin_bit_cast(i32x2, lo)[0], __builtin_bit_cast(i32x2, lo)[1],
+                         __builtin_bit_cast(i32x2, hi)[0], __builtin_bit_cast(i32x2, hi)[1]};
+        oacc[mt] = mfma16x16x32(__builtin_bit_cast(bf16x8, t), pb, oacc[mt]);
+      }
+      if (ci + 1 < nck) sstore();
     }
-    const float inv = (lsum > 0.f) ? 1.0f / lsum : 0.f;
-    const size_t prow = (((size_t)b * a.Hkv + hkv) * a.max_splits + split) * G + head;
-    float* po = a.part_o + prow * D + d0;
+
+    // ---- this piece's normalised partial output and log-sum-exp
+    float l_tot = xor16_sum(l_run);
+    l_tot = sum_with_partner32(l_tot);
+    const float inv = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
+    if (col < G) {
+      const size_t prow = (((size_t)(wg + b)) * a.Hkv + hkv) * G + col;
+      float* po = a.part_o + prow * D;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float acc = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) acc += wt[ww] * red[(ww * 16 + head) * D + d0 + e];
-      po[e] = acc * inv;
+      for (int mt = 0; mt < D / 16; ++mt) {
+        const float4 v = {oacc[mt][0] * inv, oacc[mt][1] * inv, oacc[mt][2] * inv, oacc[mt][3] * inv};
+        *(float4*)(po + 16 * mt + 4 * grp) = v;
+      }
+      if (grp == 0)
+        a.part_lse[prow] = (l_tot > 0.f && m_run != kNegInf) ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
     }
-    if (d0 == 0)
-      a.part_lse[prow] = (lsum > 0.f && mstar != kNegInf) ? (mstar + __log2f(lsum)) * kLn2 : kNegInf;
+  };
+
+  // ---- walk the sequences whose chunks meet [g0, g1), 64 at a time
+  int carry = 0;  // chunks of the sequences before this block of 64
+  for (int base = 0; base < a.B && carry < g1; base += 64) {
+    const int bb = base + lane;
+    const int n = bb < a.B ? seq_chunks(a, bb) : 0;
+    const int incl = wave_inclusive_scan(n, lane);
+    const int cs = carry + incl - n, ce = carry + incl;
+    uint64_t hit = __ballot(n > 0 && cs < g1 && ce > g0);
+    while (hit) {
+      const int i = __builtin_ctzll(hit);
+      hit &= hit - 1;
+      const int b = base + i;
+      const int sb = __builtin_amdgcn_readlane(cs, i), eb = __builtin_amdgcn_readlane(ce, i);
+      const int c0 = max(g0, sb) - sb, c1 = min(g1, eb) - sb;
+      if (record && c0 == 0) a.plan[b] = wg;
+      if (record && c1 == eb - sb) a.plan[a.B + b] = wg;
+      run_piece(b, c0, c1);
+    }
+    carry = uniform(__builtin_amdgcn_readlane(ce, 63));
   }
 }
 
-// One workgroup of 128 threads per (sequence, query head): merge the splits.
+// One workgroup of 128 threads per (sequence, query head): merge the pieces.
+// plan[b] and plan[B + b] are the first and last workgroup ranges holding
+// sequence b's chunks; ranges in between that are empty (possible when there
+// are fewer chunks than ranges) wrote nothing and are skipped.
 __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
   const int bh = blockIdx.x;
   const int b = bh / a.Hq, h = bh % a.Hq;
   const int hkv = h / a.group, head = h % a.group;
-  const int L = min(a.seq_lens[b], a.max_pages * a.page_size);
-  const int nsp = L > 0 ? (L + a.split_len - 1) / a.split_len : 1;
   const int d = threadIdx.x;
-  const size_t base = (((size_t)b * a.Hkv + hkv) * a.max_splits) * a.group + head;
-  float mx = kNegInf;
-  for (int s = 0; s < nsp; ++s) mx = __builtin_fmaxf(mx, a.part_lse[base + (size_t)s * a.group]);
-  float acc = 0.f, wsum = 0.f;
-  if (mx != kNegInf) {
-    for (int s = 0; s < nsp; ++s) {
-      const float ls = a.part_lse[base + (size_t)s * a.group];
-      const float wgt = (ls == kNegInf) ? 0.f : __expf(ls - mx);
-      wsum += wgt;
-      acc += wgt * a.part_o[(base + (size_t)s * a.group) * kD + d];
+  const int W = a.num_ranges;
+  float acc = 0.f, wsum = 0.f, mx = kNegInf;
+  if (seq_chunks(a, b) > 0) {
+    const int Tc = a.plan[2 * a.B];
+    const int wf = a.plan[b], wl = a.plan[a.B + b];
+    auto row = [&](int w) { return (((size_t)(w + b)) * a.Hkv + hkv) * a.group + head; };
+    for (int w = wf; w <= wl; ++w)
+      if (range_start(w, Tc, W) < range_start(w + 1, Tc, W)) mx = __builtin_fmaxf(mx, a.part_lse[row(w)]);
+    if (mx != kNegInf) {
+      for (int w = wf; w <= wl; ++w) {
+        if (range_start(w, Tc, W) >= range_start(w + 1, Tc, W)) continue;
+        const float ls = a.part_lse[row(w)];
+        const float wgt = (ls == kNegInf) ? 0.f : __expf(ls - mx);
+        wsum += wgt;
+        acc += wgt * a.part_o[row(w) * kD + d];
+      }
     }
   }
   const float o = (wsum > 0.f) ? acc / wsum : 0.f;
@@ -247,13 +335,33 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
   if (a.lse != nullptr && d == 0) a.lse[(size_t)b * a.Hq + h] = (wsum > 0.f) ? mx + __logf(wsum) : kNegInf;
 }
 
-size_t decode_workspace_bytes(int B, int Hq, int d, int max_splits) {
-  return (size_t)B * Hq * max_splits * d * sizeof(float) + (size_t)B * Hq * max_splits * sizeof(float);
+namespace {
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+}  // namespace
+
+// Workspace: part_o [(W + B) slots, Hkv, group, d] fp32, part_lse [(W + B) slots,
+// Hkv, group] fp32, plan [2B + 1] int32 (first range, last range per sequence,
+// then Tc), each starting on a 256-byte boundary.
+size_t decode_workspace_bytes(int B, int Hq, int d, int num_ranges) {
+  const size_t slots = (size_t)num_ranges + (size_t)B;
+  return round256(slots * Hq * d * sizeof(float)) + round256(slots * Hq * sizeof(float)) +
+         (2 * (size_t)B + 1) * sizeof(int);
+}
+
+void decode_bind_workspace(DecodeArgs& a, void* workspace) {
+  const size_t slots = (size_t)a.num_ranges + (size_t)a.B;
+  char* p = (char*)workspace;
+  a.part_o = (float*)p;
+  p += round256(slots * a.Hq * kD * sizeof(float));
+  a.part_lse = (float*)p;
+  p += round256(slots * a.Hq * sizeof(float));
+  a.plan = (int*)p;
 }
 
 template <int G>
 static hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(decode_split_kernel<G>, dim3(a.max_splits, a.Hkv, a.B), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(decode_split_kernel<G>, dim3(a.num_ranges, (a.Hkv + kWaves - 1) / kWaves),
+                     dim3(64 * kWaves), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(a.B * a.Hq), dim3(kD), 0, s, a);
@@ -261,6 +369,7 @@ static hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
+  if (a.num_ranges <= 0 || a.part_o == nullptr || a.plan == nullptr) return hipErrorInvalidValue;
   switch (a.group) {
     case 1: return launch_g<1>(a, s);
     case 2: return launch_g<2>(a, s);

@@ -133,6 +133,14 @@ __device__ __forceinline__ int tile_off(int row, int col) {
 // Workgroup-uniform integer pinned to a scalar register (the compiler cannot
 // always prove uniformity through divisions done on the vector unit).
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+// Workgroup-uniform pointer pinned to scalar registers (both 32-bit halves).
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return (T*)(((uint64_t)hi << 32) | lo);
+}
 
 // Buffer resource over [base, base + nbytes) (raw, stride 0): loads at offsets
 // >= nbytes return zeros. The range check covers the VGPR offset only.

@@ -58,16 +58,18 @@ struct DecodeArgs {
   const int* seq_lens;
   uint16_t* o;
   float* lse;
-  float* part_o;     // [B, Hkv, max_splits, group, d] fp32
-  float* part_lse;   // [B, Hkv, max_splits, group] fp32
+  float* part_o;     // [num_ranges + B slots, Hkv, group, d] fp32
+  float* part_lse;   // [num_ranges + B slots, Hkv, group] fp32
+  int* plan;         // [2B + 1]: first / last range of each sequence, total chunks
   int B, Hq, Hkv, group;
   int page_size, max_pages;
   int num_pages;     // pool size: page indices outside [0, num_pages) read as zeros
-  int split_len;     // tokens per split (multiple of 32 and of page_size)
-  int max_splits;
+  int num_ranges;    // W: equal shares of the batch's chunks, one workgroup each
   float scale_log2;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
-size_t decode_workspace_bytes(int B, int Hq, int d, int max_splits);
+size_t decode_workspace_bytes(int B, int Hq, int d, int num_ranges);
+// points part_o / part_lse / plan into a workspace of decode_workspace_bytes
+void decode_bind_workspace(DecodeArgs& a, void* workspace);
 
 }  // namespace ea

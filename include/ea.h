@@ -143,11 +143,15 @@ ea_status ea_attn_fwd_mx8(const void* q8, const void* k8, const void* v8,
  *          values are clamped to that capacity)
  *   o      [B, Hq, d] bf16 (written); lse [B, Hq] fp32 or NULL
  *   page_size a multiple of 16; d == 128; Hq / Hkv in {1, 2, 4, 8, 16}.
- *   num_splits: 0 = choose from the CU count and lengths; otherwise the number
- *          of KV splits per sequence (>= 1).
+ *   num_splits: the batch's KV tokens, taken in 32-token chunks and laid end
+ *          to end over the sequences, are cut into num_splits equal ranges, one
+ *          workgroup (of up to 8 KV heads) each; a sequence is split wherever a
+ *          range boundary falls in it. 0 = one workgroup per CU (256 over the
+ *          groups of 8 KV heads). At most 65536.
  *   workspace: device memory of at least ea_decode_workspace_size(B, Hq, Hkv,
- *          d, max_pages_per_seq * page_size, page_size, num_splits) bytes,
- *          owned by the caller; contents on entry are ignored.
+ *          d, max_pages_per_seq * page_size, page_size, num_splits) bytes
+ *          (it depends on B, Hq, d and the range count only), owned by the
+ *          caller; contents on entry are ignored.
  * The decode attends to all seq_lens[b] tokens (no mask).
  */
 size_t ea_decode_workspace_size(int B, int Hq, int Hkv, int d, int max_seqlen, int page_size,

@@ -55,14 +55,45 @@ def test_larger_pages(page_size):
     assert_lse_close(lse, rl)
 
 
-@pytest.mark.parametrize("num_splits", [1, 3, 7])
+@pytest.mark.parametrize("num_splits", [1, 3, 7, 1000])
 def test_split_counts(num_splits):
+    """num_splits = number of equal ranges of the batch's 32-token chunks; 1000
+    ranges over 135 chunks leaves most ranges empty."""
     L = [700, 2048, 31, 1500]
     pg = W.paged(len(L), 8, 2, 128, 16, L, seed=220)
     o, lse = run_decode(pg, num_splits=num_splits)
     ro, rl = oracle.decode_paged(pg.q, pg.k_cache, pg.v_cache, pg.block_table, pg.seq_lens, pg.scale)
     assert_o_close(o, ro)
     assert_lse_close(lse, rl)
+
+
+def test_many_sequences_and_head_groups():
+    """150 sequences (the schedule scans lengths 64 at a time) and Hkv = 16
+    (two workgroups of 8 KV heads per range)."""
+    rng = np.random.default_rng(250)
+    L = rng.integers(1, 300, size=150).tolist()
+    pg = W.paged(len(L), 32, 16, 128, 16, L, seed=250)
+    o, lse = run_decode(pg, num_splits=37)
+    ro, rl = oracle.decode_paged(pg.q, pg.k_cache, pg.v_cache, pg.block_table, pg.seq_lens, pg.scale)
+    assert_o_close(o, ro)
+    assert_lse_close(lse, rl)
+
+
+def test_lengths_clamped_to_capacity():
+    """seq_lens beyond max_pages_per_seq * page_size attend to the whole table
+    (full tables here, so no poisoned slot is in range)."""
+    L = [112, 112, 112]
+    pg = W.paged(len(L), 8, 2, 128, 16, L, seed=260)
+    cap = pg.block_table.shape[1] * 16
+    assert cap == 112 and (pg.block_table >= 0).all()
+    big = W.Paged(pg.q, pg.k_cache, pg.v_cache, pg.block_table, np.array([cap + 5, 1 << 30, cap], np.int32), 16,
+                  pg.scale)
+    o1, l1 = run_decode(pg)
+    o2, l2 = run_decode(big)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    ro, rl = oracle.decode_paged(pg.q, pg.k_cache, pg.v_cache, pg.block_table, pg.seq_lens, pg.scale)
+    assert_o_close(o1, ro)
+    assert_lse_close(l1, rl)
 
 
 def test_empty_sequence():
