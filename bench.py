@@ -36,10 +36,11 @@ METRIC = "attn fwd TFLOP/s (bf16 d=128 8K causal) + paged decode HBM GB/s"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
-# HBM bytes measured by rocprofv3 (FETCH_SIZE + WRITE_SIZE) per launch, scaled by
-# the copy-kernel calibration factor; None until measured for the current kernels.
-TRAFFIC_PREFILL = None
-TRAFFIC_DECODE = None
+# HBM bytes per launch measured by rocprofv3 (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0,
+# the factors a plain 1 GiB copy reads); None until measured for the current
+# kernels. Sources: profiles/*_counters.md.
+TRAFFIC_PREFILL = 617_316_352    # fwd_bf16_kernel<128, causal>: 234,863 KiB fetched, 133,122 KiB written
+TRAFFIC_DECODE = 4_866_152_448   # decode_split_kernel<4> + combine: 2,373,145 KiB fetched, 5,812 KiB written
 
 
 def parse():
