@@ -39,7 +39,7 @@ PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 # HBM bytes per launch measured by rocprofv3 (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0,
 # the factors a plain 1 GiB copy reads); None until measured for the current
 # kernels. Sources: profiles/*_counters.md.
-TRAFFIC_PREFILL = 617_316_352    # fwd_bf16_kernel<128, causal>: 234,863 KiB fetched, 133,122 KiB written
+TRAFFIC_PREFILL = None           # fwd_pp_kernel<128, causal>: not yet measured
 TRAFFIC_DECODE = 4_866_152_448   # decode_split_kernel<4> + combine: 2,373,145 KiB fetched, 5,812 KiB written
 
 
@@ -238,7 +238,7 @@ def main():
                           "tflops_best": flops / (t_pf.min() * 1e-3) / 1e12, "flop_per_launch": flops}
         out["roofline"] = {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                            "frac": tf / PEAK_BF16_TFLOPS, "traffic": TRAFFIC_PREFILL,
-                           "kernel": "ea::fwd_bf16_kernel<128, causal>"}
+                           "kernel": "ea::fwd_pp_kernel<128, causal>"}
     if run_decode:
         t_dc = np.array([e[2].elapsed_time(e[3]) for e in evs])
         nbytes = decode_bytes(pg.seq_lens, Hq, Hkv, dd, pg.page_size)

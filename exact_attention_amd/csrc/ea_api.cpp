@@ -40,7 +40,21 @@ ea_status check_tuning(const ea_fwd_tuning* t) {
     return fail(EA_ERR_INVALID, "tuning.rescale_log2 must be in [0, 16]");
   if (t->natural_order != 0 && t->natural_order != 1)
     return fail(EA_ERR_INVALID, "tuning.natural_order must be 0 or 1");
+  if (t->kernel < EA_FWD_KERNEL_AUTO || t->kernel > EA_FWD_KERNEL_PINGPONG)
+    return fail(EA_ERR_INVALID, "tuning.kernel must be 0, 1 or 2");
   return EA_OK;
+}
+
+// The ping-pong kernel covers 256-row blocks, the 4-wave kernel 128-row
+// blocks; a.n_mb arrives counted in 128-row blocks.
+hipError_t dispatch_fwd(ea::FwdArgs a, int d, bool causal, bool varlen, const ea_fwd_tuning& tt,
+                        hipStream_t s) {
+  const bool pp = tt.kernel == EA_FWD_KERNEL_PINGPONG || (tt.kernel == EA_FWD_KERNEL_AUTO && d == 128);
+  if (pp) {
+    a.n_mb = (a.n_mb + 1) / 2;
+    return ea::launch_fwd_pp(a, d, causal, varlen, tt.exp_mode, s);
+  }
+  return ea::launch_fwd(a, d, causal, varlen, tt.exp_mode, s);
 }
 
 }  // namespace
@@ -56,6 +70,7 @@ void ea_fwd_tuning_default(ea_fwd_tuning* t) {
   t->exp_mode = EA_EXP_HW;
   t->rescale_log2 = 8.0f;
   t->natural_order = 0;
+  t->kernel = EA_FWD_KERNEL_AUTO;
 }
 
 ea_status ea_attn_fwd_tuned(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -95,7 +110,7 @@ ea_status ea_attn_fwd_tuned(const void* q, const void* k, const void* v, void* o
   a.scale_log2 = scale * 1.4426950408889634f;
   a.tau = tt.rescale_log2;
   a.natural = tt.natural_order;
-  return hip_status(ea::launch_fwd(a, d, causal != 0, false, tt.exp_mode, (hipStream_t)stream),
+  return hip_status(dispatch_fwd(a, d, causal != 0, false, tt, (hipStream_t)stream),
                     "attention forward launch");
 }
 
@@ -146,7 +161,7 @@ ea_status ea_attn_fwd_varlen(const void* q, const void* k, const void* v, void* 
   a.scale_log2 = scale * 1.4426950408889634f;
   a.tau = tt.rescale_log2;
   a.natural = tt.natural_order;
-  return hip_status(ea::launch_fwd(a, d, causal != 0, true, tt.exp_mode, (hipStream_t)stream),
+  return hip_status(dispatch_fwd(a, d, causal != 0, true, tt, (hipStream_t)stream),
                     "varlen attention forward launch");
 }
 

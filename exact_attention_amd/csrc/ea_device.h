@@ -150,6 +150,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ i32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
 }
+// LDS DMA: 16 bytes per lane from the buffer at voff into LDS; lane s lands at
+// lds + 16 s (lds must be wave-uniform). Out-of-range lanes write zeros.
+__device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, EA_LDS void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, (int)voff, 0, 0, 0);
+}
 
 __device__ __forceinline__ i16x4 ds_read_tr16(const EA_LDS uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((EA_LDS i16x4*)p);

@@ -26,11 +26,15 @@ struct FwdArgs {
 
 constexpr int kFwdBlockM = 128;  // query rows per workgroup (4 waves x 32)
 constexpr int kFwdBlockN = 64;   // keys per K/V tile
+constexpr int kPpBlockM = 256;   // query rows per workgroup of the 8-wave ping-pong kernel
 
 // grid size for the forward (workgroups)
 int fwd_grid(const FwdArgs& a, bool varlen);
 hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, bool varlen, int exp_mode,
                       hipStream_t s);
+// 8-wave ping-pong forward; a.n_mb counts kPpBlockM-row blocks
+hipError_t launch_fwd_pp(const FwdArgs& a, int d, bool causal, bool varlen, int exp_mode,
+                         hipStream_t s);
 
 // MX fp8 forward
 struct Mx8Args {

@@ -69,7 +69,16 @@ typedef struct {
                               increase. Must be in [0, 16]. Default 8.0. */
   int natural_order;       /* 0 (default): causal tiles heaviest first; 1: tiles
                               in ascending row-block order. */
+  int kernel;              /* EA_FWD_KERNEL_*: which forward kernel runs.
+                              Default EA_FWD_KERNEL_AUTO. */
 } ea_fwd_tuning;
+
+/* Forward kernels (same results up to rounding order):
+ *   EA_FWD_KERNEL_AUTO      the ping-pong kernel for d = 128, else the 4-wave one
+ *   EA_FWD_KERNEL_4WAVE     4 waves x 32 query rows, two workgroups per CU
+ *   EA_FWD_KERNEL_PINGPONG  8 waves x 32 rows in two groups that alternate
+ *                           matrix products and softmax on each SIMD */
+enum { EA_FWD_KERNEL_AUTO = 0, EA_FWD_KERNEL_4WAVE = 1, EA_FWD_KERNEL_PINGPONG = 2 };
 
 /* Default tuning values. */
 void ea_fwd_tuning_default(ea_fwd_tuning* t);

@@ -54,12 +54,18 @@ SHAPES = [
 ]
 
 
+# 1: the 4-wave kernel, 2: the 8-wave ping-pong kernel (each against the oracle)
+KERNELS = [1, 2]
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("shape", SHAPES)
-def test_shapes(shape):
+def test_shapes(shape, kernel):
+    import exact_attention_amd as ea
     B, Nq, Nk, Hq, Hkv, d, causal = shape
-    log(f"fwd shape {shape}")
+    log(f"fwd shape {shape} kernel {kernel}")
     inp = W.dense(B, Nq, Nk, Hq, Hkv, d, causal, seed=77 + Nq + Nk)
-    check_full(inp)
+    check_full(inp, tuning=ea.tuning(kernel=kernel))
 
 
 def _rows(inp, b, h, rows):
@@ -125,22 +131,26 @@ def run_varlen(inp, poison_rows=0, tuning=None):
     return f64(host_bits(o))[:Tq], lse.cpu().numpy().astype(np.float64)[:, :Tq]
 
 
+@pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("causal", [True, False])
-def test_varlen_small_with_poison(causal):
+def test_varlen_small_with_poison(causal, kernel):
+    import exact_attention_amd as ea
     L = [1, 129, 300, 64, 1000, 17]
     inp = W.varlen(L, L, 4, 2, 128, causal, seed=90)
-    log(f"fwd varlen lengths={L} causal={causal}")
-    o, lse = run_varlen(inp, poison_rows=70)
+    log(f"fwd varlen lengths={L} causal={causal} kernel={kernel}")
+    o, lse = run_varlen(inp, poison_rows=70, tuning=ea.tuning(kernel=kernel))
     ro, rl = oracle.attention_varlen(f64(inp.q), f64(inp.k), f64(inp.v), inp.cu_q, inp.cu_k, causal, inp.scale)
     assert_o_close(o, ro)
     assert_lse_close(lse, rl)
 
 
-def test_varlen_rectangular_lengths():
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_varlen_rectangular_lengths(kernel):
+    import exact_attention_amd as ea
     Lq = [5, 200, 64]
     Lk = [40, 260, 64]
     inp = W.varlen(Lq, Lk, 2, 2, 64, True, seed=91)
-    o, lse = run_varlen(inp)
+    o, lse = run_varlen(inp, tuning=ea.tuning(kernel=kernel))
     ro, rl = oracle.attention_varlen(f64(inp.q), f64(inp.k), f64(inp.v), inp.cu_q, inp.cu_k, True, inp.scale)
     assert_o_close(o, ro)
     assert_lse_close(lse, rl)
@@ -173,13 +183,18 @@ def test_determinism_and_order_invariance():
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
     o3, l3 = run_dense(inp, tuning=ea.tuning(natural_order=1))
     assert np.array_equal(o1, o3) and np.array_equal(l1, l3)
+    # the 4-wave kernel is deterministic and order-invariant too
+    o4, l4 = run_dense(inp, tuning=ea.tuning(kernel=1))
+    o5, l5 = run_dense(inp, tuning=ea.tuning(kernel=1, natural_order=1))
+    assert np.array_equal(o4, o5) and np.array_equal(l4, l5)
 
 
+@pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("mode", [1, 2])
-def test_exp_modes(mode):
+def test_exp_modes(mode, kernel):
     import exact_attention_amd as ea
     inp = W.dense(2, 700, 700, 2, 2, 128, True, seed=93)
-    check_full(inp, tuning=ea.tuning(exp_mode=mode))
+    check_full(inp, tuning=ea.tuning(exp_mode=mode, kernel=kernel))
 
 
 def test_eager_rescale_matches():
