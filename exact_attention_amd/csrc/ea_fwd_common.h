@@ -1,0 +1,65 @@
+// Device helpers shared by the gfx950 forward kernels that stage K/V through
+// LDS DMA and pace their waves with workgroup barriers.
+//
+// The helpers that wrap asm statements or scheduling builtins are device
+// functions on purpose: written directly inside a kernel's lambda, target
+// builtins and register constraints are also checked in the host compilation
+// pass, and that failure silently drops the host-side kernel stub.
+#pragma once
+#include "ea_device.h"
+
+namespace ea {
+namespace {
+
+// s_waitcnt with only the vector-memory counter set (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier that neither the compiler nor the scheduler moves memory
+// operations across, and that adds no wait of its own (a __syncthreads would
+// also wait for the DMA still in flight).
+__device__ __forceinline__ void pp_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// keeps the instructions on either side in program order
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+// the value must exist here (stops the compiler sinking its computation)
+__device__ __forceinline__ void keep(const f32x16& x) { asm volatile("" ::"v"(x)); }
+__device__ __forceinline__ void keep(const bf16x8& x) { asm volatile("" ::"v"(x)); }
+__device__ __forceinline__ void keep(float x) { asm volatile("" ::"v"(x)); }
+// the compiler forgets where x came from (stops it hoisting x + constant out
+// of a loop, so a constant added to it later folds into an LDS offset field)
+__device__ __forceinline__ int launder(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// elements B .. B+7 of a score accumulator, rounded to bf16 and packed as an
+// MFMA operand
+template <int B>
+__device__ __forceinline__ bf16x8 pack_p8(const f32x16 v) {
+  const i32x4 t = {(int)pack_bf16x2(v[B + 0], v[B + 1]), (int)pack_bf16x2(v[B + 2], v[B + 3]),
+                   (int)pack_bf16x2(v[B + 4], v[B + 5]), (int)pack_bf16x2(v[B + 6], v[B + 7])};
+  return __builtin_bit_cast(bf16x8, t);
+}
+
+template <int EXPMODE>
+__device__ __forceinline__ float pp_exp2(float x, int i) {
+  if constexpr (EXPMODE == 0) {
+    return exp2_hw(x);
+  } else if constexpr (EXPMODE == 1) {
+    return exp2_poly(x);
+  } else {
+    return ((i & 3) == 3) ? exp2_poly(x) : exp2_hw(x);
+  }
+}
+
+}  // namespace
+}  // namespace ea

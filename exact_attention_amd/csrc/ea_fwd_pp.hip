@@ -36,48 +36,10 @@
 //  * Operand layouts (S^T = K Q^T, P^T passed in registers to O^T = V^T P^T,
 //    V^T from ds_read_b64_tr_b16) are those of the 4-wave kernel.
 #include "ea_device.h"
+#include "ea_fwd_common.h"
 #include "ea_internal.h"
 
 namespace ea {
-
-namespace {
-// s_waitcnt with only the vector-memory counter set (gfx9 encoding: vmcnt in
-// bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier that neither the compiler nor the scheduler moves memory
-// operations across, and that adds no wait of its own (a __syncthreads would
-// also wait for the DMA still in flight).
-__device__ __forceinline__ void pp_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_barrier" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-// elements B .. B+7 of a score accumulator, rounded to bf16 and packed as an
-// MFMA operand
-template <int B>
-__device__ __forceinline__ bf16x8 pack_p8(const f32x16 v) {
-  const i32x4 t = {(int)pack_bf16x2(v[B + 0], v[B + 1]), (int)pack_bf16x2(v[B + 2], v[B + 3]),
-                   (int)pack_bf16x2(v[B + 4], v[B + 5]), (int)pack_bf16x2(v[B + 6], v[B + 7])};
-  return __builtin_bit_cast(bf16x8, t);
-}
-
-template <int EXPMODE>
-__device__ __forceinline__ float pp_exp2(float x, int i) {
-  if constexpr (EXPMODE == 0) {
-    return exp2_hw(x);
-  } else if constexpr (EXPMODE == 1) {
-    return exp2_poly(x);
-  } else {
-    return ((i & 3) == 3) ? exp2_poly(x) : exp2_hw(x);
-  }
-}
-}  // namespace
 
 template <int D, bool CAUSAL, bool VARLEN, int EXPMODE>
 __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
@@ -232,14 +194,12 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     int ko[D / 16], vo[NDT][2];
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      ko[kk] = k_off[kk];
-      asm volatile("" : "+v"(ko[kk]));
+      ko[kk] = launder(k_off[kk]);
     }
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      vo[dt][0] = v_off[dt][0];
-      vo[dt][1] = v_off[dt][1];
-      asm volatile("" : "+v"(vo[dt][0]), "+v"(vo[dt][1]));
+      vo[dt][0] = launder(v_off[dt][0]);
+      vo[dt][1] = launder(v_off[dt][1]);
     }
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
