@@ -39,7 +39,7 @@ PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 # HBM bytes per launch measured by rocprofv3 (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0,
 # the factors a plain 1 GiB copy reads); None until measured for the current
 # kernels. Sources: profiles/*_counters.md.
-TRAFFIC_PREFILL = None           # fwd_pp_kernel<128, causal>: not yet measured
+TRAFFIC_PREFILL = 582_522_880    # fwd_pp_kernel<128, causal>: 217,698 KiB fetched, 133,474 KiB written
 TRAFFIC_DECODE = 4_866_152_448   # decode_split_kernel<4> + combine: 2,373,145 KiB fetched, 5,812 KiB written
 
 
