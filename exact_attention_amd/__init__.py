@@ -23,7 +23,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libexactattn.so")
 
 EA_EXP_HW, EA_EXP_POLY, EA_EXP_HYBRID = 0, 1, 2
-EA_FWD_KERNEL_AUTO, EA_FWD_KERNEL_4WAVE, EA_FWD_KERNEL_PINGPONG = 0, 1, 2
+EA_FWD_KERNEL_AUTO, EA_FWD_KERNEL_4WAVE, EA_FWD_KERNEL_PINGPONG, EA_FWD_KERNEL_PIPELINED = 0, 1, 2, 3
 
 _c_int, _c_float, _c_void_p, _c_size_t = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
@@ -102,7 +102,8 @@ def default_tuning() -> FwdTuning:
 
 def tuning(exp_mode: int = EA_EXP_HW, rescale_log2: float = 8.0, natural_order: int = 0,
            kernel: int = 0) -> FwdTuning:
-    """Forward tuning; kernel: 0 auto, 1 the 4-wave kernel, 2 the 8-wave ping-pong kernel."""
+    """Forward tuning; kernel: 0 auto, 1 the 4-wave kernel, 2 the 8-wave ping-pong kernel,
+    3 the 8-wave software-pipelined kernel."""
     return FwdTuning(exp_mode, rescale_log2, natural_order, kernel)
 
 

@@ -40,15 +40,19 @@ ea_status check_tuning(const ea_fwd_tuning* t) {
     return fail(EA_ERR_INVALID, "tuning.rescale_log2 must be in [0, 16]");
   if (t->natural_order != 0 && t->natural_order != 1)
     return fail(EA_ERR_INVALID, "tuning.natural_order must be 0 or 1");
-  if (t->kernel < EA_FWD_KERNEL_AUTO || t->kernel > EA_FWD_KERNEL_PINGPONG)
-    return fail(EA_ERR_INVALID, "tuning.kernel must be 0, 1 or 2");
+  if (t->kernel < EA_FWD_KERNEL_AUTO || t->kernel > EA_FWD_KERNEL_PIPELINED)
+    return fail(EA_ERR_INVALID, "tuning.kernel must be 0, 1, 2 or 3");
   return EA_OK;
 }
 
-// The ping-pong kernel covers 256-row blocks, the 4-wave kernel 128-row
-// blocks; a.n_mb arrives counted in 128-row blocks.
+// The 8-wave kernels cover 256-row blocks, the 4-wave kernel 128-row blocks;
+// a.n_mb arrives counted in 128-row blocks.
 hipError_t dispatch_fwd(ea::FwdArgs a, int d, bool causal, bool varlen, const ea_fwd_tuning& tt,
                         hipStream_t s) {
+  if (tt.kernel == EA_FWD_KERNEL_PIPELINED) {
+    a.n_mb = (a.n_mb + 1) / 2;
+    return ea::launch_fwd_sp(a, d, causal, varlen, tt.exp_mode, s);
+  }
   const bool pp = tt.kernel == EA_FWD_KERNEL_PINGPONG || (tt.kernel == EA_FWD_KERNEL_AUTO && d == 128);
   if (pp) {
     a.n_mb = (a.n_mb + 1) / 2;

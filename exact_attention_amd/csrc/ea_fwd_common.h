@@ -34,6 +34,12 @@ __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0
 __device__ __forceinline__ void keep(const f32x16& x) { asm volatile("" ::"v"(x)); }
 __device__ __forceinline__ void keep(const bf16x8& x) { asm volatile("" ::"v"(x)); }
 __device__ __forceinline__ void keep(float x) { asm volatile("" ::"v"(x)); }
+// x, computed here: the compiler may no longer move its computation under a
+// branch that uses it
+__device__ __forceinline__ float keep_val(float x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 // the compiler forgets where x came from (stops it hoisting x + constant out
 // of a loop, so a constant added to it later folds into an LDS offset field)
 __device__ __forceinline__ int launder(int x) {

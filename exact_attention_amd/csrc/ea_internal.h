@@ -35,6 +35,9 @@ hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, bool varlen, int exp
 // 8-wave ping-pong forward; a.n_mb counts kPpBlockM-row blocks
 hipError_t launch_fwd_pp(const FwdArgs& a, int d, bool causal, bool varlen, int exp_mode,
                          hipStream_t s);
+// 8-wave software-pipelined forward; a.n_mb counts kPpBlockM-row blocks
+hipError_t launch_fwd_sp(const FwdArgs& a, int d, bool causal, bool varlen, int exp_mode,
+                         hipStream_t s);
 
 // MX fp8 forward
 struct Mx8Args {

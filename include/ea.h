@@ -77,8 +77,16 @@ typedef struct {
  *   EA_FWD_KERNEL_AUTO      the ping-pong kernel for d = 128, else the 4-wave one
  *   EA_FWD_KERNEL_4WAVE     4 waves x 32 query rows, two workgroups per CU
  *   EA_FWD_KERNEL_PINGPONG  8 waves x 32 rows in two groups that alternate
- *                           matrix products and softmax on each SIMD */
-enum { EA_FWD_KERNEL_AUTO = 0, EA_FWD_KERNEL_4WAVE = 1, EA_FWD_KERNEL_PINGPONG = 2 };
+ *                           matrix products and softmax on each SIMD
+ *   EA_FWD_KERNEL_PIPELINED 8 waves x 32 rows, each wave overlapping the
+ *                           softmax of one tile with its own matrix products
+ *                           of the next and previous tiles */
+enum {
+  EA_FWD_KERNEL_AUTO = 0,
+  EA_FWD_KERNEL_4WAVE = 1,
+  EA_FWD_KERNEL_PINGPONG = 2,
+  EA_FWD_KERNEL_PIPELINED = 3
+};
 
 /* Default tuning values. */
 void ea_fwd_tuning_default(ea_fwd_tuning* t);

@@ -64,7 +64,7 @@ def test_tuning_errors(lib):
     assert lib.ea_attn_fwd_tuned(P, P, P, P, None, 1, 8, 8, 2, 2, 128, 0, 0.1, ctypes.byref(t), None) == -1
     t = ea.tuning(rescale_log2=-1.0)
     assert lib.ea_attn_fwd_tuned(P, P, P, P, None, 1, 8, 8, 2, 2, 128, 0, 0.1, ctypes.byref(t), None) == -1
-    t = ea.tuning(kernel=3)
+    t = ea.tuning(kernel=4)
     assert lib.ea_attn_fwd_tuned(P, P, P, P, None, 1, 8, 8, 2, 2, 128, 0, 0.1, ctypes.byref(t), None) == -1
     d = ea.default_tuning()
     assert d.exp_mode == 0 and d.rescale_log2 == 8.0 and d.natural_order == 0 and d.kernel == 0

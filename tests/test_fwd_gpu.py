@@ -55,7 +55,7 @@ SHAPES = [
 
 
 # 1: the 4-wave kernel, 2: the 8-wave ping-pong kernel (each against the oracle)
-KERNELS = [1, 2]
+KERNELS = [1, 2, 3]
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
@@ -187,6 +187,10 @@ def test_determinism_and_order_invariance():
     o4, l4 = run_dense(inp, tuning=ea.tuning(kernel=1))
     o5, l5 = run_dense(inp, tuning=ea.tuning(kernel=1, natural_order=1))
     assert np.array_equal(o4, o5) and np.array_equal(l4, l5)
+    # and so is the software-pipelined one
+    o6, l6 = run_dense(inp, tuning=ea.tuning(kernel=3))
+    o7, l7 = run_dense(inp, tuning=ea.tuning(kernel=3, natural_order=1))
+    assert np.array_equal(o6, o7) and np.array_equal(l6, l7)
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
