@@ -169,10 +169,10 @@ ea_status ea_attn_fwd_varlen(const void* q, const void* k, const void* v, void* 
                     "varlen attention forward launch");
 }
 
-ea_status ea_attn_fwd_mx8(const void* q8, const void* k8, const void* v8, const uint8_t* q_scale,
-                          const uint8_t* k_scale, const uint8_t* v_scale, void* o, float* lse,
-                          int B, int N, int Hq, int Hkv, int d, int causal, float scale,
-                          void* stream) {
+ea_status ea_attn_fwd_mx8_tuned(const void* q8, const void* k8, const void* v8, const uint8_t* q_scale,
+                                const uint8_t* k_scale, const uint8_t* v_scale, void* o, float* lse,
+                                int B, int N, int Hq, int Hkv, int d, int causal, float scale,
+                                const ea_fwd_tuning* tuning, void* stream) {
   if (!q8 || !k8 || !v8 || !q_scale || !k_scale || !v_scale || !o)
     return fail(EA_ERR_INVALID, "tensor pointers must be non-null");
   if (B <= 0 || N <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0)
@@ -183,6 +183,17 @@ ea_status ea_attn_fwd_mx8(const void* q8, const void* k8, const void* v8, const 
   if (!finite_pos(scale)) return fail(EA_ERR_INVALID, "scale must be finite and positive");
   if (causal != 0 && causal != 1) return fail(EA_ERR_INVALID, "causal must be 0 or 1");
   if ((long long)B * N >= (1LL << 31)) return fail(EA_ERR_UNSUPPORTED, "B * N must be below 2^31");
+  if (ea_status st = check_tuning(tuning); st != EA_OK) return st;
+  ea_fwd_tuning tt;
+  ea_fwd_tuning_default(&tt);
+  if (tuning != nullptr) tt = *tuning;
+  if (tt.exp_mode != EA_EXP_HW || tt.natural_order != 0)
+    return fail(EA_ERR_UNSUPPORTED, "MX fp8 forward: hardware exponential and heaviest-first order only");
+  if (tt.kernel == EA_FWD_KERNEL_PINGPONG)
+    return fail(EA_ERR_UNSUPPORTED, "MX fp8 forward has no ping-pong kernel (kernel 0, 1 or 3)");
+  // the pipelined kernel is the faster one on fp8 (its products are cheap
+  // next to the softmax, which it overlaps with them)
+  const bool pipelined = tt.kernel != EA_FWD_KERNEL_4WAVE;
   ea::Mx8Args a{};
   a.q = (const uint8_t*)q8;
   a.k = (const uint8_t*)k8;
@@ -197,10 +208,21 @@ ea_status ea_attn_fwd_mx8(const void* q8, const void* k8, const void* v8, const 
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.group = Hq / Hkv;
-  a.n_mb = (N + ea::kFwdBlockM - 1) / ea::kFwdBlockM;
+  const int bm = pipelined ? ea::kPpBlockM : ea::kFwdBlockM;
+  a.n_mb = (N + bm - 1) / bm;
   a.scale_log2 = scale * 1.4426950408889634f;
-  a.tau = 8.0f;
-  return hip_status(ea::launch_fwd_mx8(a, causal != 0, (hipStream_t)stream), "MX fp8 forward launch");
+  a.tau = tt.rescale_log2;
+  const hipError_t e = pipelined ? ea::launch_fwd_mx8_sp(a, causal != 0, (hipStream_t)stream)
+                                 : ea::launch_fwd_mx8(a, causal != 0, (hipStream_t)stream);
+  return hip_status(e, "MX fp8 forward launch");
+}
+
+ea_status ea_attn_fwd_mx8(const void* q8, const void* k8, const void* v8, const uint8_t* q_scale,
+                          const uint8_t* k_scale, const uint8_t* v_scale, void* o, float* lse,
+                          int B, int N, int Hq, int Hkv, int d, int causal, float scale,
+                          void* stream) {
+  return ea_attn_fwd_mx8_tuned(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, N, Hq, Hkv, d, causal,
+                               scale, nullptr, stream);
 }
 
 }  // extern "C"

@@ -22,6 +22,7 @@
 // read from the row-major V tile with ds_read_b64_tr_b8 using the same key
 // permutation.
 #include "ea_device.h"
+#include "ea_fwd_common.h"
 #include "ea_internal.h"
 
 namespace ea {
@@ -56,6 +57,9 @@ __device__ __forceinline__ int pack_fp8x4(float x0, float x1, float x2, float x3
 }
 
 constexpr int kScaleOne = 127;  // e8m0 encoding of 1.0
+
+// the value must exist here (see keep() in ea_fwd_common.h)
+__device__ __forceinline__ void keep8(const i32x8& x) { asm volatile("" ::"v"(x)); }
 
 }  // namespace
 
@@ -310,6 +314,396 @@ __global__ __launch_bounds__(256, 2) void fwd_mx8_kernel(Mx8Args a) {
       a.lse[((size_t)b * a.Hq + h) * N + qi] = v;
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Software-pipelined 8-wave variant (same method and numerics as above; this
+// file's own scheduling design). The fp8 products are twice as fast as bf16
+// ones while the softmax costs the same, so a wave that runs them one after
+// the other waits on each in turn. Here each wave issues, in one
+// straight-line block per step, the MX MFMAs of S_{s+1} = K_{s+1} Q^T and of
+// O += V_{s-1} P_{s-1} interleaved with the softmax of S_s (nothing in the
+// block depends on anything else in it), in eight fenced slots of one MFMA
+// each. 8 waves x 32 query rows; K/V tiles (64 keys x 128 bytes) arrive by
+// LDS DMA into three stages per operand; the K scales of the next tile and
+// the V scales of the current one are loaded a step ahead into registers.
+// Masking runs before the block under a branch (diagonal and ragged tiles,
+// and tiles past a wave's causal limit), the lazy O rescale after it.
+template <bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void fwd_mx8_sp_kernel(Mx8Args a) {
+  constexpr int D = 128, BM = kPpBlockM, BN = kFwdBlockN;
+  constexpr int TILE = BN * D;  // bytes per K or V tile
+  constexpr int NDT = D / 32;
+  static_assert(TILE == 8 * 1024, "one 1 KB DMA piece per wave per tile");
+  __shared__ __attribute__((aligned(1024))) uint8_t ks0[TILE], ks1[TILE], ks2[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs0[TILE], vs1[TILE], vs2[TILE];
+
+  // ---------------- tile assignment: XCD-grouped, heaviest causal row blocks first
+  const int xcd = blockIdx.x & 7;
+  const int j = blockIdx.x >> 3;
+  const int kg = j / a.n_mb;
+  const int r0 = j - kg * a.n_mb;
+  const int g = xcd + 8 * kg;
+  if (g >= a.B * a.Hq) return;
+  const int b = uniform(g / a.Hq);
+  const int h = uniform(g - b * a.Hq);
+  const int mb = uniform(a.n_mb - 1 - r0);
+  const int hk = uniform(h / a.group);
+  const int N = a.N;
+  const int row_lo = mb * BM;
+  int nkeys = N;
+  if constexpr (CAUSAL) nkeys = min(N, row_lo + BM);
+  const int nkb = uniform((nkeys + BN - 1) / BN);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = uniform(tid >> 6), hh = lane >> 5, c = lane & 31;
+  const int wave_first_q = row_lo + w * 32;
+  const int qi = wave_first_q + c;
+  const size_t qstride = (size_t)a.Hq * D, kstride = (size_t)a.Hkv * D;
+
+  // ---------------- Q^T operand and its scales (B of S^T), kept in VGPRs
+  i32x8 qf[2];
+  int qsc[2];
+  {
+    const uint8_t* qp = a.q + ((size_t)b * N + qi) * qstride + (size_t)h * D;
+    uint32_t s4 = 0x7f7f7f7fu;
+    if (qi < N) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const i32x4 lo = *(const i32x4*)(qp + 64 * ks + 16 * hh);
+        const i32x4 hi = *(const i32x4*)(qp + 64 * ks + 32 + 16 * hh);
+        qf[ks] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+      s4 = *(const uint32_t*)(a.qs + (((size_t)b * N + qi) * a.Hq + h) * 4);
+    } else {
+      qf[0] = i32x8{};
+      qf[1] = i32x8{};
+    }
+    qsc[0] = (s4 >> (8 * hh)) & 0xFF;
+    qsc[1] = (s4 >> (8 * (2 + hh))) & 0xFF;
+  }
+
+  // ---------------- K/V DMA: wave w fills 1 KB piece w of a tile. Lane s
+  // lands at tile byte 1024 w + 16 s = row 8 w + s / 8, slot s % 8; it fetches
+  // the global chunk (s % 8) ^ swz8(row) of that row. A tile at or past nkb
+  // gets no records, so its DMA writes zeros without touching memory; only
+  // the last tile can be partial.
+  const uint8_t* kg_base = a.k + ((size_t)b * N) * kstride + (size_t)hk * D;
+  const uint8_t* vg_base = a.v + ((size_t)b * N) * kstride + (size_t)hk * D;
+  const int drow = 8 * w + (lane >> 3);
+  const uint32_t dma_off = (uint32_t)(drow * (int)kstride + (((lane & 7) ^ swz8(drow)) << 4));
+  const uint32_t nrec_full = (uint32_t)uniform((BN - 1) * (int)kstride + D);
+  const uint32_t nrec_last = (uint32_t)uniform(nkb > 0 ? (min(N - (nkb - 1) * BN, BN) - 1) * (int)kstride + D : 0);
+  auto tile_rsrc = [&](const uint8_t* gbase, int t) __attribute__((always_inline)) {
+    const uint32_t nrec = t < nkb - 1 ? nrec_full : (t == nkb - 1 ? nrec_last : 0u);
+    return make_rsrc(gbase + (size_t)t * (BN * kstride), nrec);
+  };
+  auto kstage = [&](int r) __attribute__((always_inline)) -> EA_LDS uint8_t* {
+    return r == 0 ? (EA_LDS uint8_t*)ks0 : r == 1 ? (EA_LDS uint8_t*)ks1 : (EA_LDS uint8_t*)ks2;
+  };
+  auto vstage = [&](int r) __attribute__((always_inline)) -> EA_LDS uint8_t* {
+    return r == 0 ? (EA_LDS uint8_t*)vs0 : r == 1 ? (EA_LDS uint8_t*)vs1 : (EA_LDS uint8_t*)vs2;
+  };
+  auto dma_issue = [&](EA_LDS uint8_t* stage, __amdgpu_buffer_rsrc_t rs) __attribute__((always_inline)) {
+    buffer_load16_lds(rs, (EA_LDS void*)(stage + 1024 * w), dma_off);
+  };
+
+  // ---------------- scales: K scale dwords of keys 64 t + c and 64 t + 32 + c,
+  // V scale bytes of key block 2 t + hh, columns 32 dt + c (zero past the end)
+  const uint8_t* ksc_base = a.ks + ((size_t)b * N * a.Hkv + hk) * 4;
+  const int nkb32 = N / 32;
+  const uint8_t* vsc_base = a.vs + ((size_t)b * nkb32 * a.Hkv + hk) * D;
+  const __amdgpu_buffer_rsrc_t rs_ksc = make_rsrc(ksc_base, (uint32_t)((N - 1) * a.Hkv * 4 + 4));
+  const __amdgpu_buffer_rsrc_t rs_vsc = make_rsrc(vsc_base, (uint32_t)((nkb32 - 1) * a.Hkv * D + D));
+  auto load_kscale = [&](int t, uint32_t (&dst)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      dst[u] = __builtin_amdgcn_raw_buffer_load_b32(rs_ksc, (t * BN + 32 * u + c) * a.Hkv * 4, 0, 0);
+  };
+  auto load_vscale = [&](int t, uint32_t (&dst)[NDT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+      dst[dt] = __builtin_amdgcn_raw_buffer_load_b8(rs_vsc, (2 * t + hh) * a.Hkv * D + 32 * dt + c, 0, 0);
+  };
+
+  // loop-invariant LDS byte offsets: K operand (rows c, c + 32; chunks
+  // 4*ks + hh and 4*ks + 2 + hh) and V^T transposed reads
+  int k_off[2][2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    k_off[ks][0] = tile8_off(c, 64 * ks + 16 * hh);
+    k_off[ks][1] = tile8_off(c, 64 * ks + 32 + 16 * hh);
+  }
+  const int jj = (lane & 15) >> 1;
+  const int tr_row = 4 * hh + jj + 4 * (jj >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+  int v_off[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) v_off[dt] = tile8_off(tr_row, 32 * dt + tr_col);
+
+  float m_run = kNegInf, l_run = 0.f;
+  f32x16 oacc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16{};
+  f32x16 sc0, sc1;                        // S of the tile whose softmax runs in this step
+  f32x16 sn0 = f32x16{}, sn1 = f32x16{};  // S of the next tile
+  i32x8 pprev = i32x8{}, pcur = i32x8{};  // P^T (e4m3) of the previous tile, of this one
+  uint32_t kraw_cur[2], kraw_nxt[2];      // K scales of tile s + 1 (this step), s + 2
+  uint32_t vraw_cur[NDT], vraw_nxt[NDT];  // V scales of tile s - 1 (this step), s
+  const float sl = a.scale_log2;
+  const float tau = a.tau;
+
+  auto need_mask = [&](int s) __attribute__((always_inline)) {
+    const int kbase = s * BN;
+    bool m = kbase + BN > N;
+    if constexpr (CAUSAL) m = m || (kbase + BN - 1 > wave_first_q);
+    return m;
+  };
+  auto apply_mask = [&](int s) __attribute__((always_inline)) {
+    int lim = N;
+    if constexpr (CAUSAL) lim = min(N, qi + 1);
+    const int rel = lim - s * BN - 4 * hh;  // element i is valid iff its key offset < rel
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int ko = 8 * (i >> 2) + (i & 3);
+      sc0[i] = (ko < rel) ? sc0[i] : kNegInf;
+      sc1[i] = (ko + 32 < rel) ? sc1[i] : kNegInf;
+    }
+  };
+
+  // ---- the pipelined block of step s (stage r = s mod 3): slot j holds MFMA
+  // j (j < 4: S_{s+1} key half j % 2, d half j / 2; j >= 4: PV for d tile
+  // j - 4), the operand reads of the MFMA two slots later, and a share of the
+  // softmax of S_s: the row max (slots 0-1), the rescale test (slot 1), exp2
+  // and the row sum (slots 2-6), the e4m3 packing (slot 7). The scale loads
+  // for the next step go in slot 0, this wave's DMA piece in slot 7.
+  constexpr int NMF = 8, RA = 2, EXPS = 5;
+  float alpha = 1.f;
+  auto block = [&](int r, int s, __amdgpu_buffer_rsrc_t rs_k, __amdgpu_buffer_rsrc_t rs_v)
+                   __attribute__((always_inline)) -> bool {
+    const EA_LDS uint8_t* ks = kstage((r + 1) % 3);
+    const EA_LDS uint8_t* vs = vstage((r + 2) % 3);
+    int ko[2][2], vo[NDT];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      ko[k2][0] = launder(k_off[k2][0]);
+      ko[k2][1] = launder(k_off[k2][1]);
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) vo[dt] = launder(v_off[dt]);
+    int ksc[2][2], vsc[NDT];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) ksc[t][k2] = (kraw_cur[t] >> (8 * (2 * k2 + hh))) & 0xFF;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) vsc[dt] = (int)(vraw_cur[dt] & 0xFF);
+
+    i32x8 opnd[NMF];
+    auto read_operand = [&](int jx) __attribute__((always_inline)) {
+      if (jx < 4) {
+        const int t = jx & 1, k2 = jx >> 1;
+        const i32x4 lo = lds_load<i32x4>(ks + ko[k2][0] + 32 * D * t);
+        const i32x4 hi = lds_load<i32x4>(ks + ko[k2][1] + 32 * D * t);
+        opnd[jx] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      } else {
+        const int dt = jx - 4;
+        const i32x2 q0 = ds_read_tr8(vs + vo[dt]);
+        const i32x2 q1 = ds_read_tr8(vs + vo[dt] + 16 * D);
+        const i32x2 q2 = ds_read_tr8(vs + vo[dt] + 32 * D);
+        const i32x2 q3 = ds_read_tr8(vs + vo[dt] + 48 * D);
+        opnd[jx] = i32x8{q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
+      }
+    };
+    auto elem = [&](int e) __attribute__((always_inline)) -> float { return e < 16 ? sc0[e] : sc1[e - 16]; };
+    auto set_elem = [&](int e, float v) __attribute__((always_inline)) {
+      if (e < 16) {
+        sc0[e] = v;
+      } else {
+        sc1[e - 16] = v;
+      }
+    };
+    auto exp_first = [](int k) { return (32 * k) / EXPS; };
+    float mx0 = kNegInf, mx1 = kNegInf, neg_m = 0.f;
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+    bool resc = false;
+
+#pragma unroll
+    for (int jx = 0; jx < RA; ++jx) read_operand(jx);
+    sched_fence();
+#pragma unroll
+    for (int i = 0; i < NMF; ++i) {
+      if (i + RA < NMF) read_operand(i + RA);
+      if (i < 4) {
+        const int t = i & 1, k2 = i >> 1;
+        if (t) {
+          sn1 = mfma_mx8(opnd[i], qf[k2], k2 == 0 ? f32x16{} : sn1, ksc[1][k2], qsc[k2]);
+        } else {
+          sn0 = mfma_mx8(opnd[i], qf[k2], k2 == 0 ? f32x16{} : sn0, ksc[0][k2], qsc[k2]);
+        }
+      } else {
+        const int dt = i - 4;
+        oacc[dt] = mfma_mx8(opnd[i], pprev, oacc[dt], vsc[dt], kScaleOne);
+      }
+      if (i == 0) {
+        load_kscale(s + 2, kraw_nxt);
+        load_vscale(s, vraw_nxt);
+      }
+      if (i < 2) {
+        // row max over this lane's 32 keys, two chains of max3
+#pragma unroll
+        for (int e = 16 * i; e < 16 * i + 16; e += 4) {
+          mx0 = __builtin_fmaxf(__builtin_fmaxf(mx0, elem(e)), elem(e + 2));
+          mx1 = __builtin_fmaxf(__builtin_fmaxf(mx1, elem(e + 1)), elem(e + 3));
+        }
+      }
+      if (i == 1) {
+        // with the partner lane's 32 keys: the row max; the lazy rescale test;
+        // rows that have seen no key yet keep m = -inf and get alpha = 0
+        const float mx = max_with_partner32(__builtin_fmaxf(mx0, mx1));
+        const float m_new = __builtin_fmaxf(m_run, mx * sl);
+        resc = __ballot(m_new > m_run + tau) != 0;
+        const float a_raw = exp2_hw(m_run - m_new);
+        alpha = resc ? ((m_run == kNegInf) ? 0.f : a_raw) : 1.f;
+        m_run = resc ? m_new : m_run;
+        neg_m = (m_run == kNegInf) ? 0.f : -m_run;
+      } else if (i >= 2 && i < 2 + EXPS) {
+        const int e0 = exp_first(i - 2), e1 = exp_first(i - 1);
+#pragma unroll
+        for (int e = e0; e < e1; ++e) {
+          const float p = exp2_hw(__builtin_fmaf(elem(e), sl, neg_m));
+          set_elem(e, p);
+          ls[e & 3] += p;
+        }
+      } else if (i == NMF - 1) {
+        // P^T -> e4m3 (scale 1): bytes 0..15 key tile 0, 16..31 key tile 1
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) {
+          pcur[wd] = pack_fp8x4(sc0[4 * wd], sc0[4 * wd + 1], sc0[4 * wd + 2], sc0[4 * wd + 3]);
+          pcur[4 + wd] = pack_fp8x4(sc1[4 * wd], sc1[4 * wd + 1], sc1[4 * wd + 2], sc1[4 * wd + 3]);
+        }
+        l_run = l_run * alpha + ((ls[0] + ls[1]) + (ls[2] + ls[3]));
+        // this wave's piece of K_{s+3} (into the stage K_s left) and V_{s+1}
+        // (into the stage V_{s-2} left)
+        dma_issue(kstage(r), rs_k);
+        dma_issue(vstage((r + 1) % 3), rs_v);
+      }
+      sched_fence();
+    }
+    // the softmax results and the next tile's scores must exist inside this
+    // block (the compiler would otherwise sink their computation below the
+    // rescale branch, or into the next step, next to their first use)
+    keep(sn0);
+    keep(sn1);
+    keep8(pcur);
+    keep(l_run);
+    keep(m_run);
+    keep(alpha);
+    return resc;
+  };
+
+  // ---- one step: mask, block, rescale, rotate the pipeline registers, then
+  // retire a stage: everything but this step's two DMA instructions (the
+  // scale loads were issued before them) has landed, and every wave is past
+  // its reads of the stages the next step's DMA overwrites
+  auto step = [&](int r, int s) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t rs_k = tile_rsrc(kg_base, s + 3);
+    const __amdgpu_buffer_rsrc_t rs_v = tile_rsrc(vg_base, s + 1);
+    if (need_mask(s)) apply_mask(s);
+    const bool resc = block(r, s, rs_k, rs_v);
+    if (resc) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+    }
+    sc0 = sn0;
+    sc1 = sn1;
+    pprev = pcur;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) kraw_cur[u] = kraw_nxt[u];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) vraw_cur[dt] = vraw_nxt[dt];
+    wait_vmcnt<2>();
+    pp_barrier();
+  };
+
+  // prologue: K_0, K_1, K_2 and V_0 with the scales of K_0 and K_1; the V
+  // stage that step 0 multiplies by P = 0 is zeroed; S_0 is computed here and
+  // all waves are past their reads of K_0 before step 0 overwrites its stage
+  lds_store<i32x4>((EA_LDS uint8_t*)vs2 + 16 * tid, i32x4{});
+  uint32_t kraw0[2];
+  load_kscale(0, kraw0);
+  load_kscale(1, kraw_cur);
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) vraw_cur[dt] = kScaleOne;
+  // (under a branch: with no tiles there is nothing to fetch, and the wait
+  // tracking then places no full wait at the loop head)
+  if (nkb > 0) {
+    dma_issue(kstage(0), tile_rsrc(kg_base, 0));
+    dma_issue(kstage(1), tile_rsrc(kg_base, 1));
+    dma_issue(kstage(2), tile_rsrc(kg_base, 2));
+    dma_issue(vstage(0), tile_rsrc(vg_base, 0));
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2) {
+    const int s0k = (kraw0[0] >> (8 * (2 * k2 + hh))) & 0xFF;
+    const int s1k = (kraw0[1] >> (8 * (2 * k2 + hh))) & 0xFF;
+    const i32x4 a0l = lds_load<i32x4>((EA_LDS uint8_t*)ks0 + k_off[k2][0]);
+    const i32x4 a0h = lds_load<i32x4>((EA_LDS uint8_t*)ks0 + k_off[k2][1]);
+    const i32x4 a1l = lds_load<i32x4>((EA_LDS uint8_t*)ks0 + k_off[k2][0] + 32 * D);
+    const i32x4 a1h = lds_load<i32x4>((EA_LDS uint8_t*)ks0 + k_off[k2][1] + 32 * D);
+    sc0 = mfma_mx8(i32x8{a0l[0], a0l[1], a0l[2], a0l[3], a0h[0], a0h[1], a0h[2], a0h[3]}, qf[k2],
+                   k2 == 0 ? f32x16{} : sc0, s0k, qsc[k2]);
+    sc1 = mfma_mx8(i32x8{a1l[0], a1l[1], a1l[2], a1l[3], a1h[0], a1h[1], a1h[2], a1h[3]}, qf[k2],
+                   k2 == 0 ? f32x16{} : sc1, s1k, qsc[k2]);
+  }
+  __syncthreads();
+
+  // steps 0 .. nkb; the exits are breaks so that only the path through the
+  // third step returns to the loop head
+  for (int s = 0;; s += 3) {
+    step(0, s);
+    if (s + 1 > nkb) break;
+    step(1, s + 1);
+    if (s + 2 > nkb) break;
+    step(2, s + 2);
+    if (s + 3 > nkb) break;
+  }
+  // no DMA may still be writing this workgroup's LDS when it exits
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // ---------------- epilogue
+  const float l_tot = sum_with_partner32(l_run);
+  const float inv = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
+  if (qi < N) {
+    uint16_t* op = a.o + ((size_t)b * N + qi) * qstride + (size_t)h * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * dt + 8 * g4 + 4 * hh;
+        uint2 val;
+        val.x = pack_bf16x2(oacc[dt][4 * g4] * inv, oacc[dt][4 * g4 + 1] * inv);
+        val.y = pack_bf16x2(oacc[dt][4 * g4 + 2] * inv, oacc[dt][4 * g4 + 3] * inv);
+        *(uint2*)(op + d0) = val;
+      }
+    }
+    if (a.lse != nullptr && hh == 0) {
+      const float v = (l_tot > 0.f && m_run != kNegInf) ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
+      a.lse[((size_t)b * a.Hq + h) * N + qi] = v;
+    }
+  }
+}
+
+hipError_t launch_fwd_mx8_sp(const Mx8Args& a, bool causal, hipStream_t s) {
+  const int grid = 8 * ((a.B * a.Hq + 7) / 8) * a.n_mb;
+  if (causal) {
+    hipLaunchKernelGGL(fwd_mx8_sp_kernel<true>, dim3(grid), dim3(512), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(fwd_mx8_sp_kernel<false>, dim3(grid), dim3(512), 0, s, a);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_fwd_mx8(const Mx8Args& a, bool causal, hipStream_t s) {

@@ -55,6 +55,8 @@ struct Mx8Args {
   float tau;
 };
 hipError_t launch_fwd_mx8(const Mx8Args& a, bool causal, hipStream_t s);
+// 8-wave software-pipelined MX fp8 forward; a.n_mb counts kPpBlockM-row blocks
+hipError_t launch_fwd_mx8_sp(const Mx8Args& a, bool causal, hipStream_t s);
 
 // Paged split-KV decode
 struct DecodeArgs {

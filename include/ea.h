@@ -145,6 +145,20 @@ ea_status ea_attn_fwd_mx8(const void* q8, const void* k8, const void* v8,
                           float scale, void* stream);
 
 /*
+ * ea_attn_fwd_mx8_tuned -- ea_attn_fwd_mx8 with forward tuning (NULL = the
+ * defaults). tuning->kernel selects EA_FWD_KERNEL_4WAVE or
+ * EA_FWD_KERNEL_PIPELINED (AUTO: the pipelined one); EA_FWD_KERNEL_PINGPONG,
+ * exp_mode other than EA_EXP_HW and natural_order = 1 return
+ * EA_ERR_UNSUPPORTED. rescale_log2 is the lazy-rescale threshold, which also
+ * bounds P before its e4m3 rounding (P <= 2^rescale_log2, so values above 8
+ * can overflow e4m3's 448).
+ */
+ea_status ea_attn_fwd_mx8_tuned(const void* q8, const void* k8, const void* v8,
+                                const uint8_t* q_scale, const uint8_t* k_scale, const uint8_t* v_scale,
+                                void* o, float* lse, int B, int N, int Hq, int Hkv, int d, int causal,
+                                float scale, const ea_fwd_tuning* tuning, void* stream);
+
+/*
  * Paged split-KV decode ("Faster, more flexible FlashAttention-4 for LLM
  * inference": PR 1999/2104 for KV pages of any size, PR 1940 for splitting the
  * KV sequence over workgroups plus a combine kernel, PR 1993 for one query tile

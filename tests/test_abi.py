@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("ea_attn_fwd", "ea_attn_fwd_varlen", "ea_attn_fwd_mx8", "ea_attn_decode_paged",
+    for n in ("ea_attn_fwd", "ea_attn_fwd_varlen", "ea_attn_fwd_mx8", "ea_attn_fwd_mx8_tuned", "ea_attn_decode_paged",
               "ea_decode_workspace_size", "ea_last_error"):
         assert n in names
 
@@ -82,6 +82,19 @@ def test_mx8_argument_errors(lib):
     assert f(P, P, P, P, P, None, P, None, 1, 64, 2, 2, 128, 1, 0.1, None) == -1
     assert f(P, P, P, P, P, P, P, None, 1, 48, 2, 2, 128, 1, 0.1, None) == -2   # N % 32
     assert f(P, P, P, P, P, P, P, None, 1, 64, 2, 2, 64, 1, 0.1, None) == -2    # d
+
+
+def test_mx8_tuning_errors(lib):
+    import exact_attention_amd as ea
+    f = lib.ea_attn_fwd_mx8_tuned
+
+    def call(t):
+        return f(P, P, P, P, P, P, P, None, 1, 64, 2, 2, 128, 1, 0.1, ctypes.byref(t), None)
+
+    assert call(ea.tuning(kernel=2)) == -2      # no ping-pong fp8 kernel
+    assert call(ea.tuning(exp_mode=1)) == -2    # hardware exponential only
+    assert call(ea.tuning(natural_order=1)) == -2
+    assert call(ea.tuning(kernel=4)) == -1
 
 
 def test_decode_argument_errors(lib):

@@ -21,11 +21,15 @@ NORM_TOL = 5e-2
 LSE_TOL = 5e-2
 
 
-def run_mx8(m):
+# the 4-wave kernel and the 8-wave software-pipelined one
+KERNELS = [1, 3]
+
+
+def run_mx8(m, kernel=0):
     import exact_attention_amd as ea
     t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
     o, lse = ea.attn_fwd_mx8(t(m.q8), t(m.k8), t(m.v8), t(m.q_scale), t(m.k_scale), t(m.v_scale),
-                             m.causal, m.scale)
+                             m.causal, m.scale, tuning=ea.tuning(kernel=kernel))
     torch.cuda.synchronize()
     return f64(host_bits(o)), lse.cpu().numpy().astype(np.float64)
 
@@ -55,9 +59,10 @@ def check_normwise(o, ro, lse, rl, what):
     (1, 256, 2, 2, True), (1, 256, 2, 2, False),
     (2, 320, 4, 2, True),      # N % 64 != 0 (ragged tail tile), GQA 2:1
     (1, 96, 1, 1, False), (1, 1024, 2, 1, True)])
-def test_mx8_small(shape):
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_mx8_small(shape, kernel):
     B, N, Hq, Hkv, causal = shape
-    log(f"mx8 shape {shape}")
+    log(f"mx8 shape {shape} kernel {kernel}")
     # quantise Q with Hq heads and K/V with Hkv heads
     qf = W.normal_f32(300 + N, W.STREAM_Q, B * N * Hq * 128).reshape(B, N, Hq, 128)
     kf = W.normal_f32(300 + N, W.STREAM_K, B * N * Hkv * 128).reshape(B, N, Hkv, 128)
@@ -66,23 +71,25 @@ def test_mx8_small(shape):
     k8, ks = W.mx_quantize_e4m3(kf, axis=3)
     v8, vs = W.mx_quantize_e4m3(vf, axis=1)
     m = W.MX8(q8, k8, v8, qs, ks, vs, causal, 1 / np.sqrt(128))
-    o, lse = run_mx8(m)
+    o, lse = run_mx8(m, kernel)
     q, k, v = deq(m)
     ro, rl = oracle.attention(q, k, v, causal, m.scale)
     check_normwise(o, ro, lse, rl, f"shape {shape}")
 
 
-def test_mx8_determinism():
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_mx8_determinism(kernel):
     m = W.mx8(1, 512, 2, 128, True, seed=310)
-    o1, l1 = run_mx8(m)
-    o2, l2 = run_mx8(m)
+    o1, l1 = run_mx8(m, kernel)
+    o2, l2 = run_mx8(m, kernel)
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
-def test_fp8_workload_sampled():
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_fp8_workload_sampled(kernel):
     m = W.fp8_prefill()
-    log(f"mx8 workload shape={m.q8.shape}")
-    o, lse = run_mx8(m)
+    log(f"mx8 workload shape={m.q8.shape} kernel {kernel}")
+    o, lse = run_mx8(m, kernel)
     B, N, H, d = m.q8.shape
     rng = np.random.default_rng(8)
     rows = sorted(set([0, 1, 63, 64, 127, 128, N // 2, N - 65, N - 1] + rng.integers(0, N, 20).tolist()))
