@@ -16,7 +16,11 @@ bytes sits under ``decode``, the fp8 forward under ``fp8``. ``roofline``
 describes the dominant kernel (the bf16 prefill forward, MFMA-bound);
 ``roofline_decode`` the decode (HBM-bound), ``roofline_fp8`` the fp8 forward.
 ``cpu_baseline`` times the CPU fp64 oracle on a bounded sample of the same
-workload on this host's cores.
+workload on this host's cores. After the timed region, ``sustained`` in each
+MFMA roofline object gives the rate the vendor BLAS reaches on a large GEMM of
+the same input type on this GPU (bf16 8192^3 through torch.matmul, e4m3
+16384^3 through torch._scaled_mm), a measured ceiling to read ``achieved``
+against beside the published peak.
 """
 from __future__ import annotations
 
@@ -52,6 +56,8 @@ def parse():
     p.add_argument("--only", choices=["prefill", "decode", "fp8"], default=None,
                    help="time one kernel family only (profiling runs)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-gemm-calibration", action="store_true",
+                   help="skip the vendor-GEMM rate measured after the timed region")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle time budget per leg")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy (calibrates HBM byte counters)")
@@ -69,6 +75,36 @@ def copy_calibration():
         y.copy_(x)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes": 1 << 30, "calls": 3}))
+
+
+def gemm_rate(torch, dev, dtype_name, n, reps=10):
+    """TFLOP/s of one n^3 GEMM through the vendor BLAS (median of reps), or None."""
+    try:
+        if dtype_name == "bf16":
+            a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+            b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+            run = lambda: a @ b  # noqa: E731
+        else:
+            a = torch.randn(n, n, device=dev).to(torch.float8_e4m3fn)
+            b = torch.randn(n, n, device=dev).to(torch.float8_e4m3fn).t().contiguous().t()
+            one = torch.ones((), device=dev)
+            run = lambda: torch._scaled_mm(a, b, scale_a=one, scale_b=one, out_dtype=torch.bfloat16)  # noqa: E731
+        for _ in range(3):
+            run()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            run()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        del a, b
+        return 2.0 * n ** 3 / (float(np.median(ts)) * 1e-3) / 1e12
+    except Exception:  # noqa: BLE001 -- an unavailable GEMM type leaves the field null
+        return None
 
 
 def prefill_flops(B, H, N, d):
@@ -259,9 +295,16 @@ def main():
         if run_prefill:
             out["fp8"]["ratio_to_bf16"] = tf8 / out["value"]
         out["roofline_fp8"] = {"bound": "mfma", "achieved": tf8, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                               "frac": tf8 / PEAK_FP8_TFLOPS, "traffic": None, "kernel": "ea::fwd_mx8_kernel<causal>"}
+                               "frac": tf8 / PEAK_FP8_TFLOPS, "traffic": None, "kernel": "ea::fwd_mx8_sp_kernel<causal>"}
         if not (run_prefill or run_decode):
             out["value"], out["unit"], out["dtype"] = tf8, "TFLOP/s", "fp8_e4m3"
+    if not args.no_gemm_calibration:
+        for key, dt_name, n in (("roofline", "bf16", 8192), ("roofline_fp8", "fp8", 16384)):
+            if key in out:
+                r = gemm_rate(torch, dev, dt_name, n)
+                out[key]["sustained"] = {
+                    "what": f"vendor BLAS {dt_name} GEMM {n}^3 on this GPU", "unit": "TFLOP/s",
+                    "value": r, "frac": (out[key]["achieved"] / r) if r else None}
     props = torch.cuda.get_device_properties(dev)
     cfg["device"] = props.name
     cfg["cus"] = props.multi_processor_count
