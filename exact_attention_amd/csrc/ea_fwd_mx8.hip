@@ -45,14 +45,23 @@ __device__ __forceinline__ f32x16 mfma_mx8(i32x8 a, i32x8 b, f32x16 c, int scale
   // formats: 0 = fp8 e4m3 for both operands
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, scale_b);
 }
+// same, with the scale of A taken from byte SA of its register (the
+// instruction's own byte select; the other bytes are ignored)
+template <int SA>
+__device__ __forceinline__ f32x16 mfma_mx8_sel(i32x8 a, i32x8 b, f32x16 c, int scale_a, int scale_b) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, SA, scale_a, 0, scale_b);
+}
 
 __device__ __forceinline__ i32x2 ds_read_tr8(const EA_LDS uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((EA_LDS i32x2*)p);
 }
 
-// four fp32 -> four e4m3 bytes (round to nearest even; inputs stay below 448)
+// four fp32 -> four e4m3 bytes (round to nearest even; inputs stay below 448).
+// The first conversion writes the low half of its destination and keeps the
+// rest of the register it is given, which the second conversion then
+// overwrites, so any register serves (x0's own bits: no zeroing move).
 __device__ __forceinline__ int pack_fp8x4(float x0, float x1, float x2, float x3) {
-  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, __float_as_int(x0), false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, lo, true);
 }
 
@@ -483,21 +492,14 @@ __global__ __launch_bounds__(512, 1) void fwd_mx8_sp_kernel(Mx8Args a) {
                    __attribute__((always_inline)) -> bool {
     const EA_LDS uint8_t* ks = kstage((r + 1) % 3);
     const EA_LDS uint8_t* vs = vstage((r + 2) % 3);
-    int ko[2][2], vo[NDT];
+    const auto& ko = k_off;
+    const auto& vo = v_off;
+    // K scale of (key row, d block 2 k2 + hh) is byte 2 k2 + hh of its dword:
+    // after a shift by 8 hh it is byte 2 k2, which the MFMA selects itself; a
+    // V scale is byte 0 of its (zero-extended) load
+    int ksh[2];
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      ko[k2][0] = launder(k_off[k2][0]);
-      ko[k2][1] = launder(k_off[k2][1]);
-    }
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) vo[dt] = launder(v_off[dt]);
-    int ksc[2][2], vsc[NDT];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) ksc[t][k2] = (kraw_cur[t] >> (8 * (2 * k2 + hh))) & 0xFF;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) vsc[dt] = (int)(vraw_cur[dt] & 0xFF);
+    for (int t = 0; t < 2; ++t) ksh[t] = (int)(kraw_cur[t] >> (8 * hh));
 
     i32x8 opnd[NMF];
     auto read_operand = [&](int jx) __attribute__((always_inline)) {
@@ -536,14 +538,15 @@ __global__ __launch_bounds__(512, 1) void fwd_mx8_sp_kernel(Mx8Args a) {
       if (i + RA < NMF) read_operand(i + RA);
       if (i < 4) {
         const int t = i & 1, k2 = i >> 1;
-        if (t) {
-          sn1 = mfma_mx8(opnd[i], qf[k2], k2 == 0 ? f32x16{} : sn1, ksc[1][k2], qsc[k2]);
+        f32x16& sn = t ? sn1 : sn0;
+        if (k2 == 0) {
+          sn = mfma_mx8_sel<0>(opnd[i], qf[0], f32x16{}, ksh[t], qsc[0]);
         } else {
-          sn0 = mfma_mx8(opnd[i], qf[k2], k2 == 0 ? f32x16{} : sn0, ksc[0][k2], qsc[k2]);
+          sn = mfma_mx8_sel<2>(opnd[i], qf[1], sn, ksh[t], qsc[1]);
         }
       } else {
         const int dt = i - 4;
-        oacc[dt] = mfma_mx8(opnd[i], pprev, oacc[dt], vsc[dt], kScaleOne);
+        oacc[dt] = mfma_mx8(opnd[i], pprev, oacc[dt], (int)vraw_cur[dt], kScaleOne);
       }
       if (i == 0) {
         load_kscale(s + 2, kraw_nxt);
