@@ -45,6 +45,7 @@ PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 # kernels. Sources: profiles/*_counters.md.
 TRAFFIC_PREFILL = 582_522_880    # fwd_pp_kernel<128, causal>: 217,698 KiB fetched, 133,474 KiB written
 TRAFFIC_DECODE = 4_866_152_448   # decode_split_kernel<4> + combine: 2,373,145 KiB fetched, 5,812 KiB written
+TRAFFIC_FP8 = 491_217_920        # fwd_mx8_sp_kernel<causal>: 173,215 KiB fetched, 133,275 KiB written
 
 
 def parse():
@@ -295,7 +296,7 @@ def main():
         if run_prefill:
             out["fp8"]["ratio_to_bf16"] = tf8 / out["value"]
         out["roofline_fp8"] = {"bound": "mfma", "achieved": tf8, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                               "frac": tf8 / PEAK_FP8_TFLOPS, "traffic": None, "kernel": "ea::fwd_mx8_sp_kernel<causal>"}
+                               "frac": tf8 / PEAK_FP8_TFLOPS, "traffic": TRAFFIC_FP8, "kernel": "ea::fwd_mx8_sp_kernel<causal>"}
         if not (run_prefill or run_decode):
             out["value"], out["unit"], out["dtype"] = tf8, "TFLOP/s", "fp8_e4m3"
     if not args.no_gemm_calibration:
