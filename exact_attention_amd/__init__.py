@@ -43,6 +43,9 @@ _SIGNATURES = {
     "ea_attn_fwd": ([_c_void_p] * 5 + [_c_int] * 7 + [_c_float, _c_void_p], _c_int),
     "ea_attn_fwd_tuned": ([_c_void_p] * 5 + [_c_int] * 7 + [_c_float, ctypes.POINTER(FwdTuning), _c_void_p], _c_int),
     "ea_attn_fwd_varlen": ([_c_void_p] * 7 + [_c_int] * 8 + [_c_float, ctypes.POINTER(FwdTuning), _c_void_p], _c_int),
+    "ea_attn_fwd_varlen_ordered": ([_c_void_p] * 7 + [_c_int] * 8 + [_c_float, _c_void_p, ctypes.POINTER(FwdTuning),
+                                                                    _c_void_p], _c_int),
+    "ea_varlen_lpt_order": ([_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p], _c_int),
     "ea_attn_fwd_mx8": ([_c_void_p] * 8 + [_c_int] * 6 + [_c_float, _c_void_p], _c_int),
     "ea_attn_fwd_mx8_tuned": ([_c_void_p] * 8 + [_c_int] * 6 + [_c_float, ctypes.POINTER(FwdTuning), _c_void_p],
                               _c_int),
@@ -132,10 +135,31 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, *, tunin
     return o, lse
 
 
+def varlen_lpt_order(cu_seqlens_q, cu_seqlens_k, causal: bool, block_m: int = 256):
+    """Heaviest-sequence-first order of a packed batch (ea_varlen_lpt_order).
+    Returns (order, weights), int32 [S] on the GPU: order[v] = actual sequence."""
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
+    _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1)
+    S = cu_seqlens_q.shape[0] - 1
+    if cu_seqlens_k.shape[0] != S + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    order = torch.empty(S, dtype=torch.int32, device=cu_seqlens_q.device)
+    weights = torch.empty(S, dtype=torch.int32, device=cu_seqlens_q.device)
+    st = lib().ea_varlen_lpt_order(_ptr(cu_seqlens_q), _ptr(cu_seqlens_k), S, int(bool(causal)), int(block_m),
+                                   _ptr(weights), _ptr(order), _stream(cu_seqlens_q))
+    _check(st, "ea_varlen_lpt_order")
+    return order, weights
+
+
 def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, causal: bool = False,
-                    scale: float | None = None, *, tuning: FwdTuning | None = None, want_lse: bool = True):
+                    scale: float | None = None, *, tuning: FwdTuning | None = None, want_lse: bool = True,
+                    seq_order: torch.Tensor | None = None):
     """Packed variable-length forward. q [Tq,Hq,d], k/v [Tk,Hkv,d] bf16 (THD);
-    cu_seqlens int32 [S+1] on the GPU. Returns (o [Tq,Hq,d], lse [Hq,Tq])."""
+    cu_seqlens int32 [S+1] on the GPU; seq_order (int32 [S] on the GPU, e.g.
+    from varlen_lpt_order) sets the order the workgroups visit the sequences.
+    Returns (o [Tq,Hq,d], lse [Hq,Tq])."""
+    if seq_order is not None:
+        _need(seq_order, "seq_order", torch.int32, 1)
     _need(q, "q", torch.bfloat16, 3)
     _need(k, "k", torch.bfloat16, 3)
     _need(v, "v", torch.bfloat16, 3)
@@ -150,10 +174,12 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, caus
         scale = 1.0 / math.sqrt(d)
     o = torch.empty_like(q)
     lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device) if want_lse else None
-    st = lib().ea_attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens_q),
-                                  _ptr(cu_seqlens_k), S, Tq, Tk, int(max_seqlen_q), Hq, Hkv, d,
-                                  int(bool(causal)), float(scale),
-                                  ctypes.byref(tuning) if tuning is not None else None, _stream(q))
+    if seq_order is not None and seq_order.shape[0] != S:
+        raise ValueError("seq_order must have one entry per sequence")
+    st = lib().ea_attn_fwd_varlen_ordered(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens_q),
+                                          _ptr(cu_seqlens_k), S, Tq, Tk, int(max_seqlen_q), Hq, Hkv, d,
+                                          int(bool(causal)), float(scale), _ptr(seq_order),
+                                          ctypes.byref(tuning) if tuning is not None else None, _stream(q))
     _check(st, "ea_attn_fwd_varlen")
     return o, lse
 

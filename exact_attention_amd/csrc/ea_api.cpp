@@ -124,10 +124,11 @@ ea_status ea_attn_fwd(const void* q, const void* k, const void* v, void* o, floa
   return ea_attn_fwd_tuned(q, k, v, o, lse, B, Nq, Nk, Hq, Hkv, d, causal, scale, nullptr, stream);
 }
 
-ea_status ea_attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
-                             const int* cu_seqlens_q, const int* cu_seqlens_k, int num_seqs,
-                             int total_q, int total_k, int max_seqlen_q, int Hq, int Hkv, int d,
-                             int causal, float scale, const ea_fwd_tuning* tuning, void* stream) {
+ea_status ea_attn_fwd_varlen_ordered(const void* q, const void* k, const void* v, void* o, float* lse,
+                                     const int* cu_seqlens_q, const int* cu_seqlens_k, int num_seqs,
+                                     int total_q, int total_k, int max_seqlen_q, int Hq, int Hkv, int d,
+                                     int causal, float scale, const int* seq_order,
+                                     const ea_fwd_tuning* tuning, void* stream) {
   if (!q || !k || !v || !o || !cu_seqlens_q || !cu_seqlens_k)
     return fail(EA_ERR_INVALID, "q, k, v, o and cu_seqlens must be non-null");
   if (num_seqs <= 0 || total_q <= 0 || total_k <= 0 || max_seqlen_q <= 0 || Hq <= 0 || Hkv <= 0 ||
@@ -165,8 +166,32 @@ ea_status ea_attn_fwd_varlen(const void* q, const void* k, const void* v, void* 
   a.scale_log2 = scale * 1.4426950408889634f;
   a.tau = tt.rescale_log2;
   a.natural = tt.natural_order;
+  a.seq_order = seq_order;
   return hip_status(dispatch_fwd(a, d, causal != 0, true, tt, (hipStream_t)stream),
                     "varlen attention forward launch");
+}
+
+ea_status ea_attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                             const int* cu_seqlens_q, const int* cu_seqlens_k, int num_seqs,
+                             int total_q, int total_k, int max_seqlen_q, int Hq, int Hkv, int d,
+                             int causal, float scale, const ea_fwd_tuning* tuning, void* stream) {
+  return ea_attn_fwd_varlen_ordered(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k,
+                                    max_seqlen_q, Hq, Hkv, d, causal, scale, nullptr, tuning, stream);
+}
+
+ea_status ea_varlen_lpt_order(const int* cu_seqlens_q, const int* cu_seqlens_k, int num_seqs, int causal,
+                              int block_m, int* weights, int* order, void* stream) {
+  if (!cu_seqlens_q || !cu_seqlens_k || !weights || !order)
+    return fail(EA_ERR_INVALID, "cu_seqlens, weights and order must be non-null");
+  if (num_seqs <= 0) return fail(EA_ERR_INVALID, "num_seqs must be positive");
+  if (num_seqs > (1 << 16)) return fail(EA_ERR_UNSUPPORTED, "at most 65536 sequences (the ranking is quadratic)");
+  if (causal != 0 && causal != 1) return fail(EA_ERR_INVALID, "causal must be 0 or 1");
+  if (block_m != ea::kFwdBlockM && block_m != ea::kPpBlockM)
+    return fail(EA_ERR_INVALID, "block_m must be %d or %d (the forward kernels' row blocks)", ea::kFwdBlockM,
+                ea::kPpBlockM);
+  return hip_status(ea::launch_lpt_order(cu_seqlens_q, cu_seqlens_k, num_seqs, causal, block_m, weights, order,
+                                         (hipStream_t)stream),
+                    "varlen LPT order launch");
 }
 
 ea_status ea_attn_fwd_mx8_tuned(const void* q8, const void* k8, const void* v8, const uint8_t* q_scale,

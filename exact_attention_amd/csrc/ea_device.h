@@ -130,6 +130,15 @@ __device__ __forceinline__ int tile_off(int row, int col) {
   return row * D + (((col >> 3) ^ swz<D>(row)) << 3) + (col & 7);
 }
 
+// Packed (varlen) forwards walk sequences in a virtual order: the actual
+// sequence of virtual index sv, or -1 when the order holds an index outside
+// [0, nseq) (such an entry then contributes no rows).
+__device__ __forceinline__ int varlen_seq(const int* order, int nseq, int sv) {
+  if (order == nullptr) return sv;
+  const int s = order[sv];
+  return (s >= 0 && s < nseq) ? s : -1;
+}
+
 // Workgroup-uniform integer pinned to a scalar register (the compiler cannot
 // always prove uniformity through divisions done on the vector unit).
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }

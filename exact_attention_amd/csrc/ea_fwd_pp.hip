@@ -67,16 +67,22 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     h = g - seq * a.Hq;
     mb = a.natural ? r : a.n_mb - 1 - r;
   } else {
-    int g = xcd, nm = 0;
-    for (; g < ngroups; g += 8) {
-      const int s = g / a.Hq;
-      nm = (a.cu_q[s + 1] - a.cu_q[s] + BM - 1) / BM;
+    // groups (virtual sequence, head), dealt to the XCDs in snake order
+    // (round k: XCD x takes group 8k + x for even k, 8k + 7 - x for odd k),
+    // so a heaviest-first order pairs heavy groups with light ones; the
+    // optional order maps a virtual sequence to the actual one
+    int g = xcd, nm = 0, s = 0;
+    for (int k = 0;; ++k) {
+      g = 8 * k + ((k & 1) ? 7 - xcd : xcd);
+      if (g >= ngroups) break;
+      s = varlen_seq(a.seq_order, a.nseq, g / a.Hq);
+      nm = s < 0 ? 0 : (a.cu_q[s + 1] - a.cu_q[s] + BM - 1) / BM;
       if (j < nm) break;
       j -= nm;
     }
     if (g >= ngroups) return;
-    seq = g / a.Hq;
-    h = g - seq * a.Hq;
+    seq = s;
+    h = g - (g / a.Hq) * a.Hq;
     mb = a.natural ? j : nm - 1 - j;
   }
   int q0, lq, k0, lk;

@@ -22,6 +22,7 @@ struct FwdArgs {
   float scale_log2;    // softmax scale * log2(e)
   float tau;           // lazy-rescale threshold in log2 units
   int natural;         // 1: ascending row-block order
+  const int* seq_order;  // packed only: virtual -> actual sequence, or null (input order)
 };
 
 constexpr int kFwdBlockM = 128;  // query rows per workgroup (4 waves x 32)
@@ -38,6 +39,10 @@ hipError_t launch_fwd_pp(const FwdArgs& a, int d, bool causal, bool varlen, int 
 // 8-wave software-pipelined forward; a.n_mb counts kPpBlockM-row blocks
 hipError_t launch_fwd_sp(const FwdArgs& a, int d, bool causal, bool varlen, int exp_mode,
                          hipStream_t s);
+
+// varlen batch order (heaviest sequence first): weights[b] and order[virtual] = actual
+hipError_t launch_lpt_order(const int* cu_q, const int* cu_k, int n, int causal, int block_m, int* weights,
+                            int* order, hipStream_t s);
 
 // MX fp8 forward
 struct Mx8Args {

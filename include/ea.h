@@ -128,6 +128,43 @@ ea_status ea_attn_fwd_varlen(const void* q, const void* k, const void* v, void* 
                              int causal, float scale, const ea_fwd_tuning* tuning, void* stream);
 
 /*
+ * ea_varlen_lpt_order -- the varlen batch order of "FlashAttention4 close
+ * reading", section 3.3 (scheduling): a preprocessing step weighs each
+ * sequence by its heaviest work tile -- the number of 64-key tiles in the
+ * main loop of its last block of block_m query rows (causal: keys up to that
+ * block's last row, bottom-right aligned; non-causal: all keys; 0 without
+ * queries) -- and sorts the sequences by weight, heaviest first, equal
+ * weights in input order. No data moves: the result is a permutation.
+ *   cu_seqlens_q / cu_seqlens_k: device int32 [num_seqs + 1], as for the
+ *     varlen forward.
+ *   block_m: 256 for the 8-wave forward kernels (the default for d = 128),
+ *     128 for the 4-wave kernel; any of the two gives a valid order.
+ *   weights: device int32 [num_seqs], written (the weights above).
+ *   order: device int32 [num_seqs], written: order[v] = the actual sequence
+ *     at virtual position v.
+ * Both buffers belong to the caller. Enqueued on stream; the ranking is a
+ * quadratic count spread over num_seqs threads, so num_seqs <= 65536
+ * (EA_ERR_UNSUPPORTED beyond). Lengths are read on the device, so every layer
+ * of a model that shares cu_seqlens can reuse one order.
+ */
+ea_status ea_varlen_lpt_order(const int* cu_seqlens_q, const int* cu_seqlens_k, int num_seqs, int causal,
+                              int block_m, int* weights, int* order, void* stream);
+
+/*
+ * ea_attn_fwd_varlen_ordered -- ea_attn_fwd_varlen whose workgroups visit the
+ * sequences in the order given by seq_order (device int32 [num_seqs],
+ * order[v] = actual sequence; NULL = input order), e.g. from
+ * ea_varlen_lpt_order. The results do not depend on the order. seq_order
+ * must be a permutation of 0..num_seqs-1: an entry outside that range
+ * contributes no rows, and a sequence listed twice is computed twice.
+ */
+ea_status ea_attn_fwd_varlen_ordered(const void* q, const void* k, const void* v, void* o, float* lse,
+                                     const int* cu_seqlens_q, const int* cu_seqlens_k, int num_seqs,
+                                     int total_q, int total_k, int max_seqlen_q, int Hq, int Hkv, int d,
+                                     int causal, float scale, const int* seq_order,
+                                     const ea_fwd_tuning* tuning, void* stream);
+
+/*
  * ea_attn_fwd_mx8 -- forward with MX-scaled FP8 (OCP e4m3) inputs.
  *   q8, k8, v8     [B, N, H*, d] e4m3 codes (uint8)
  *   q_scale, k_scale [B, N, H*, d/32] e8m0 scale bytes (2^(s-127)), one per 32

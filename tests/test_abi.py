@@ -29,7 +29,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("ea_attn_fwd", "ea_attn_fwd_varlen", "ea_attn_fwd_mx8", "ea_attn_fwd_mx8_tuned", "ea_attn_decode_paged",
+    for n in ("ea_attn_fwd", "ea_attn_fwd_varlen", "ea_attn_fwd_varlen_ordered", "ea_varlen_lpt_order",
+              "ea_attn_fwd_mx8", "ea_attn_fwd_mx8_tuned", "ea_attn_decode_paged",
               "ea_decode_workspace_size", "ea_last_error"):
         assert n in names
 
@@ -125,3 +126,13 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         ea.attn_fwd(q, q, q)
+
+
+def test_varlen_lpt_order_argument_errors(lib):
+    f = lib.ea_varlen_lpt_order
+    assert f(None, P, 4, 1, 256, P, P, None) == -1
+    assert f(P, P, 4, 1, 256, None, P, None) == -1
+    assert f(P, P, 0, 1, 256, P, P, None) == -1
+    assert f(P, P, 4, 2, 256, P, P, None) == -1
+    assert f(P, P, 4, 1, 100, P, P, None) == -1        # not a forward row block
+    assert f(P, P, 1 << 17, 1, 256, P, P, None) == -2  # quadratic ranking: capped

@@ -1,0 +1,90 @@
+"""GPU tests of the varlen LPT batch order (ea_varlen_lpt_order) against the
+scheduling oracle, and of the forward walking sequences in that order."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.schedule as S
+import workloads as W
+from _helpers import assert_lse_close, assert_o_close, f64, host_bits, log
+
+pytestmark = pytest.mark.gpu
+
+
+def dev_order(cu_q, cu_k, causal, block_m):
+    import exact_attention_amd as ea
+    order, weights = ea.varlen_lpt_order(torch.from_numpy(np.asarray(cu_q, np.int32)).cuda(),
+                                         torch.from_numpy(np.asarray(cu_k, np.int32)).cuda(), causal, block_m)
+    torch.cuda.synchronize()
+    return order.cpu().numpy().tolist(), weights.cpu().numpy().tolist()
+
+
+def cu_of(lengths):
+    return np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("block_m", [128, 256])
+def test_order_matches_oracle(causal, block_m):
+    rng = np.random.default_rng(41)
+    for n in (1, 3, 7, 300, 1000):          # several ranking workgroups for n > 256
+        lq = rng.integers(0, 5000, n)
+        lk = lq + rng.integers(-200, 400, n) * (rng.random(n) < 0.5)
+        lk = np.maximum(lk, 0)
+        lq[rng.random(n) < 0.05] = 0          # sequences without queries
+        lk[:n // 3] = lk[0]                   # many equal weights (ties keep input order)
+        cu_q, cu_k = cu_of(lq), cu_of(lk)
+        log(f"lpt order n={n} causal={causal} block_m={block_m}")
+        order, weights = dev_order(cu_q, cu_k, causal, block_m)
+        want_w = [S.seq_weight(int(a), int(b), causal, block_m, 64) for a, b in zip(lq, lk)]
+        assert weights == want_w
+        assert order == S.lpt_order(cu_q, cu_k, causal, block_m, 64)
+
+
+def test_order_of_the_pages_example():
+    # the close-reading page's permutation: 0,1,2,3 -> 1,2,3,0
+    order, _ = dev_order([0, 64, 128, 192, 256], [0, 64, 320, 512, 640], False, 256)
+    assert order == [1, 2, 3, 0]
+
+
+def run_varlen_ordered(inp, kernel, order=None, poison=None):
+    import exact_attention_amd as ea
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()  # noqa: E731
+    q, k, v = t(inp.q).view(torch.bfloat16), t(inp.k).view(torch.bfloat16), t(inp.v).view(torch.bfloat16)
+    cu_q, cu_k = t(inp.cu_q), t(inp.cu_k)
+    maxq = int(np.diff(inp.cu_q).max())
+    o, lse = ea.attn_fwd_varlen(q, k, v, cu_q, cu_k, maxq, inp.causal, inp.scale,
+                                tuning=ea.tuning(kernel=kernel), seq_order=order)
+    torch.cuda.synchronize()
+    return f64(host_bits(o)), lse.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("kernel", [1, 2, 3])
+def test_forward_in_lpt_order_is_bitwise_the_same(kernel):
+    import exact_attention_amd as ea
+    L = [40, 1300, 7, 600, 2100, 0, 333]
+    inp = W.varlen(L, L, 4, 2, 128, True, seed=42)
+    cu_q = torch.from_numpy(inp.cu_q).cuda()
+    order, _ = ea.varlen_lpt_order(cu_q, cu_q, True, 128 if kernel == 1 else 256)
+    assert order.cpu().numpy().tolist() == S.lpt_order(inp.cu_q, inp.cu_k, True, 128 if kernel == 1 else 256, 64)
+    log(f"varlen forward in LPT order, kernel {kernel}: {order.cpu().numpy().tolist()}")
+    o1, l1 = run_varlen_ordered(inp, kernel)
+    o2, l2 = run_varlen_ordered(inp, kernel, order)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    ro, rl = oracle.attention_varlen(f64(inp.q), f64(inp.k), f64(inp.v), inp.cu_q, inp.cu_k, True, inp.scale)
+    assert_o_close(o2, ro)
+    assert_lse_close(l2, rl)
+
+
+def test_order_entry_out_of_range_contributes_no_rows():
+    # documented behaviour: an entry outside [0, num_seqs) is skipped (and its
+    # sequence, missing from the order, is not computed); the other sequences
+    # are unaffected
+    L = [100, 70, 200]
+    inp = W.varlen(L, L, 2, 2, 128, True, seed=43)
+    order = torch.tensor([2, -1, 0], dtype=torch.int32).cuda()
+    o_all, _ = run_varlen_ordered(inp, 2)
+    o, _ = run_varlen_ordered(inp, 2, order)
+    a, b = int(inp.cu_q[1]), int(inp.cu_q[2])
+    assert np.array_equal(o[:a], o_all[:a]) and np.array_equal(o[b:], o_all[b:])
