@@ -60,6 +60,8 @@ def parse():
     p.add_argument("--no-gemm-calibration", action="store_true",
                    help="skip the vendor-GEMM rate measured after the timed region")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle time budget per leg")
+    p.add_argument("--decode-page-size", type=int, choices=[1, 2, 4, 8, 16], default=16,
+                   help="view the decode pool as pages of this many tokens (same tokens, same memory)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy (calibrates HBM byte counters)")
     return p.parse_args()
@@ -200,9 +202,12 @@ def main():
         tun = ea.tuning(exp_mode=args.exp_mode)
     if run_decode:
         pg = W.paged_decode_device(dev)
+        if args.decode_page_size != 16:
+            pg = W.split_pages(pg, args.decode_page_size)
         dq = dev_bf16(pg.q)
-        bt = torch.from_numpy(pg.block_table).to(dev)
-        sl = torch.from_numpy(pg.seq_lens).to(dev)
+        bt = torch.from_numpy(np.ascontiguousarray(pg.block_table)).to(dev)
+        sl = torch.from_numpy(np.ascontiguousarray(pg.seq_lens)).to(dev)
+        assert bt.is_contiguous() and pg.k_cache.is_contiguous() and pg.v_cache.is_contiguous()
         Bd, Hq, dd = pg.q.shape
         Hkv = pg.k_cache.shape[2]
         ws = torch.empty(ea.decode_workspace_size(Bd, Hq, Hkv, dd, bt.shape[1] * pg.page_size, pg.page_size),
@@ -263,7 +268,7 @@ def main():
            "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1), bf16-rounded)"}
     cfg = {"workload": "prefill fwd B=4 H=16 N=8192 d=128 causal bf16 + paged decode B=64 Hq=32 Hkv=8 "
-                       "d=128 ctx U[512,32768] page 16 bf16 (split-KV + LSE combine)",
+                       f"d=128 ctx U[512,32768] page {args.decode_page_size} bf16 (split-KV + LSE combine)",
            "exp_mode": args.exp_mode, "input_gen_s": round(t_gen, 1)}
     if run_prefill:
         t_pf = np.array([e[0].elapsed_time(e[1]) for e in evs])      # ms
@@ -284,7 +289,8 @@ def main():
                          "bytes_per_launch": nbytes, "gbs_best": nbytes / (t_dc.min() * 1e-3) / 1e9}
         out["roofline_decode"] = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                   "frac": gbs / PEAK_HBM_GBS, "traffic": TRAFFIC_DECODE,
-                                  "kernel": "ea::decode_split_kernel<4> + decode_combine_kernel"}
+                                  "kernel": f"ea::decode_split_kernel<{'true' if pg.page_size % 16 == 0 else 'false'}>"
+                                            " + decode_combine_kernel"}
         if not run_prefill:
             out["value"], out["unit"] = gbs, "GB/s"
     if run_fp8:

@@ -258,12 +258,12 @@ ea_status ea_attn_fwd_mx8(const void* q8, const void* k8, const void* v8, const 
 namespace {
 
 // Number of equal shares W the batch's KV chunks are cut into (one workgroup
-// of 8 KV heads each). By default one workgroup per CU: 256 CUs over the
-// groups of 8 KV heads, fixed so the workspace size does not depend on the
-// device. Any W gives the same result up to rounding.
-int choose_ranges(int Hkv, int num_splits) {
+// per group of 8 (KV head, query-head block) pairs each). By default one
+// workgroup per CU: 256 CUs over those groups, fixed so the workspace size
+// does not depend on the device. Any W gives the same result up to rounding.
+int choose_ranges(int Hq, int Hkv, int num_splits) {
   if (num_splits > 0) return num_splits;
-  const int head_groups = (Hkv + 7) / 8;
+  const int head_groups = ea::decode_head_groups(Hkv, Hq / Hkv);
   const int w = (256 + head_groups - 1) / head_groups;
   return w < 1 ? 1 : w;
 }
@@ -274,11 +274,12 @@ extern "C" {
 
 size_t ea_decode_workspace_size(int B, int Hq, int Hkv, int d, int max_seqlen, int page_size,
                                 int num_splits) {
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || max_seqlen < 0 || page_size <= 0 || num_splits < 0)
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || max_seqlen < 0 || page_size <= 0 || num_splits < 0 ||
+      Hq % Hkv)
     return 0;
   (void)max_seqlen;
   (void)page_size;
-  return ea::decode_workspace_bytes(B, Hq, d, choose_ranges(Hkv, num_splits));
+  return ea::decode_workspace_bytes(B, Hq, d, choose_ranges(Hq, Hkv, num_splits));
 }
 
 ea_status ea_attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
@@ -294,9 +295,6 @@ ea_status ea_attn_decode_paged(const void* q, const void* k_cache, const void* v
   if (Hq % Hkv) return fail(EA_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
   const int group = Hq / Hkv;
   if (d != 128) return fail(EA_ERR_UNSUPPORTED, "paged decode supports d = 128 only");
-  if (page_size % 16) return fail(EA_ERR_UNSUPPORTED, "page_size must be a multiple of 16");
-  if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16)
-    return fail(EA_ERR_UNSUPPORTED, "Hq / Hkv must be 1, 2, 4, 8 or 16");
   if (!finite_pos(scale)) return fail(EA_ERR_INVALID, "scale must be finite and positive");
   if (num_splits < 0) return fail(EA_ERR_INVALID, "num_splits must be >= 0");
   if (num_splits > 65536) return fail(EA_ERR_UNSUPPORTED, "num_splits above 65536");
@@ -304,7 +302,7 @@ ea_status ea_attn_decode_paged(const void* q, const void* k_cache, const void* v
     return fail(EA_ERR_UNSUPPORTED, "batch context too long (2^31 32-token chunks)");
   if ((long long)max_pages_per_seq * page_size >= (1LL << 31))
     return fail(EA_ERR_UNSUPPORTED, "max context too long");
-  if ((long long)num_pages * page_size * Hkv * d >= (1LL << 40))
+  if ((long long)num_pages * page_size * Hkv * d >= (1LL << 40) || (long long)num_pages * page_size >= (1LL << 31))
     return fail(EA_ERR_UNSUPPORTED, "KV pool too large");
   const int max_seqlen = max_pages_per_seq * page_size;
   const size_t need = ea_decode_workspace_size(B, Hq, Hkv, d, max_seqlen, page_size, num_splits);
@@ -326,7 +324,7 @@ ea_status ea_attn_decode_paged(const void* q, const void* k_cache, const void* v
   a.page_size = page_size;
   a.max_pages = max_pages_per_seq;
   a.num_pages = num_pages;
-  a.num_ranges = choose_ranges(Hkv, num_splits);
+  a.num_ranges = choose_ranges(Hq, Hkv, num_splits);
   a.scale_log2 = scale * 1.4426950408889634f;
   ea::decode_bind_workspace(a, workspace);
   return hip_status(ea::launch_decode(a, (hipStream_t)stream), "paged decode launch");

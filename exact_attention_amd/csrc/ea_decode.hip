@@ -23,11 +23,24 @@
 //  * A workgroup of 8 waves serves 8 KV heads, one wave per head, all walking
 //    the same chunks. In the [pages, page_size, Hkv, d] cache a token's rows for
 //    all KV heads are adjacent, so the workgroup streams whole contiguous rows.
-//  * A chunk is two 16-token tiles; 16 divides page_size, so a tile lies in one
-//    page. Page indices are loaded 128 tiles at a time (two per lane) and read
-//    with v_readlane in the loop; each tile is a buffer resource bounded by the
-//    sequence length, so tokens at or past it (stale or poisoned slots of a
-//    last page) and page indices outside the pool read as zeros, no branch.
+//  * A chunk is two 16-token tiles. When 16 divides page_size a tile lies in
+//    one page: page indices are loaded 128 tiles at a time (two per lane) and
+//    read with v_readlane in the loop; each tile is a buffer resource bounded
+//    by the sequence length, so tokens at or past it (stale or poisoned slots
+//    of a last page) and page indices outside the pool read as zeros, no
+//    branch.
+//  * Any other page size (down to 1) takes the per-token path. Address
+//    generation is decoupled from use, as in the pages' transposed scheme for
+//    small pages: lane i < 32 looks up the page of the chunk's token i once
+//    (block-table entry prefetched one chunk ahead) and forms its row index;
+//    each lane then fetches the row indices of the 8 tokens it copies with
+//    lane shuffles instead of recomputing them. Tokens at or past the sequence
+//    end and pages outside the pool read as zeros.
+//  * Query heads: the G = Hq / Hkv heads of one KV head are packed as columns
+//    of 16-wide blocks (PR 2186's GQA packing for any ratio). G <= 16 leaves
+//    unused columns; G > 16 gives a KV head several blocks, one wave each, and
+//    those waves of one workgroup read the same K/V rows (from cache after the
+//    first).
 //  * Each wave copies its chunk's K and V rows into its own LDS region (no
 //    workgroup barrier anywhere), prefetching the next chunk into VGPRs while
 //    it computes the current one. S^T = K Q^T and O^T = V^T P^T use
@@ -81,19 +94,24 @@ __device__ __forceinline__ int range_start(int w, int Tc, int W) {
   return (int)(((long long)w * Tc) / W);
 }
 
-template <int G>
+template <bool PAGE16>
 __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(DecodeArgs a) {
   constexpr int D = kD;
   constexpr int TILE = kChunk * D;  // bf16 elements per K or V chunk
   __shared__ __attribute__((aligned(16))) uint16_t smem_raw[kWaves * 2 * TILE];
   EA_LDS uint16_t* sm = (EA_LDS uint16_t*)smem_raw;
 
-  // grid: x = workgroup range w of W, y = group of kWaves KV heads; wave i
-  // owns KV head kWaves*y + i.
+  // grid: x = workgroup range w of W, y = group of kWaves (KV head, column
+  // block) pairs; wave i owns pair kWaves*y + i: KV head vh / ncb, query heads
+  // 16 * (vh % ncb) + 0..15 of its group.
   const int wg = blockIdx.x, W = gridDim.x;
   const int tid = threadIdx.x, lane = tid & 63, wv = uniform(tid >> 6);
-  const int hkv = uniform(kWaves * (int)blockIdx.y + wv);
-  if (hkv >= a.Hkv) return;  // no barriers below: idle waves may leave
+  const int G = a.group, ncb = (G + 15) / 16;
+  const int vh = uniform(kWaves * (int)blockIdx.y + wv);
+  if (vh >= a.Hkv * ncb) return;  // no barriers below: idle waves may leave
+  const int hkv = uniform(vh / ncb);
+  const int c_lo = uniform(16 * (vh - hkv * ncb));  // first query head of this wave's block
+  const int ncols = uniform(min(16, G - c_lo));
   const int Tc = total_chunks(a, lane);
   // lane 0 of the first wave of head group 0 records Tc (workgroup 0, whose
   // range may be empty) and which ranges hold each sequence's first and last
@@ -144,9 +162,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(DecodeArgs
     // Q^T operand (B of S^T = K Q^T): column = packed query head, k = d
     bf16x8 qf[D / 32];
     {
-      const uint16_t* qp = a.q + ((size_t)b * a.Hq + (size_t)hkv * G + col) * D + 8 * grp;
+      const uint16_t* qp = a.q + ((size_t)b * a.Hq + (size_t)hkv * G + c_lo + col) * D + 8 * grp;
 #pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk) qf[kk] = (col < G) ? *(const bf16x8*)(qp + 32 * kk) : bf16x8{};
+      for (int kk = 0; kk < D / 32; ++kk) qf[kk] = (col < ncols) ? *(const bf16x8*)(qp + 32 * kk) : bf16x8{};
     }
 
     // Page indices of 128 consecutive 16-token tiles (64 chunks), two per lane;
@@ -188,6 +206,37 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(DecodeArgs
           rv[4 * tl + u] = buffer_load16(rs[tl][1], voff0 + 4 * u * row_bytes);
         }
     };
+    // per-token path (page sizes 16 does not divide): lane i < 32 holds the
+    // block-table entry and slot of token i of a chunk, and from them the row
+    // index page * page_size + slot, or -1 for a token past the end or a page
+    // outside the pool.
+    auto bt_entry = [&](int ci, int& slot) -> int {
+      const int t = t_begin + kChunk * ci + lane;
+      const int pi = t / ps;
+      slot = t - pi * ps;
+      return (lane < kChunk && t < t_end) ? bt[pi] : -1;
+    };
+    auto row_index = [&](int ent, int slot) -> int {
+      return (unsigned)ent < (unsigned)a.num_pages ? ent * ps + slot : -1;
+    };
+    const size_t row_elems = (size_t)a.Hkv * D;
+    const uint16_t* kbase = a.kc + (size_t)hkv * D + 8 * col;
+    const uint16_t* vbase = a.vc + (size_t)hkv * D + 8 * col;
+    auto gload_rows = [&](int rows) {
+#pragma unroll
+      for (int tl = 0; tl < 2; ++tl)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int ri = __shfl(rows, 16 * tl + 4 * u + grp);
+          i32x4 kx = i32x4{}, vx = i32x4{};
+          if (ri >= 0) {
+            kx = *(const i32x4*)(kbase + (size_t)ri * row_elems);
+            vx = *(const i32x4*)(vbase + (size_t)ri * row_elems);
+          }
+          rk[4 * tl + u] = kx;
+          rv[4 * tl + u] = vx;
+        }
+    };
     auto sstore = [&]() {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -201,15 +250,31 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(DecodeArgs
 #pragma unroll
     for (int mt = 0; mt < D / 16; ++mt) oacc[mt] = f32x4{};
 
-    load_pages(0);
-    gload(0);
+    int ent_next = -1, slot_next = 0;  // per-token path: entry of chunk ci + 1
+    if constexpr (PAGE16) {
+      load_pages(0);
+      gload(0);
+    } else {
+      int slot0;
+      const int ent0 = bt_entry(0, slot0);
+      if (nck > 1) ent_next = bt_entry(1, slot_next);
+      gload_rows(row_index(ent0, slot0));
+    }
     sstore();
     __builtin_amdgcn_s_waitcnt(0);
     for (int ci = 0; ci < nck; ++ci) {
       const int t0 = t_begin + kChunk * ci;
       if (ci + 1 < nck) {
-        if (((ci + 1) & 63) == 0) load_pages(ci + 1);
-        gload(ci + 1);
+        if constexpr (PAGE16) {
+          if (((ci + 1) & 63) == 0) load_pages(ci + 1);
+          gload(ci + 1);
+        } else {
+          // the entry of chunk ci + 1 was loaded one chunk ago (before the
+          // loads of chunk ci, which the last sstore waited for)
+          const int rows = row_index(ent_next, slot_next);
+          if (ci + 2 < nck) ent_next = bt_entry(ci + 2, slot_next);
+          gload_rows(rows);
+        }
       }
       // ---- S^T = K Q^T for two 16-token tiles
       f32x4 s[2];
@@ -266,8 +331,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(DecodeArgs
     float l_tot = xor16_sum(l_run);
     l_tot = sum_with_partner32(l_tot);
     const float inv = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
-    if (col < G) {
-      const size_t prow = (((size_t)(wg + b)) * a.Hkv + hkv) * G + col;
+    if (col < ncols) {
+      const size_t prow = (((size_t)(wg + b)) * a.Hkv + hkv) * G + c_lo + col;
       float* po = a.part_o + prow * D;
 #pragma unroll
       for (int mt = 0; mt < D / 16; ++mt) {
@@ -358,9 +423,9 @@ void decode_bind_workspace(DecodeArgs& a, void* workspace) {
   a.plan = (int*)p;
 }
 
-template <int G>
-static hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(decode_split_kernel<G>, dim3(a.num_ranges, (a.Hkv + kWaves - 1) / kWaves),
+template <bool PAGE16>
+static hipError_t launch_p(const DecodeArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(decode_split_kernel<PAGE16>, dim3(a.num_ranges, decode_head_groups(a.Hkv, a.group)),
                      dim3(64 * kWaves), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -370,13 +435,12 @@ static hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   if (a.num_ranges <= 0 || a.part_o == nullptr || a.plan == nullptr) return hipErrorInvalidValue;
-  switch (a.group) {
-    case 1: return launch_g<1>(a, s);
-    case 2: return launch_g<2>(a, s);
-    case 4: return launch_g<4>(a, s);
-    case 8: return launch_g<8>(a, s);
-    default: return launch_g<16>(a, s);
-  }
+  return (a.page_size % 16 == 0) ? launch_p<true>(a, s) : launch_p<false>(a, s);
+}
+
+int decode_head_groups(int Hkv, int group) {
+  const int ncb = (group + 15) / 16;
+  return (Hkv * ncb + kWaves - 1) / kWaves;
 }
 
 }  // namespace ea

@@ -83,6 +83,8 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 size_t decode_workspace_bytes(int B, int Hq, int d, int num_ranges);
+// workgroups along y: groups of 8 (KV head, 16-column block of its query heads) pairs
+int decode_head_groups(int Hkv, int group);
 // points part_o / part_lse / plan into a workspace of decode_workspace_bytes
 void decode_bind_workspace(DecodeArgs& a, void* workspace);
 

@@ -199,7 +199,8 @@ ea_status ea_attn_fwd_mx8_tuned(const void* q8, const void* k8, const void* v8,
  * Paged split-KV decode ("Faster, more flexible FlashAttention-4 for LLM
  * inference": PR 1999/2104 for KV pages of any size, PR 1940 for splitting the
  * KV sequence over workgroups plus a combine kernel, PR 1993 for one query tile
- * per workgroup, PR 2186 for packing the query heads of one KV head together).
+ * per workgroup, PR 2186 for packing the query heads of one KV head together,
+ * for any ratio Hq / Hkv).
  *
  *   q      [B, Hq, d] bf16 (one query token per sequence)
  *   k_cache, v_cache [num_pages, page_size, Hkv, d] bf16
@@ -210,12 +211,17 @@ ea_status ea_attn_fwd_mx8_tuned(const void* q8, const void* k8, const void* v8,
  *   seq_lens [B] int32, each in [0, max_pages_per_seq * page_size] (larger
  *          values are clamped to that capacity)
  *   o      [B, Hq, d] bf16 (written); lse [B, Hq] fp32 or NULL
- *   page_size a multiple of 16; d == 128; Hq / Hkv in {1, 2, 4, 8, 16}.
+ *   page_size >= 1 (multiples of 16 take a per-tile load path, other sizes
+ *          a per-token one). The arithmetic follows the logical token order
+ *          only, so the same tokens give bitwise the same output whatever the
+ *          page size and page placement. d == 128; any Hq that is a multiple
+ *          of Hkv; num_pages * page_size < 2^31.
  *   num_splits: the batch's KV tokens, taken in 32-token chunks and laid end
  *          to end over the sequences, are cut into num_splits equal ranges, one
- *          workgroup (of up to 8 KV heads) each; a sequence is split wherever a
+ *          workgroup (of up to 8 KV heads, or blocks of 16 query heads) each; a sequence is split wherever a
  *          range boundary falls in it. 0 = one workgroup per CU (256 over the
- *          groups of 8 KV heads). At most 65536.
+ *          groups of 8 (KV head, block of 16 of its query heads) pairs). At
+ *          most 65536.
  *   workspace: device memory of at least ea_decode_workspace_size(B, Hq, Hkv,
  *          d, max_pages_per_seq * page_size, page_size, num_splits) bytes
  *          (it depends on B, Hq, d and the range count only), owned by the

@@ -110,12 +110,15 @@ def test_decode_argument_errors(lib):
     assert call(q=None) == -1
     assert call(Hq=6, Hkv=4) == -1
     assert call(d=64) == -2
-    assert call(ps=8) == -2
-    assert call(Hq=6, Hkv=2) == -2          # group 3 not built
+    assert call(ps=8, npages=1 << 28) == -2  # pool of 2^31 token slots
     assert call(scale=0.0) == -1
     assert call(ns=-1) == -1
     assert call(wsb=ws - 1) == -4 and "workspace" in _err(lib)
     assert call(wsp=None) == -4
+    # query heads beyond 16 per KV head take more (KV head, block) pairs per
+    # range group, so the default range count and the workspace shrink
+    assert lib.ea_decode_workspace_size(4, 64, 1, 128, 1024, 16, 0) > 0
+    assert lib.ea_decode_workspace_size(4, 6, 4, 128, 1024, 16, 0) == 0   # Hq % Hkv
     # more splits need more workspace
     assert lib.ea_decode_workspace_size(4, 8, 2, 128, 1024, 16, 8) >= lib.ea_decode_workspace_size(4, 8, 2, 128, 1024, 16, 1)
 

@@ -33,8 +33,10 @@ def run_decode(pg, num_splits=0, want_lse=True):
     return f64(host_bits(o)), (lse.cpu().numpy().astype(np.float64) if lse is not None else None)
 
 
-@pytest.mark.parametrize("group", [1, 4, 8, 16])
+@pytest.mark.parametrize("group", [1, 3, 4, 5, 6, 7, 8, 12, 16, 20, 32, 64])
 def test_small_paged_decode(group):
+    """Any number of query heads per KV head: up to 16 share one column block
+    (unused columns padded), more take several blocks of 16."""
     L = [1, 16, 17, 40, 100, 513]
     Hkv = 2
     pg = W.paged(len(L), Hkv * group, Hkv, 128, 16, L, seed=200 + group)
@@ -132,8 +134,13 @@ def test_gather_bit_exact_under_permutation():
     assert np.array_equal(o1, o3) and np.array_equal(l1, l3)
 
 
-def test_decode_workload_sampled():
+@pytest.mark.parametrize("page_size", [16, 1, 4])
+def test_decode_workload_sampled(page_size):
+    """The decode workload (B=64, Hq=32, Hkv=8, contexts U{512..32768}); page
+    sizes 1 and 4 view the same pool as smaller pages (per-token path)."""
     pg = W.paged_decode_device("cuda")
+    if page_size != 16:
+        pg = W.split_pages(pg, page_size)
     log(f"decode workload: B={pg.q.shape[0]} pages={pg.k_cache.shape[0]} "
         f"lengths min={pg.seq_lens.min()} max={pg.seq_lens.max()}")
     o, lse = run_decode(pg)
@@ -144,3 +151,77 @@ def test_decode_workload_sampled():
     assert_o_close(o[pick], ro)
     assert_lse_close(lse[pick], rl)
     assert np.isfinite(o).all() and np.isfinite(lse).all()
+
+
+@pytest.mark.parametrize("page_size", [1, 2, 3, 5, 8, 12, 24, 40])
+def test_any_page_size(page_size):
+    """Page sizes 16 does not divide (down to one token per page) take the
+    per-token load path; lengths end inside, at and past page boundaries."""
+    L = [1, 2, 31, 32, 33, 97, 640, 1001]
+    pg = W.paged(len(L), 8, 2, 128, page_size, L, seed=300 + page_size)
+    log(f"decode page_size={page_size} lengths={L}")
+    o, lse = run_decode(pg)
+    ro, rl = oracle.decode_paged(pg.q, pg.k_cache, pg.v_cache, pg.block_table, pg.seq_lens, pg.scale)
+    assert_o_close(o, ro)
+    assert_lse_close(lse, rl)
+
+
+def relayout(pg, page_size, seed):
+    """The same logical tokens as pg in a pool of another page size: pages in a
+    seeded random order, the unused slots of every last page NaN-poisoned."""
+    B = pg.q.shape[0]
+    L = pg.seq_lens.astype(np.int64)
+    tail = pg.k_cache.shape[2:]
+    ks, vs = [], []
+    for b in range(B):
+        n = int(L[b])
+        t = np.arange(n)
+        pages = pg.block_table[b, t // pg.page_size]
+        ks.append(pg.k_cache[pages, t % pg.page_size])
+        vs.append(pg.v_cache[pages, t % pg.page_size])
+    npg = (L + page_size - 1) // page_size
+    P = int(npg.sum())
+    phys = np.random.default_rng(seed).permutation(P).astype(np.int32)
+    kc = np.full((P, page_size) + tail, W.BF16_NAN, dtype=np.uint16)
+    vc = np.full((P, page_size) + tail, W.BF16_NAN, dtype=np.uint16)
+    bt = np.full((B, int(npg.max())), -1, dtype=np.int32)
+    off = 0
+    for b in range(B):
+        for j in range(int(npg[b])):
+            lo, hi = j * page_size, min(int(L[b]), (j + 1) * page_size)
+            kc[phys[off], :hi - lo] = ks[b][lo:hi]
+            vc[phys[off], :hi - lo] = vs[b][lo:hi]
+            bt[b, j] = phys[off]
+            off += 1
+    return W.Paged(pg.q, kc, vc, bt, pg.seq_lens.copy(), page_size, pg.scale)
+
+
+def test_page_size_invariance_bitwise():
+    """The arithmetic follows the logical token order only: the same tokens
+    laid out in pages of 16, 1, 5, 24 or 64 (each pool in its own random page
+    order) decode to the same bits, through both load paths."""
+    L = [5, 48, 129, 700, 1500, 3]
+    base = W.paged(len(L), 12, 2, 128, 16, L, seed=320)
+    o0, l0 = run_decode(base)
+    for ps in (1, 5, 24, 64):
+        o1, l1 = run_decode(relayout(base, ps, seed=321 + ps))
+        log(f"page size {ps} vs 16: max |do| = {np.nanmax(np.abs(o1 - o0)):.3g}")
+        assert np.array_equal(o0, o1) and np.array_equal(l0, l1), ps
+    ro, rl = oracle.decode_paged(base.q, base.k_cache, base.v_cache, base.block_table, base.seq_lens, base.scale)
+    assert_o_close(o0, ro)
+    assert_lse_close(l0, rl)
+
+
+def test_small_pages_many_sequences_odd_group():
+    """One-token pages, 6 query heads per KV head, 130 sequences, several
+    range counts (ranges cut sequences at arbitrary chunks)."""
+    rng = np.random.default_rng(330)
+    L = rng.integers(0, 400, size=130).tolist()
+    pg = W.paged(len(L), 24, 4, 128, 1, L, seed=330)
+    ro, rl = oracle.decode_paged(pg.q, pg.k_cache, pg.v_cache, pg.block_table, pg.seq_lens, pg.scale)
+    nz = np.asarray(L) > 0
+    for ns in (0, 7, 300):
+        o, lse = run_decode(pg, num_splits=ns)
+        assert_o_close(o[nz], ro[nz])
+        assert_lse_close(lse[nz], rl[nz])
+        assert np.all(o[~nz] == 0) and np.all(np.isneginf(lse[~nz]))

@@ -373,3 +373,17 @@ def test_planted_mistakes_are_caught(monkeypatch):
     o_mod = np.stack([oracle.attention(q[:, :, h:h + 1], k[:, :, h % 2:h % 2 + 1], v[:, :, h % 2:h % 2 + 1], True, 0.5, threads=1)[0][:, :, 0]
                       for h in range(4)], axis=2)
     assert not np.allclose(o_mod, ob, atol=1e-6)
+
+
+def test_split_pages_view_gathers_the_same_tokens():
+    """Seeing a pool of 16-token pages as pages of 1, 4 or 8 tokens (no data
+    moved, block table rewritten) gathers the same tokens, so the oracle's
+    decode is bitwise unchanged."""
+    pg = W.paged(3, 8, 2, 128, 16, [1, 37, 160], seed=77)
+    ro, rl = oracle.decode_paged(pg.q, pg.k_cache, pg.v_cache, pg.block_table, pg.seq_lens, pg.scale)
+    for ps in (1, 4, 8):
+        sp = W.split_pages(pg, ps)
+        assert sp.k_cache.shape[1] == ps and sp.block_table.shape[1] == pg.block_table.shape[1] * 16 // ps
+        assert sp.block_table.flags.c_contiguous
+        so, sl = oracle.decode_paged(sp.q, sp.k_cache, sp.v_cache, sp.block_table, sp.seq_lens, sp.scale)
+        assert np.array_equal(so, ro) and np.array_equal(sl, rl)

@@ -323,6 +323,24 @@ def paged_decode() -> Paged:
     return paged(64, 32, 8, 128, 16, L, seed=1003, max_pages=32768 // 16)
 
 
+def split_pages(pg: Paged, page_size: int) -> Paged:
+    """The same pool seen as pages of ``page_size`` tokens, a divisor of the
+    pool's page size: page p of the pool becomes pages p*r .. p*r + r - 1
+    (r = old / new size), so no data moves; the block table is rewritten."""
+    old = pg.page_size
+    assert old % page_size == 0, (old, page_size)
+    r = old // page_size
+    kc = pg.k_cache.reshape((pg.k_cache.shape[0] * r, page_size) + tuple(pg.k_cache.shape[2:]))
+    vc = pg.v_cache.reshape((pg.v_cache.shape[0] * r, page_size) + tuple(pg.v_cache.shape[2:]))
+    bt = np.asarray(pg.block_table)
+    B, mp = bt.shape
+    j = np.arange(mp * r)
+    src = bt[:, j // r]
+    # (fancy indexing may return a column-major array; the table must be row-major)
+    nbt = np.ascontiguousarray(np.where(src >= 0, src * r + (j % r)[None, :], -1), dtype=np.int32)
+    return Paged(pg.q, kc, vc, nbt, pg.seq_lens, page_size, pg.scale)
+
+
 def normal_bf16_device(seed: int, stream: int, shape, device, chunk: int = 1 << 28):
     """iid N(0,1) draws rounded (RNE) to bf16 on a GPU: torch's seeded
     Philox generator on ``device``, drawn in chunks of ``chunk`` elements
