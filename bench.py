@@ -60,6 +60,8 @@ def parse():
     p.add_argument("--no-gemm-calibration", action="store_true",
                    help="skip the vendor-GEMM rate measured after the timed region")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle time budget per leg")
+    p.add_argument("--fp8-format", choices=["e4m3", "e5m2"], default="e4m3",
+                   help="element format of the fp8 forward's MX inputs")
     p.add_argument("--decode-page-size", type=int, choices=[1, 2, 4, 8, 16], default=16,
                    help="view the decode pool as pages of this many tokens (same tokens, same memory)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -223,7 +225,7 @@ def main():
         do = torch.empty_like(dq)
         dlse = torch.empty((Bd, Hq), dtype=torch.float32, device=dev)
     if run_fp8:
-        m8 = W.fp8_prefill()
+        m8 = W.fp8_prefill(args.fp8_format)
         t8 = [torch.from_numpy(np.ascontiguousarray(x)).to(dev)
               for x in (m8.q8, m8.k8, m8.v8, m8.q_scale, m8.k_scale, m8.v_scale)]
         B8, N8, H8, d8 = m8.q8.shape
@@ -248,9 +250,9 @@ def main():
             ev[3].record(stream)
         if run_fp8:
             ev[4].record(stream)
-            r = ea.lib().ea_attn_fwd_mx8(*[ea._ptr(x) for x in t8], ea._ptr(o8), ea._ptr(lse8), B8, N8, H8, H8, d8,
-                                        1, m8.scale, stream.cuda_stream)
-            ea._check(r, "ea_attn_fwd_mx8")
+            r = ea.lib().ea_attn_fwd_mx8_fmt(*[ea._ptr(x) for x in t8], ea._ptr(o8), ea._ptr(lse8), B8, N8, H8, H8,
+                                            d8, 1, m8.scale, ea.FP8_FORMATS[m8.fmt], None, stream.cuda_stream)
+            ea._check(r, "ea_attn_fwd_mx8_fmt")
             ev[5].record(stream)
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
@@ -298,13 +300,14 @@ def main():
         flops8 = prefill_flops(B8, H8, N8, d8)
         tf8 = flops8 / (t_8.mean() * 1e-3) / 1e12
         out["fp8"] = {"value": tf8, "unit": "TFLOP/s", "ms_mean": float(t_8.mean()), "ms_min": float(t_8.min()),
-                      "flop_per_launch": flops8, "workload": "B=2 H=16 N=16384 d=128 causal MX e4m3"}
+                      "flop_per_launch": flops8, "workload": f"B=2 H=16 N=16384 d=128 causal MX {m8.fmt}"}
         if run_prefill:
             out["fp8"]["ratio_to_bf16"] = tf8 / out["value"]
         out["roofline_fp8"] = {"bound": "mfma", "achieved": tf8, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                               "frac": tf8 / PEAK_FP8_TFLOPS, "traffic": TRAFFIC_FP8, "kernel": "ea::fwd_mx8_sp_kernel<causal>"}
+                               "frac": tf8 / PEAK_FP8_TFLOPS, "traffic": TRAFFIC_FP8 if m8.fmt == "e4m3" else None,
+                               "kernel": f"ea::fwd_mx8_sp_kernel<causal, {m8.fmt}>"}
         if not (run_prefill or run_decode):
-            out["value"], out["unit"], out["dtype"] = tf8, "TFLOP/s", "fp8_e4m3"
+            out["value"], out["unit"], out["dtype"] = tf8, "TFLOP/s", f"fp8_{m8.fmt}"
     if not args.no_gemm_calibration:
         for key, dt_name, n in (("roofline", "bf16", 8192), ("roofline_fp8", "fp8", 16384)):
             if key in out:

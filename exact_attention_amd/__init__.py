@@ -49,6 +49,8 @@ _SIGNATURES = {
     "ea_attn_fwd_mx8": ([_c_void_p] * 8 + [_c_int] * 6 + [_c_float, _c_void_p], _c_int),
     "ea_attn_fwd_mx8_tuned": ([_c_void_p] * 8 + [_c_int] * 6 + [_c_float, ctypes.POINTER(FwdTuning), _c_void_p],
                               _c_int),
+    "ea_attn_fwd_mx8_fmt": ([_c_void_p] * 8 + [_c_int] * 6 + [_c_float, _c_int, ctypes.POINTER(FwdTuning), _c_void_p],
+                            _c_int),
     "ea_decode_workspace_size": ([_c_int] * 7, _c_size_t),
     "ea_attn_decode_paged": ([_c_void_p] * 7 + [_c_int] * 7 + [_c_float, _c_int, _c_void_p, _c_size_t, _c_void_p], _c_int),
     "ea_test_exp2": ([_c_void_p, _c_void_p, _c_int, _c_int, _c_void_p], _c_int),
@@ -184,10 +186,16 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, caus
     return o, lse
 
 
+FP8_FORMATS = {"e4m3": 0, "e5m2": 1}
+
+
 def attn_fwd_mx8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = True, scale: float | None = None,
-                 *, tuning: FwdTuning | None = None, want_lse: bool = True):
-    """MX fp8 forward. q8/k8/v8 [B,N,H,d] uint8 e4m3 codes; q_scale/k_scale
-    [B,N,H,d/32] and v_scale [B,N/32,Hkv,d] uint8 e8m0. Returns (o bf16, lse)."""
+                 *, tuning: FwdTuning | None = None, want_lse: bool = True, fmt: str = "e4m3"):
+    """MX fp8 forward. q8/k8/v8 [B,N,H,d] uint8 codes in ``fmt`` ("e4m3" or
+    "e5m2"); q_scale/k_scale [B,N,H,d/32] and v_scale [B,N/32,Hkv,d] uint8
+    e8m0. Returns (o bf16, lse)."""
+    if fmt not in FP8_FORMATS:
+        raise ValueError(f"fmt must be one of {sorted(FP8_FORMATS)}")
     for t, n in ((q8, "q8"), (k8, "k8"), (v8, "v8"), (q_scale, "q_scale"), (k_scale, "k_scale"), (v_scale, "v_scale")):
         _need(t, n, torch.uint8, 4)
     B, N, Hq, d = q8.shape
@@ -196,9 +204,10 @@ def attn_fwd_mx8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = True, sca
         scale = 1.0 / math.sqrt(d)
     o = torch.empty((B, N, Hq, d), dtype=torch.bfloat16, device=q8.device)
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q8.device) if want_lse else None
-    st = lib().ea_attn_fwd_mx8_tuned(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale),
-                                     _ptr(o), _ptr(lse), B, N, Hq, Hkv, d, int(bool(causal)), float(scale),
-                                     ctypes.byref(tuning) if tuning is not None else None, _stream(q8))
+    st = lib().ea_attn_fwd_mx8_fmt(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale),
+                                   _ptr(o), _ptr(lse), B, N, Hq, Hkv, d, int(bool(causal)), float(scale),
+                                   FP8_FORMATS[fmt], ctypes.byref(tuning) if tuning is not None else None,
+                                   _stream(q8))
     _check(st, "ea_attn_fwd_mx8")
     return o, lse
 

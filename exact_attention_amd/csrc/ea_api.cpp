@@ -194,10 +194,10 @@ ea_status ea_varlen_lpt_order(const int* cu_seqlens_q, const int* cu_seqlens_k, 
                     "varlen LPT order launch");
 }
 
-ea_status ea_attn_fwd_mx8_tuned(const void* q8, const void* k8, const void* v8, const uint8_t* q_scale,
-                                const uint8_t* k_scale, const uint8_t* v_scale, void* o, float* lse,
-                                int B, int N, int Hq, int Hkv, int d, int causal, float scale,
-                                const ea_fwd_tuning* tuning, void* stream) {
+ea_status ea_attn_fwd_mx8_fmt(const void* q8, const void* k8, const void* v8, const uint8_t* q_scale,
+                              const uint8_t* k_scale, const uint8_t* v_scale, void* o, float* lse,
+                              int B, int N, int Hq, int Hkv, int d, int causal, float scale, int in_format,
+                              const ea_fwd_tuning* tuning, void* stream) {
   if (!q8 || !k8 || !v8 || !q_scale || !k_scale || !v_scale || !o)
     return fail(EA_ERR_INVALID, "tensor pointers must be non-null");
   if (B <= 0 || N <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0)
@@ -208,6 +208,8 @@ ea_status ea_attn_fwd_mx8_tuned(const void* q8, const void* k8, const void* v8, 
   if (!finite_pos(scale)) return fail(EA_ERR_INVALID, "scale must be finite and positive");
   if (causal != 0 && causal != 1) return fail(EA_ERR_INVALID, "causal must be 0 or 1");
   if ((long long)B * N >= (1LL << 31)) return fail(EA_ERR_UNSUPPORTED, "B * N must be below 2^31");
+  if (in_format != EA_FP8_E4M3 && in_format != EA_FP8_E5M2)
+    return fail(EA_ERR_INVALID, "in_format must be EA_FP8_E4M3 (0) or EA_FP8_E5M2 (1)");
   if (ea_status st = check_tuning(tuning); st != EA_OK) return st;
   ea_fwd_tuning tt;
   ea_fwd_tuning_default(&tt);
@@ -237,9 +239,18 @@ ea_status ea_attn_fwd_mx8_tuned(const void* q8, const void* k8, const void* v8, 
   a.n_mb = (N + bm - 1) / bm;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.tau = tt.rescale_log2;
+  a.fmt = in_format;
   const hipError_t e = pipelined ? ea::launch_fwd_mx8_sp(a, causal != 0, (hipStream_t)stream)
                                  : ea::launch_fwd_mx8(a, causal != 0, (hipStream_t)stream);
   return hip_status(e, "MX fp8 forward launch");
+}
+
+ea_status ea_attn_fwd_mx8_tuned(const void* q8, const void* k8, const void* v8, const uint8_t* q_scale,
+                                const uint8_t* k_scale, const uint8_t* v_scale, void* o, float* lse,
+                                int B, int N, int Hq, int Hkv, int d, int causal, float scale,
+                                const ea_fwd_tuning* tuning, void* stream) {
+  return ea_attn_fwd_mx8_fmt(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, N, Hq, Hkv, d, causal, scale,
+                             EA_FP8_E4M3, tuning, stream);
 }
 
 ea_status ea_attn_fwd_mx8(const void* q8, const void* k8, const void* v8, const uint8_t* q_scale,

@@ -1,4 +1,7 @@
-// Exact attention forward with MX-scaled FP8 (OCP e4m3) inputs for gfx950.
+// Exact attention forward with MX-scaled FP8 inputs (OCP e4m3, or e5m2 as
+// "Faster, more flexible FlashAttention-4 for LLM inference", PR 2109, also
+// allows) for gfx950. The input format only changes the format fields of the
+// scaled MFMA; P is re-quantised to e4m3 in both cases.
 //
 // Method ("Low-precision FlashAttention-4: end-to-end block-scaled attention
 // for Blackwell", section 2.1): both contractions use block-scaled MMA with
@@ -41,15 +44,20 @@ __device__ __forceinline__ int tile8_off(int row, int col) {
   return row * 128 + (((col >> 4) ^ swz8(row)) << 4) + (col & 15);
 }
 
+// Operand formats of the scaled MFMA (its cbsz / blgp fields): 0 = fp8 OCP
+// e4m3, 1 = bf8 OCP e5m2.
+constexpr int kFmtE4M3 = 0;
+constexpr int kFmtE5M2 = 1;
+
+template <int FA, int FB>
 __device__ __forceinline__ f32x16 mfma_mx8(i32x8 a, i32x8 b, f32x16 c, int scale_a, int scale_b) {
-  // formats: 0 = fp8 e4m3 for both operands
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, scale_b);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, scale_a, 0, scale_b);
 }
 // same, with the scale of A taken from byte SA of its register (the
 // instruction's own byte select; the other bytes are ignored)
-template <int SA>
+template <int SA, int FA, int FB>
 __device__ __forceinline__ f32x16 mfma_mx8_sel(i32x8 a, i32x8 b, f32x16 c, int scale_a, int scale_b) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, SA, scale_a, 0, scale_b);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, SA, scale_a, 0, scale_b);
 }
 
 __device__ __forceinline__ i32x2 ds_read_tr8(const EA_LDS uint8_t* p) {
@@ -72,7 +80,8 @@ __device__ __forceinline__ void keep8(const i32x8& x) { asm volatile("" ::"v"(x)
 
 }  // namespace
 
-template <bool CAUSAL>
+// FMT: format of Q, K and V (kFmtE4M3 or kFmtE5M2); P is always e4m3.
+template <bool CAUSAL, int FMT>
 __global__ __launch_bounds__(256, 2) void fwd_mx8_kernel(Mx8Args a) {
   constexpr int D = 128, BM = kFwdBlockM, BN = kFwdBlockN;
   constexpr int TILE = BN * D;            // bytes per K or V tile
@@ -224,9 +233,9 @@ __global__ __launch_bounds__(256, 2) void fwd_mx8_kernel(Mx8Args a) {
       const i32x4 a0h = lds_load<i32x4>(ks + k_off[kq][1]);
       const i32x4 a1l = lds_load<i32x4>(ks + k_off[kq][0] + 32 * D);
       const i32x4 a1h = lds_load<i32x4>(ks + k_off[kq][1] + 32 * D);
-      s0 = mfma_mx8(i32x8{a0l[0], a0l[1], a0l[2], a0l[3], a0h[0], a0h[1], a0h[2], a0h[3]}, qf[kq], s0,
+      s0 = mfma_mx8<FMT, FMT>(i32x8{a0l[0], a0l[1], a0l[2], a0l[3], a0h[0], a0h[1], a0h[2], a0h[3]}, qf[kq], s0,
                     kscale[0][kq], qsc[kq]);
-      s1 = mfma_mx8(i32x8{a1l[0], a1l[1], a1l[2], a1l[3], a1h[0], a1h[1], a1h[2], a1h[3]}, qf[kq], s1,
+      s1 = mfma_mx8<FMT, FMT>(i32x8{a1l[0], a1l[1], a1l[2], a1l[3], a1h[0], a1h[1], a1h[2], a1h[3]}, qf[kq], s1,
                     kscale[1][kq], qsc[kq]);
     }
     __builtin_amdgcn_s_setprio(0);
@@ -287,7 +296,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mx8_kernel(Mx8Args a) {
       const i32x2 r2 = ds_read_tr8(vs + v_off[dt] + 32 * D);
       const i32x2 r3 = ds_read_tr8(vs + v_off[dt] + 48 * D);
       const i32x8 va = {r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
-      oacc[dt] = mfma_mx8(va, pb, oacc[dt], vscale[dt], kScaleOne);
+      oacc[dt] = mfma_mx8<FMT, kFmtE4M3>(va, pb, oacc[dt], vscale[dt], kScaleOne);
     }
     __builtin_amdgcn_s_setprio(0);
   };
@@ -338,7 +347,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mx8_kernel(Mx8Args a) {
 // the V scales of the current one are loaded a step ahead into registers.
 // Masking runs before the block under a branch (diagonal and ragged tiles,
 // and tiles past a wave's causal limit), the lazy O rescale after it.
-template <bool CAUSAL>
+template <bool CAUSAL, int FMT>
 __global__ __launch_bounds__(512, 1) void fwd_mx8_sp_kernel(Mx8Args a) {
   constexpr int D = 128, BM = kPpBlockM, BN = kFwdBlockN;
   constexpr int TILE = BN * D;  // bytes per K or V tile
@@ -540,13 +549,13 @@ __global__ __launch_bounds__(512, 1) void fwd_mx8_sp_kernel(Mx8Args a) {
         const int t = i & 1, k2 = i >> 1;
         f32x16& sn = t ? sn1 : sn0;
         if (k2 == 0) {
-          sn = mfma_mx8_sel<0>(opnd[i], qf[0], f32x16{}, ksh[t], qsc[0]);
+          sn = mfma_mx8_sel<0, FMT, FMT>(opnd[i], qf[0], f32x16{}, ksh[t], qsc[0]);
         } else {
-          sn = mfma_mx8_sel<2>(opnd[i], qf[1], sn, ksh[t], qsc[1]);
+          sn = mfma_mx8_sel<2, FMT, FMT>(opnd[i], qf[1], sn, ksh[t], qsc[1]);
         }
       } else {
         const int dt = i - 4;
-        oacc[dt] = mfma_mx8(opnd[i], pprev, oacc[dt], (int)vraw_cur[dt], kScaleOne);
+        oacc[dt] = mfma_mx8<FMT, kFmtE4M3>(opnd[i], pprev, oacc[dt], (int)vraw_cur[dt], kScaleOne);
       }
       if (i == 0) {
         load_kscale(s + 2, kraw_nxt);
@@ -656,9 +665,9 @@ __global__ __launch_bounds__(512, 1) void fwd_mx8_sp_kernel(Mx8Args a) {
     const i32x4 a0h = lds_load<i32x4>((EA_LDS uint8_t*)ks0 + k_off[k2][1]);
     const i32x4 a1l = lds_load<i32x4>((EA_LDS uint8_t*)ks0 + k_off[k2][0] + 32 * D);
     const i32x4 a1h = lds_load<i32x4>((EA_LDS uint8_t*)ks0 + k_off[k2][1] + 32 * D);
-    sc0 = mfma_mx8(i32x8{a0l[0], a0l[1], a0l[2], a0l[3], a0h[0], a0h[1], a0h[2], a0h[3]}, qf[k2],
+    sc0 = mfma_mx8<FMT, FMT>(i32x8{a0l[0], a0l[1], a0l[2], a0l[3], a0h[0], a0h[1], a0h[2], a0h[3]}, qf[k2],
                    k2 == 0 ? f32x16{} : sc0, s0k, qsc[k2]);
-    sc1 = mfma_mx8(i32x8{a1l[0], a1l[1], a1l[2], a1l[3], a1h[0], a1h[1], a1h[2], a1h[3]}, qf[k2],
+    sc1 = mfma_mx8<FMT, FMT>(i32x8{a1l[0], a1l[1], a1l[2], a1l[3], a1h[0], a1h[1], a1h[2], a1h[3]}, qf[k2],
                    k2 == 0 ? f32x16{} : sc1, s1k, qsc[k2]);
   }
   __syncthreads();
@@ -699,24 +708,31 @@ __global__ __launch_bounds__(512, 1) void fwd_mx8_sp_kernel(Mx8Args a) {
   }
 }
 
-hipError_t launch_fwd_mx8_sp(const Mx8Args& a, bool causal, hipStream_t s) {
+template <int FMT>
+static hipError_t launch_mx8_f(const Mx8Args& a, bool causal, bool pipelined, hipStream_t s) {
   const int grid = 8 * ((a.B * a.Hq + 7) / 8) * a.n_mb;
-  if (causal) {
-    hipLaunchKernelGGL(fwd_mx8_sp_kernel<true>, dim3(grid), dim3(512), 0, s, a);
+  if (pipelined) {
+    if (causal) {
+      hipLaunchKernelGGL((fwd_mx8_sp_kernel<true, FMT>), dim3(grid), dim3(512), 0, s, a);
+    } else {
+      hipLaunchKernelGGL((fwd_mx8_sp_kernel<false, FMT>), dim3(grid), dim3(512), 0, s, a);
+    }
   } else {
-    hipLaunchKernelGGL(fwd_mx8_sp_kernel<false>, dim3(grid), dim3(512), 0, s, a);
+    if (causal) {
+      hipLaunchKernelGGL((fwd_mx8_kernel<true, FMT>), dim3(grid), dim3(256), 0, s, a);
+    } else {
+      hipLaunchKernelGGL((fwd_mx8_kernel<false, FMT>), dim3(grid), dim3(256), 0, s, a);
+    }
   }
   return hipGetLastError();
 }
 
+hipError_t launch_fwd_mx8_sp(const Mx8Args& a, bool causal, hipStream_t s) {
+  return a.fmt == kFmtE5M2 ? launch_mx8_f<kFmtE5M2>(a, causal, true, s) : launch_mx8_f<kFmtE4M3>(a, causal, true, s);
+}
+
 hipError_t launch_fwd_mx8(const Mx8Args& a, bool causal, hipStream_t s) {
-  const int grid = 8 * ((a.B * a.Hq + 7) / 8) * a.n_mb;
-  if (causal) {
-    hipLaunchKernelGGL(fwd_mx8_kernel<true>, dim3(grid), dim3(256), 0, s, a);
-  } else {
-    hipLaunchKernelGGL(fwd_mx8_kernel<false>, dim3(grid), dim3(256), 0, s, a);
-  }
-  return hipGetLastError();
+  return a.fmt == kFmtE5M2 ? launch_mx8_f<kFmtE5M2>(a, causal, false, s) : launch_mx8_f<kFmtE4M3>(a, causal, false, s);
 }
 
 }  // namespace ea

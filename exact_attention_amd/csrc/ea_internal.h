@@ -58,6 +58,7 @@ struct Mx8Args {
   int n_mb;
   float scale_log2;
   float tau;
+  int fmt;  // Q/K/V codes: 0 = OCP e4m3, 1 = OCP e5m2
 };
 hipError_t launch_fwd_mx8(const Mx8Args& a, bool causal, hipStream_t s);
 // 8-wave software-pipelined MX fp8 forward; a.n_mb counts kPpBlockM-row blocks

@@ -195,6 +195,23 @@ ea_status ea_attn_fwd_mx8_tuned(const void* q8, const void* k8, const void* v8,
                                 void* o, float* lse, int B, int N, int Hq, int Hkv, int d, int causal,
                                 float scale, const ea_fwd_tuning* tuning, void* stream);
 
+/* FP8 element formats of the MX inputs (OCP FP8): e4m3 = 4 exponent bits
+ * (bias 7), 3 mantissa bits, largest finite 448, no infinities; e5m2 = 5
+ * exponent bits (bias 15), 2 mantissa bits, largest finite 57344, with
+ * infinities. "Faster, more flexible FlashAttention-4 for LLM inference", PR
+ * 2109, accepts both for the attention inputs. */
+enum { EA_FP8_E4M3 = 0, EA_FP8_E5M2 = 1 };
+/*
+ * ea_attn_fwd_mx8_fmt -- ea_attn_fwd_mx8_tuned with the element format of the
+ * q8 / k8 / v8 codes given by in_format (EA_FP8_E4M3 or EA_FP8_E5M2; anything
+ * else is EA_ERR_INVALID). Scales, layouts, tuning and outputs are those of
+ * ea_attn_fwd_mx8_tuned; P is re-quantised to e4m3 in both cases (P <=
+ * 2^rescale_log2 fits e4m3's range).
+ */
+ea_status ea_attn_fwd_mx8_fmt(const void* q8, const void* k8, const void* v8,
+                              const uint8_t* q_scale, const uint8_t* k_scale, const uint8_t* v_scale,
+                              void* o, float* lse, int B, int N, int Hq, int Hkv, int d, int causal,
+                              float scale, int in_format, const ea_fwd_tuning* tuning, void* stream);
 /*
  * Paged split-KV decode ("Faster, more flexible FlashAttention-4 for LLM
  * inference": PR 1999/2104 for KV pages of any size, PR 1940 for splitting the

@@ -26,6 +26,7 @@ Parity status: every function is pinned by a CPU test in
 from .attention import (  # noqa: F401
     bf16_to_f64,
     e4m3_to_f64,
+    e5m2_to_f64,
     e8m0_to_f64,
     dequant_mx,
     allowed_keys,

@@ -56,16 +56,30 @@ def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
     return s * val
 
 
+def e5m2_to_f64(codes: np.ndarray) -> np.ndarray:
+    """OCP FP8 E5M2 codes -> float64: sign, 5-bit exponent (bias 15), 2-bit
+    mantissa; exponent 0 is subnormal (m * 2^-16); exponent 31 is infinity
+    (m = 0) or NaN."""
+    c = np.asarray(codes).astype(np.int64)
+    s = np.where((c >> 7) & 1, -1.0, 1.0)
+    e = (c >> 2) & 0x1F
+    m = c & 0x3
+    val = np.where(e == 0, m * 2.0 ** -16, (1.0 + m / 4.0) * np.ldexp(1.0, e - 15))
+    val = np.where(e == 31, np.where(m == 0, np.inf, np.nan), val)
+    return s * val
+
+
 def e8m0_to_f64(scales: np.ndarray) -> np.ndarray:
     """E8M0 scale bytes -> 2^(byte - 127) (0xFF is NaN)."""
     s = np.asarray(scales).astype(np.int64)
     return np.where(s == 255, np.nan, np.ldexp(1.0, s - 127))
 
 
-def dequant_mx(codes: np.ndarray, scales: np.ndarray, axis: int, block: int = 32) -> np.ndarray:
-    """Dequantise MX e4m3 data: element value times the e8m0 scale of its block
-    of ``block`` consecutive elements along ``axis`` [P5 §2.1]."""
-    vals = e4m3_to_f64(codes)
+def dequant_mx(codes: np.ndarray, scales: np.ndarray, axis: int, block: int = 32, fmt: str = "e4m3") -> np.ndarray:
+    """Dequantise MX fp8 data (``fmt`` "e4m3" or "e5m2"): element value times
+    the e8m0 scale of its block of ``block`` consecutive elements along
+    ``axis`` [P5 §2.1]."""
+    vals = {"e4m3": e4m3_to_f64, "e5m2": e5m2_to_f64}[fmt](codes)
     sc = np.repeat(e8m0_to_f64(scales), block, axis=axis)
     return vals * sc
 

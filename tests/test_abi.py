@@ -30,7 +30,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("ea_attn_fwd", "ea_attn_fwd_varlen", "ea_attn_fwd_varlen_ordered", "ea_varlen_lpt_order",
-              "ea_attn_fwd_mx8", "ea_attn_fwd_mx8_tuned", "ea_attn_decode_paged",
+              "ea_attn_fwd_mx8", "ea_attn_fwd_mx8_tuned", "ea_attn_fwd_mx8_fmt", "ea_attn_decode_paged",
               "ea_decode_workspace_size", "ea_last_error"):
         assert n in names
 
@@ -83,6 +83,10 @@ def test_mx8_argument_errors(lib):
     assert f(P, P, P, P, P, None, P, None, 1, 64, 2, 2, 128, 1, 0.1, None) == -1
     assert f(P, P, P, P, P, P, P, None, 1, 48, 2, 2, 128, 1, 0.1, None) == -2   # N % 32
     assert f(P, P, P, P, P, P, P, None, 1, 64, 2, 2, 64, 1, 0.1, None) == -2    # d
+    g = lib.ea_attn_fwd_mx8_fmt
+    assert g(P, P, P, P, P, P, P, None, 1, 64, 2, 2, 128, 1, 0.1, 2, None, None) == -1   # no such format
+    assert "in_format" in _err(lib)
+    assert g(P, P, P, P, P, P, P, None, 1, 64, 2, 2, 64, 1, 0.1, 1, None, None) == -2    # d, e5m2
 
 
 def test_mx8_tuning_errors(lib):

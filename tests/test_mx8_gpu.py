@@ -1,5 +1,5 @@
 """GPU parity of the MX fp8 forward against the fp64 oracle on the dequantised
-inputs (e4m3 value x 2^(e8m0 - 127), exact in fp64).
+inputs (e4m3 or e5m2 value x 2^(e8m0 - 127), exact in fp64).
 
 The kernel re-quantises P to e4m3 before P V, which the oracle does not mirror
 (the kernel's P depends on its running max and tiling), so the contract is
@@ -29,14 +29,15 @@ def run_mx8(m, kernel=0):
     import exact_attention_amd as ea
     t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
     o, lse = ea.attn_fwd_mx8(t(m.q8), t(m.k8), t(m.v8), t(m.q_scale), t(m.k_scale), t(m.v_scale),
-                             m.causal, m.scale, tuning=ea.tuning(kernel=kernel))
+                             m.causal, m.scale, tuning=ea.tuning(kernel=kernel), fmt=m.fmt)
     torch.cuda.synchronize()
     return f64(host_bits(o)), lse.cpu().numpy().astype(np.float64)
 
 
 def deq(m):
-    return (oracle.dequant_mx(m.q8, m.q_scale, axis=3), oracle.dequant_mx(m.k8, m.k_scale, axis=3),
-            oracle.dequant_mx(m.v8, m.v_scale, axis=1))
+    return (oracle.dequant_mx(m.q8, m.q_scale, axis=3, fmt=m.fmt),
+            oracle.dequant_mx(m.k8, m.k_scale, axis=3, fmt=m.fmt),
+            oracle.dequant_mx(m.v8, m.v_scale, axis=1, fmt=m.fmt))
 
 
 def check_normwise(o, ro, lse, rl, what):
@@ -60,17 +61,18 @@ def check_normwise(o, ro, lse, rl, what):
     (2, 320, 4, 2, True),      # N % 64 != 0 (ragged tail tile), GQA 2:1
     (1, 96, 1, 1, False), (1, 1024, 2, 1, True)])
 @pytest.mark.parametrize("kernel", KERNELS)
-def test_mx8_small(shape, kernel):
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_mx8_small(shape, kernel, fmt):
     B, N, Hq, Hkv, causal = shape
-    log(f"mx8 shape {shape} kernel {kernel}")
+    log(f"mx8 shape {shape} kernel {kernel} {fmt}")
     # quantise Q with Hq heads and K/V with Hkv heads
     qf = W.normal_f32(300 + N, W.STREAM_Q, B * N * Hq * 128).reshape(B, N, Hq, 128)
     kf = W.normal_f32(300 + N, W.STREAM_K, B * N * Hkv * 128).reshape(B, N, Hkv, 128)
     vf = W.normal_f32(300 + N, W.STREAM_V, B * N * Hkv * 128).reshape(B, N, Hkv, 128)
-    q8, qs = W.mx_quantize_e4m3(qf, axis=3)
-    k8, ks = W.mx_quantize_e4m3(kf, axis=3)
-    v8, vs = W.mx_quantize_e4m3(vf, axis=1)
-    m = W.MX8(q8, k8, v8, qs, ks, vs, causal, 1 / np.sqrt(128))
+    q8, qs = W.mx_quantize(qf, axis=3, fmt=fmt)
+    k8, ks = W.mx_quantize(kf, axis=3, fmt=fmt)
+    v8, vs = W.mx_quantize(vf, axis=1, fmt=fmt)
+    m = W.MX8(q8, k8, v8, qs, ks, vs, causal, 1 / np.sqrt(128), fmt)
     o, lse = run_mx8(m, kernel)
     q, k, v = deq(m)
     ro, rl = oracle.attention(q, k, v, causal, m.scale)
@@ -102,5 +104,30 @@ def test_fp8_workload_sampled(kernel):
         nrm = np.linalg.norm(got - ro) / np.linalg.norm(ro)
         dl = np.abs(lse[b, h, rows] - rl).max()
         log(f"  (b={b},h={h}) sampled rows: normwise {nrm:.3e} max|dlse| {dl:.3e}")
+        assert nrm <= NORM_TOL and dl <= LSE_TOL
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_e5m2_long_sampled(kernel):
+    """e5m2 inputs at the fp8 workload's sequence length (B=1, H=4, N=16384,
+    causal), sampled rows; the same bits read as e4m3 would be far off, so
+    this also shows the format reaches the matrix core."""
+    m = W.mx8(1, 16384, 4, 128, True, seed=1104, fmt="e5m2")
+    log(f"mx8 e5m2 shape={m.q8.shape} kernel {kernel}")
+    o, lse = run_mx8(m, kernel)
+    N = m.q8.shape[1]
+    rng = np.random.default_rng(9)
+    rows = sorted(set([0, 1, 64, 255, 256, N // 2, N - 1] + rng.integers(0, N, 16).tolist()))
+    for h in range(4):
+        sl = (slice(0, 1), slice(None), slice(h, h + 1))
+        q = oracle.dequant_mx(m.q8[sl], m.q_scale[sl], axis=3, fmt="e5m2")
+        k = oracle.dequant_mx(m.k8[sl], m.k_scale[sl], axis=3, fmt="e5m2")
+        v = oracle.dequant_mx(m.v8[sl], m.v_scale[sl], axis=1, fmt="e5m2")
+        ro, rl = oracle.attention_rows(q, k, v, 0, 0, rows, True, m.scale)
+        got = o[0, rows, h, :]
+        nrm = np.linalg.norm(got - ro) / np.linalg.norm(ro)
+        dl = np.abs(lse[0, h, rows] - rl).max()
+        log(f"  h={h} sampled rows: normwise {nrm:.3e} max|dlse| {dl:.3e}")
         assert nrm <= NORM_TOL and dl <= LSE_TOL
     assert np.isfinite(o).all() and np.isfinite(lse).all()

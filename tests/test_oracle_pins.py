@@ -308,6 +308,46 @@ def test_e4m3_encode_matches_torch_in_range_and_roundtrips():
     assert W.f32_to_e4m3_bits(np.array([1000.0, -1000.0])).tolist() == [0x7E, 0xFE]
 
 
+def test_e5m2_decode_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.e5m2_to_f64(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e5m2).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert ours[0x7B] == 57344.0 and ours[0x7C] == np.inf and ours[0x01] == 2.0 ** -16 and ours[0x04] == 2.0 ** -14
+
+
+def test_e5m2_encode_matches_torch_in_range_and_roundtrips():
+    x = np.concatenate([_rand(20000, 44) * 3000, _rand(2000, 45) * 1e-3, _rand(200, 46) * 1e-5])
+    x = x[np.abs(x) <= 57344]
+    ours = W.f32_to_e5m2_bits(x)
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.float8_e5m2).view(torch.uint8).numpy()
+    assert np.array_equal(ours, ref)
+    finite = np.array([c for c in range(256) if ((c >> 2) & 0x1F) != 0x1F], dtype=np.uint8)
+    vals = oracle.e5m2_to_f64(finite)
+    assert np.array_equal(oracle.e5m2_to_f64(W.f32_to_e5m2_bits(vals)), vals)
+    assert W.f32_to_e5m2_bits(np.array([1e6, -1e6])).tolist() == [0x7B, 0xFB]
+
+
+def test_mx_quantiser_e5m2_invariants():
+    x = _rand((2, 64, 2, 64), 47).astype(np.float32)
+    x[1, 3, 1, 32:] = 0.0
+    codes, sc = W.mx_quantize(x, axis=3, fmt="e5m2")
+    deq = oracle.dequant_mx(codes, sc, axis=3, fmt="e5m2")
+    vals = oracle.e5m2_to_f64(codes)
+    assert np.all(np.isfinite(vals)) and np.all(np.abs(vals) <= 57344)
+    nz = sc != 0
+    blkmax = np.abs(vals).reshape(2, 64, 2, 2, 32).max(-1)
+    assert np.all(blkmax[nz] >= 28672) and np.all(blkmax[nz] <= 57344)     # ceil rule: in [fmax/2, fmax]
+    assert np.all(deq[1, 3, 1, 32:] == 0)
+    rel = np.abs(deq - x) / np.maximum(np.abs(x), 1e-30)
+    normal = np.abs(vals) >= 2.0 ** -14
+    assert np.all(rel[normal] <= 2.0 ** -3 + 1e-12)                        # 2 mantissa bits
+    # an e5m2 tensor decoded as e4m3 is a different tensor (the format matters)
+    assert not np.allclose(oracle.dequant_mx(codes, sc, axis=3), deq)
+
+
 def test_e8m0_and_mx_quantiser_invariants():
     assert oracle.e8m0_to_f64(np.array([127, 0, 254, 128])).tolist() == [1.0, 2.0 ** -127, 2.0 ** 127, 2.0]
     x = _rand((3, 64, 2, 96), 37).astype(np.float32)

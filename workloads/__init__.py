@@ -87,27 +87,62 @@ def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
     return code.astype(np.uint8)
 
 
-def _mx_rows(blk: np.ndarray):
+E5M2_MAX = 57344.0
+
+
+def f32_to_e5m2_bits(x: np.ndarray) -> np.ndarray:
+    """Encode finite values as OCP FP8 E5M2 (bias 15, 2 mantissa bits, largest
+    finite 57344), round to nearest even, saturating to +-57344 (the MX
+    quantiser never exceeds it). Returns uint8 codes; exact in float32."""
+    x = np.asarray(x, dtype=np.float32)
+    a = np.abs(x)
+    sign = np.signbit(x).astype(np.uint8)
+    # quantisation step: 2^(floor(log2 a) - 2) for normals, 2^-16 below 2^-14
+    _, e = np.frexp(np.maximum(a, np.float32(2.0 ** -14)))
+    step = np.ldexp(np.float32(1.0), (e - 3).astype(np.int32))
+    q = np.round(a / step) * step
+    q = np.minimum(q, np.float32(E5M2_MAX))
+    _, e2 = np.frexp(np.maximum(q, np.float32(2.0 ** -14)))
+    E = (e2 - 1).astype(np.int32)
+    normal = q >= np.float32(2.0 ** -14)
+    exp_field = np.where(normal, E + 15, 0).astype(np.uint8)
+    mant = np.where(normal, (q / np.ldexp(np.float32(1.0), E) - np.float32(1.0)) * np.float32(4.0),
+                    q / np.float32(2.0 ** -16))
+    code = (sign << 7) | (exp_field << 2) | np.rint(mant).astype(np.uint8)
+    return code.astype(np.uint8)
+
+
+FP8_FORMATS = {"e4m3": (E4M3_MAX, f32_to_e4m3_bits), "e5m2": (E5M2_MAX, f32_to_e5m2_bits)}
+
+
+def _mx_rows(blk: np.ndarray, fmt: str = "e4m3"):
     """MX quantisation of rows of 32-element blocks: blk [..., 32] float32."""
+    fmax, encode = FP8_FORMATS[fmt]
     amax = np.abs(blk).max(axis=-1).astype(np.float64)
-    ratio = amax / E4M3_MAX
+    ratio = amax / fmax
     f, e = np.frexp(np.where(ratio > 0, ratio, 1.0))      # ratio = f * 2^e, f in [0.5,1)
     E = np.where(f == 0.5, e - 1, e)                       # ceil(log2 ratio)
     E = np.where(amax > 0, E, -127)
     E = np.clip(E, -127, 127).astype(np.int32)
     scaled = blk * np.ldexp(np.float32(1.0), -E)[..., None].astype(np.float32)
-    return f32_to_e4m3_bits(scaled), (E + 127).astype(np.uint8)
+    return encode(scaled), (E + 127).astype(np.uint8)
 
 
 def mx_quantize_e4m3(x: np.ndarray, axis: int, block: int = 32, threads: int | None = None):
-    """Quantise float data to e4m3 codes with one e8m0 scale per ``block``
-    consecutive elements along ``axis``.
+    """mx_quantize with e4m3 element codes."""
+    return mx_quantize(x, axis, block, threads, fmt="e4m3")
+
+
+def mx_quantize(x: np.ndarray, axis: int, block: int = 32, threads: int | None = None, fmt: str = "e4m3"):
+    """Quantise float data to fp8 codes (``fmt`` "e4m3" or "e5m2") with one
+    e8m0 scale per ``block`` consecutive elements along ``axis``.
 
     Scale rule (one of two readings of the block-scaling recipe; the other one,
-    floor(log2 amax) - 8, can saturate the block maximum): E = ceil(log2(amax /
-    448)) computed from the exponent and mantissa bits, clamped to [-127, 127];
-    an all-zero block gets E = -127. The stored scale byte is E + 127 and the
-    element codes are e4m3(x / 2^E).
+    floor(log2 amax) - emax, can saturate the block maximum): E =
+    ceil(log2(amax / fmax)) computed from the exponent and mantissa bits, with
+    fmax the format's largest finite value (448 or 57344), clamped to
+    [-127, 127]; an all-zero block gets E = -127. The stored scale byte is
+    E + 127 and the element codes are fp8(x / 2^E).
 
     Returns (codes uint8 same shape as x, scales uint8 with ``axis`` shortened
     by ``block``)."""
@@ -126,7 +161,7 @@ def mx_quantize_e4m3(x: np.ndarray, axis: int, block: int = 32, threads: int | N
 
     def run(lo):
         hi = min(rows, lo + step)
-        c, s_ = _mx_rows(blk[lo:hi])
+        c, s_ = _mx_rows(blk[lo:hi], fmt)
         codes[lo:hi] = c
         scales[lo:hi] = s_
 
@@ -427,22 +462,24 @@ class MX8:
     v_scale: np.ndarray
     causal: bool
     scale: float
+    fmt: str = "e4m3"    # element format of q8 / k8 / v8
 
 
-def mx8(B: int, N: int, H: int, d: int, causal: bool, seed: int, scale: float | None = None) -> MX8:
+def mx8(B: int, N: int, H: int, d: int, causal: bool, seed: int, scale: float | None = None,
+        fmt: str = "e4m3") -> MX8:
     n = B * N * H * d
     q = normal_f32(seed, STREAM_Q, n).reshape(B, N, H, d)
-    q8, qs = mx_quantize_e4m3(q, axis=3)
+    q8, qs = mx_quantize(q, axis=3, fmt=fmt)
     del q
     k = normal_f32(seed, STREAM_K, n).reshape(B, N, H, d)
-    k8, ks = mx_quantize_e4m3(k, axis=3)
+    k8, ks = mx_quantize(k, axis=3, fmt=fmt)
     del k
     v = normal_f32(seed, STREAM_V, n).reshape(B, N, H, d)
-    v8, vs = mx_quantize_e4m3(v, axis=1)
+    v8, vs = mx_quantize(v, axis=1, fmt=fmt)
     del v
-    return MX8(q8, k8, v8, qs, ks, vs, causal, float(scale if scale is not None else 1.0 / np.sqrt(d)))
+    return MX8(q8, k8, v8, qs, ks, vs, causal, float(scale if scale is not None else 1.0 / np.sqrt(d)), fmt)
 
 
-def fp8_prefill() -> MX8:
-    """Workload 4: B=2, H=16, N=16384, d=128, causal, MX e4m3."""
-    return mx8(2, 16384, 16, 128, True, seed=1004)
+def fp8_prefill(fmt: str = "e4m3") -> MX8:
+    """Workload 4: B=2, H=16, N=16384, d=128, causal, MX e4m3 (or e5m2)."""
+    return mx8(2, 16384, 16, 128, True, seed=1004, fmt=fmt)
