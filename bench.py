@@ -60,6 +60,8 @@ def parse():
     p.add_argument("--no-gemm-calibration", action="store_true",
                    help="skip the vendor-GEMM rate measured after the timed region")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle time budget per leg")
+    p.add_argument("--prefill-dims", choices=["128,128", "192,128"], default="128,128",
+                   help="head dims (d_qk, d_v) of the bf16 prefill forward")
     p.add_argument("--fp8-format", choices=["e4m3", "e5m2"], default="e4m3",
                    help="element format of the fp8 forward's MX inputs")
     p.add_argument("--decode-page-size", type=int, choices=[1, 2, 4, 8, 16], default=16,
@@ -112,8 +114,10 @@ def gemm_rate(torch, dev, dtype_name, n, reps=10):
         return None
 
 
-def prefill_flops(B, H, N, d):
-    return 4.0 * B * H * N * N * d / 2.0
+def prefill_flops(B, H, N, d, dv=None):
+    """Causal forward FLOPs, counted as half of the full N x N work:
+    2 N^2 d (scores) + 2 N^2 dv (P V) per (batch, head), halved."""
+    return 2.0 * B * H * N * N * (d + (dv or d)) / 2.0
 
 
 def decode_bytes(seq_lens, Hq, Hkv, d, page_size):
@@ -137,7 +141,7 @@ def cpu_baseline_prefill(inp, budget_s):
             k = _f64(inp.k[b:b + 1, :, h:h + 1])
             v = _f64(inp.v[b:b + 1, :, h:h + 1])
             oracle.attention(q, k, v, True, inp.scale, threads=threads)
-            done_flops += prefill_flops(1, 1, N, d)
+            done_flops += prefill_flops(1, 1, N, d, inp.v.shape[3])
             heads += 1
             if time.perf_counter() - t0 > budget_s:
                 break
@@ -196,9 +200,10 @@ def main():
     run_fp8 = args.only in (None, "fp8")
     t_gen = time.perf_counter()
     if run_prefill:
-        inp = W.prefill(True)
+        d_qk, d_v = (int(x) for x in args.prefill_dims.split(","))
+        inp = W.prefill(True) if d_qk == 128 else W.dense(4, 8192, 8192, 16, 16, d_qk, True, seed=1192, dv=d_v)
         q, k, v = dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v)
-        o = torch.empty_like(q)
+        o = torch.empty_like(q) if d_v == d_qk else torch.empty(q.shape[:3] + (d_v,), dtype=q.dtype, device=dev)
         B, N, H, d = inp.q.shape
         lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
         tun = ea.tuning(exp_mode=args.exp_mode)
@@ -269,12 +274,13 @@ def main():
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1), bf16-rounded)"}
-    cfg = {"workload": "prefill fwd B=4 H=16 N=8192 d=128 causal bf16 + paged decode B=64 Hq=32 Hkv=8 "
+    pf_dims = "d=128" if args.prefill_dims == "128,128" else f"(d_qk,d_v)=({args.prefill_dims})"
+    cfg = {"workload": f"prefill fwd B=4 H=16 N=8192 {pf_dims} causal bf16 + paged decode B=64 Hq=32 Hkv=8 "
                        f"d=128 ctx U[512,32768] page {args.decode_page_size} bf16 (split-KV + LSE combine)",
            "exp_mode": args.exp_mode, "input_gen_s": round(t_gen, 1)}
     if run_prefill:
         t_pf = np.array([e[0].elapsed_time(e[1]) for e in evs])      # ms
-        flops = prefill_flops(B, H, N, d)
+        flops = prefill_flops(B, H, N, d, d_v)
         tf = flops / (t_pf.mean() * 1e-3) / 1e12
         out["value"] = tf
         out["unit"] = "TFLOP/s"

@@ -42,6 +42,7 @@ _SIGNATURES = {
     "ea_fwd_tuning_default": ([ctypes.POINTER(FwdTuning)], None),
     "ea_attn_fwd": ([_c_void_p] * 5 + [_c_int] * 7 + [_c_float, _c_void_p], _c_int),
     "ea_attn_fwd_tuned": ([_c_void_p] * 5 + [_c_int] * 7 + [_c_float, ctypes.POINTER(FwdTuning), _c_void_p], _c_int),
+    "ea_attn_fwd_hd": ([_c_void_p] * 5 + [_c_int] * 8 + [_c_float, ctypes.POINTER(FwdTuning), _c_void_p], _c_int),
     "ea_attn_fwd_varlen": ([_c_void_p] * 7 + [_c_int] * 8 + [_c_float, ctypes.POINTER(FwdTuning), _c_void_p], _c_int),
     "ea_attn_fwd_varlen_ordered": ([_c_void_p] * 7 + [_c_int] * 8 + [_c_float, _c_void_p, ctypes.POINTER(FwdTuning),
                                                                     _c_void_p], _c_int),
@@ -116,23 +117,25 @@ def tuning(exp_mode: int = EA_EXP_HW, rescale_log2: float = 8.0, natural_order: 
 
 def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, *, tuning: FwdTuning | None = None,
              out: torch.Tensor | None = None, lse: torch.Tensor | None = None, want_lse: bool = True):
-    """Exact attention forward. q [B,Nq,Hq,d], k/v [B,Nk,Hkv,d] bf16 (BSHD).
-    Returns (o [B,Nq,Hq,d] bf16, lse [B,Hq,Nq] fp32 natural log or None)."""
+    """Exact attention forward. q [B,Nq,Hq,d], k [B,Nk,Hkv,d], v [B,Nk,Hkv,dv]
+    bf16 (BSHD); dv = d, or (d, dv) = (192, 128). Returns (o [B,Nq,Hq,dv]
+    bf16, lse [B,Hq,Nq] fp32 natural log or None)."""
     _need(q, "q", torch.bfloat16, 4)
     _need(k, "k", torch.bfloat16, 4)
     _need(v, "v", torch.bfloat16, 4)
     B, Nq, Hq, d = q.shape
     _, Nk, Hkv, _ = k.shape
-    if tuple(v.shape) != tuple(k.shape) or k.shape[0] != B or k.shape[3] != d:
-        raise ValueError("k and v must be [B, Nk, Hkv, d] matching q")
+    dv = v.shape[3]
+    if tuple(v.shape[:3]) != tuple(k.shape[:3]) or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("k must be [B, Nk, Hkv, d] matching q and v [B, Nk, Hkv, dv]")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    o = out if out is not None else torch.empty_like(q)
+    o = out if out is not None else torch.empty((B, Nq, Hq, dv), dtype=q.dtype, device=q.device)
     if want_lse and lse is None:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
-    st = lib().ea_attn_fwd_tuned(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Nq, Nk, Hq, Hkv, d,
-                                 int(bool(causal)), float(scale),
-                                 ctypes.byref(tuning) if tuning is not None else None, _stream(q))
+    st = lib().ea_attn_fwd_hd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Nq, Nk, Hq, Hkv, d, dv,
+                              int(bool(causal)), float(scale),
+                              ctypes.byref(tuning) if tuning is not None else None, _stream(q))
     _check(st, "ea_attn_fwd")
     return o, lse
 

@@ -47,8 +47,14 @@ ea_status check_tuning(const ea_fwd_tuning* t) {
 
 // The 8-wave kernels cover 256-row blocks, the 4-wave kernel 128-row blocks;
 // a.n_mb arrives counted in 128-row blocks.
-hipError_t dispatch_fwd(ea::FwdArgs a, int d, bool causal, bool varlen, const ea_fwd_tuning& tt,
+// d / dv: head dims of Q, K and of V, O; d != dv (192 / 128) runs the
+// ping-pong kernel only (checked by the callers).
+hipError_t dispatch_fwd(ea::FwdArgs a, int d, int dv, bool causal, bool varlen, const ea_fwd_tuning& tt,
                         hipStream_t s) {
+  if (d != dv) {
+    a.n_mb = (a.n_mb + 1) / 2;
+    return ea::launch_fwd_pp(a, d, dv, causal, varlen, tt.exp_mode, s);
+  }
   if (tt.kernel == EA_FWD_KERNEL_PIPELINED) {
     a.n_mb = (a.n_mb + 1) / 2;
     return ea::launch_fwd_sp(a, d, causal, varlen, tt.exp_mode, s);
@@ -56,7 +62,7 @@ hipError_t dispatch_fwd(ea::FwdArgs a, int d, bool causal, bool varlen, const ea
   const bool pp = tt.kernel == EA_FWD_KERNEL_PINGPONG || (tt.kernel == EA_FWD_KERNEL_AUTO && d == 128);
   if (pp) {
     a.n_mb = (a.n_mb + 1) / 2;
-    return ea::launch_fwd_pp(a, d, causal, varlen, tt.exp_mode, s);
+    return ea::launch_fwd_pp(a, d, d, causal, varlen, tt.exp_mode, s);
   }
   return ea::launch_fwd(a, d, causal, varlen, tt.exp_mode, s);
 }
@@ -77,17 +83,22 @@ void ea_fwd_tuning_default(ea_fwd_tuning* t) {
   t->kernel = EA_FWD_KERNEL_AUTO;
 }
 
-ea_status ea_attn_fwd_tuned(const void* q, const void* k, const void* v, void* o, float* lse,
-                            int B, int Nq, int Nk, int Hq, int Hkv, int d, int causal,
-                            float scale, const ea_fwd_tuning* tuning, void* stream) {
+ea_status ea_attn_fwd_hd(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int Nq, int Nk, int Hq, int Hkv, int d_qk, int d_v, int causal,
+                         float scale, const ea_fwd_tuning* tuning, void* stream) {
+  const int d = d_qk;
   if (!q || !k || !v || !o) return fail(EA_ERR_INVALID, "q, k, v and o must be non-null");
-  if (B <= 0 || Nq <= 0 || Nk <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0)
-    return fail(EA_ERR_INVALID, "B, Nq, Nk, Hq, Hkv and d must be positive");
+  if (B <= 0 || Nq <= 0 || Nk <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || d_v <= 0)
+    return fail(EA_ERR_INVALID, "B, Nq, Nk, Hq, Hkv and the head dims must be positive");
   if (Hq % Hkv) return fail(EA_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
-  if (d != 64 && d != 128) return fail(EA_ERR_UNSUPPORTED, "head dim %d not supported (64 or 128)", d);
+  if (!((d == 64 && d_v == 64) || (d == 128 && d_v == 128) || (d == 192 && d_v == 128)))
+    return fail(EA_ERR_UNSUPPORTED, "head dims (%d, %d) not supported: (64, 64), (128, 128) or (192, 128)", d, d_v);
   if (!finite_pos(scale)) return fail(EA_ERR_INVALID, "scale must be finite and positive");
   if (causal != 0 && causal != 1) return fail(EA_ERR_INVALID, "causal must be 0 or 1");
   if (ea_status st = check_tuning(tuning); st != EA_OK) return st;
+  if (d != d_v && tuning != nullptr && tuning->kernel != EA_FWD_KERNEL_AUTO &&
+      tuning->kernel != EA_FWD_KERNEL_PINGPONG)
+    return fail(EA_ERR_UNSUPPORTED, "head dims (%d, %d) run on the ping-pong kernel only", d, d_v);
   if ((long long)B * Nq >= (1LL << 31) || (long long)B * Nk >= (1LL << 31))
     return fail(EA_ERR_UNSUPPORTED, "B * N must be below 2^31");
   const int n_mb = (Nq + ea::kFwdBlockM - 1) / ea::kFwdBlockM;
@@ -114,8 +125,15 @@ ea_status ea_attn_fwd_tuned(const void* q, const void* k, const void* v, void* o
   a.scale_log2 = scale * 1.4426950408889634f;
   a.tau = tt.rescale_log2;
   a.natural = tt.natural_order;
-  return hip_status(dispatch_fwd(a, d, causal != 0, false, tt, (hipStream_t)stream),
+  return hip_status(dispatch_fwd(a, d, d_v, causal != 0, false, tt, (hipStream_t)stream),
                     "attention forward launch");
+}
+
+ea_status ea_attn_fwd_tuned(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int Nq, int Nk, int Hq, int Hkv, int d, int causal,
+                            float scale, const ea_fwd_tuning* tuning, void* stream) {
+  if (d > 0 && d != 64 && d != 128) return fail(EA_ERR_UNSUPPORTED, "head dim %d not supported (64 or 128)", d);
+  return ea_attn_fwd_hd(q, k, v, o, lse, B, Nq, Nk, Hq, Hkv, d, d, causal, scale, tuning, stream);
 }
 
 ea_status ea_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
@@ -167,7 +185,7 @@ ea_status ea_attn_fwd_varlen_ordered(const void* q, const void* k, const void* v
   a.tau = tt.rescale_log2;
   a.natural = tt.natural_order;
   a.seq_order = seq_order;
-  return hip_status(dispatch_fwd(a, d, causal != 0, true, tt, (hipStream_t)stream),
+  return hip_status(dispatch_fwd(a, d, d, causal != 0, true, tt, (hipStream_t)stream),
                     "varlen attention forward launch");
 }
 

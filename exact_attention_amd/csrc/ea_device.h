@@ -117,10 +117,15 @@ __device__ __forceinline__ float add_bf16x2(uint32_t packed, float acc) {
 //      position, the chunk bits 0-1.
 // swz depends on row % 16 only, so moving 16 rows (or 32) is a constant
 // address offset. D = 64 rows have 8 chunks: swz(row) = ((row & 3) << 1) |
-// ((row >> 2) & 1).
+// ((row >> 2) & 1). D = 192 rows (384 bytes, 24 chunks) span one and a half
+// 256-byte bank lines, so a row's parity already picks the bank half of a
+// chunk; swz(row) = (row >> 1) & 7 permutes the chunk within its aligned
+// group of 8 (it stays inside the row) and gives the 8 rows of each parity
+// distinct bank groups: 16 consecutive rows at one chunk hit all 16 groups.
 // ---------------------------------------------------------------------------
 template <int D>
 __device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 192) return (row >> 1) & 7;
   if constexpr (D >= 128) return ((row & 3) << 2) | ((row >> 2) & 3);
   return ((row & 3) << 1) | ((row >> 2) & 1);
 }

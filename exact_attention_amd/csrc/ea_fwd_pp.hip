@@ -35,23 +35,31 @@
 //    register copy per stage and offset.
 //  * Operand layouts (S^T = K Q^T, P^T passed in registers to O^T = V^T P^T,
 //    V^T from ds_read_b64_tr_b16) are those of the 4-wave kernel.
+#include <type_traits>
+
 #include "ea_device.h"
 #include "ea_fwd_common.h"
 #include "ea_internal.h"
 
 namespace ea {
 
-template <int D, bool CAUSAL, bool VARLEN, int EXPMODE>
+// D: head dim of Q and K; DV: head dim of V and O (equal, or 192 / 128).
+template <int D, int DV, bool CAUSAL, bool VARLEN, int EXPMODE>
 __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   constexpr int BM = kPpBlockM, BN = kFwdBlockN;
-  constexpr int TILE = BN * D;               // bf16 elements per stage
-  constexpr int NDT = D / 32;                // 32-wide d tiles of O^T
-  constexpr int ROWB = D * 2;                // bytes per K/V row
-  constexpr int NI = TILE * 2 / 1024;        // 1 KB DMA instructions per tile
+  constexpr int TILE = BN * D;               // bf16 elements per K stage
+  constexpr int VTILE = BN * DV;             // ... per V stage
+  constexpr int NDT = DV / 32;               // 32-wide d tiles of O^T
+  constexpr int ROWB = D * 2;                // bytes per K row
+  constexpr int VROWB = DV * 2;              // bytes per V row
+  constexpr int NI = TILE * 2 / 1024;        // 1 KB DMA instructions per K tile
   constexpr int IPW = NI / 4;                // ... per wave of group A
-  static_assert(IPW >= 1 && NI % 4 == 0, "tile must split into 4 waves of 1 KB DMA");
+  constexpr int NIV = VTILE * 2 / 1024;      // ... per V tile
+  constexpr int IPWV = NIV / 4;
+  static_assert(IPW >= 1 && NI % 4 == 0 && IPWV >= 1 && NIV % 4 == 0,
+                "tiles must split into 4 waves of 1 KB DMA");
   __shared__ __attribute__((aligned(1024))) uint16_t ks0[TILE], ks1[TILE], ks2[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t vs0[TILE], vs1[TILE], vs2[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t vs0[VTILE], vs1[VTILE], vs2[VTILE];
 
   // ---------------- tile assignment (XCD-grouped, heaviest first)
   const int xcd = blockIdx.x & 7;
@@ -118,6 +126,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   const int wrow = row_lo + 64 * (w & 3) + 32 * grp;    // wave's first query row
   const int qi = wrow + c;                              // this lane's query row
   const size_t qstride = (size_t)a.Hq * D, kstride = (size_t)a.Hkv * D;
+  const size_t ostride = (size_t)a.Hq * DV, vstride = (size_t)a.Hkv * DV;
 
   // ---------------- Q^T operand (B of S^T = K Q^T), kept in VGPRs
   bf16x8 qf[D / 16];
@@ -131,22 +140,34 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   // w*IPW+IPW-1 of a tile. Lane s of piece p lands at stage byte 1024 p + 16 s = row r, slot sl;
   // it fetches the global 16-byte chunk sl ^ swz(r) of row r.
   const uint16_t* kg_base = a.k + (size_t)k0 * kstride + (size_t)hk * D;
-  const uint16_t* vg_base = a.v + (size_t)k0 * kstride + (size_t)hk * D;
-  uint32_t dma_off[IPW];
+  const uint16_t* vg_base = a.v + (size_t)k0 * vstride + (size_t)hk * DV;
+  uint32_t dma_off[IPW], dma_voff[IPWV];
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
     const int p = 1024 * ((w & 3) * IPW + i) + 16 * lane;
     const int r = p / ROWB, sl = (p % ROWB) / 16;
     dma_off[i] = (uint32_t)(r * (int)kstride * 2 + ((sl ^ swz<D>(r)) << 4));
   }
-  auto dma_tile = [&](EA_LDS uint16_t* stage, const uint16_t* gbase, int t) __attribute__((always_inline)) {
-    const int rows = t < nkb ? min(lk - t * BN, BN) : 0;  // tiles past the causal bound are not fetched
-    const uint32_t nrec = rows > 0 ? (uint32_t)((rows - 1) * (int)kstride * 2 + D * 2) : 0u;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(gbase + (size_t)(rows > 0 ? t : 0) * BN * kstride, nrec);
 #pragma unroll
-    for (int i = 0; i < IPW; ++i)
-      buffer_load16_lds(rs, (EA_LDS void*)(stage + 512 * ((w & 3) * IPW + i)), dma_off[i]);
+  for (int i = 0; i < IPWV; ++i) {
+    const int p = 1024 * ((w & 3) * IPWV + i) + 16 * lane;
+    const int r = p / VROWB, sl = (p % VROWB) / 16;
+    dma_voff[i] = (uint32_t)(r * (int)vstride * 2 + ((sl ^ swz<DV>(r)) << 4));
+  }
+  // one K (V_TILE = false) or V tile into a stage; rows past the sequence land as zeros
+  auto dma_tile = [&](EA_LDS uint16_t* stage, const uint16_t* gbase, int t, auto v_tile) __attribute__((always_inline)) {
+    constexpr bool V = decltype(v_tile)::value;
+    constexpr int DD = V ? DV : D, NP = V ? IPWV : IPW;
+    const size_t stride = V ? vstride : kstride;
+    const int rows = t < nkb ? min(lk - t * BN, BN) : 0;  // tiles past the causal bound are not fetched
+    const uint32_t nrec = rows > 0 ? (uint32_t)((rows - 1) * (int)stride * 2 + DD * 2) : 0u;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(gbase + (size_t)(rows > 0 ? t : 0) * BN * stride, nrec);
+#pragma unroll
+    for (int i = 0; i < NP; ++i)
+      buffer_load16_lds(rs, (EA_LDS void*)(stage + 512 * ((w & 3) * NP + i)), V ? dma_voff[i] : dma_off[i]);
   };
+  using KTILE = std::integral_constant<bool, false>;
+  using VTILE_ = std::integral_constant<bool, true>;
   // stage r is a constant wherever these are inlined, so every access names
   // one LDS object
   auto kstage = [&](int r) __attribute__((always_inline)) -> EA_LDS uint16_t* {
@@ -166,8 +187,8 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   int v_off[NDT][2];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {
-    v_off[dt][0] = tile_off<D>(tr_row, 32 * dt + tr_col);
-    v_off[dt][1] = tile_off<D>(tr_row + 8, 32 * dt + tr_col);
+    v_off[dt][0] = tile_off<DV>(tr_row, 32 * dt + tr_col);
+    v_off[dt][1] = tile_off<DV>(tr_row + 8, 32 * dt + tr_col);
   }
   const int wave_last_q = wrow + 31;
   const int wave_first_q = wrow;
@@ -219,8 +240,8 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     for (int st = 0; st < 4; ++st) {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const i16x4 lo = ds_read_tr16(vs + vo[dt][0] + 16 * st * D);
-        const i16x4 hi = ds_read_tr16(vs + vo[dt][1] + 16 * st * D);
+        const i16x4 lo = ds_read_tr16(vs + vo[dt][0] + 16 * st * DV);
+        const i16x4 hi = ds_read_tr16(vs + vo[dt][1] + 16 * st * DV);
         const i32x4 t = {__builtin_bit_cast(i32x2, lo)[0], __builtin_bit_cast(i32x2, lo)[1],
                          __builtin_bit_cast(i32x2, hi)[0], __builtin_bit_cast(i32x2, hi)[1]};
         oacc[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, t), pb[st], oacc[dt]);
@@ -311,26 +332,26 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     mfma_part(r);
     pp_barrier();
     if (grp == 0) {
-      dma_tile(kstage((r + 2) % 3), kg_base, s + 2);
-      dma_tile(vstage((r + 1) % 3), vg_base, s + 1);
+      dma_tile(kstage((r + 2) % 3), kg_base, s + 2, KTILE{});
+      dma_tile(vstage((r + 1) % 3), vg_base, s + 1, VTILE_{});
     }
     valu_part(s, act);
-    if (grp == 0) wait_vmcnt<2 * IPW>();
+    if (grp == 0) wait_vmcnt<IPW + IPWV>();
     pp_barrier();
   };
 
   // prologue: K_0, K_1 and V_0 (read in steps 0 and 1); the V stage that
   // step 0 multiplies by P = 0 is zeroed so it holds no stale NaN
   {
-    static_assert(TILE % (8 * 512) == 0, "stage zeroing covers the tile");
+    static_assert(VTILE % (8 * 512) == 0, "stage zeroing covers the tile");
 #pragma unroll
-    for (int i = 0; i < TILE / (8 * 512); ++i)
+    for (int i = 0; i < VTILE / (8 * 512); ++i)
       lds_store<i32x4>((EA_LDS uint16_t*)vs2 + 8 * (tid + 512 * i), i32x4{});
   }
   if (grp == 0) {
-    dma_tile(kstage(0), kg_base, 0);
-    dma_tile(kstage(1), kg_base, 1);
-    dma_tile(vstage(0), vg_base, 0);
+    dma_tile(kstage(0), kg_base, 0, KTILE{});
+    dma_tile(kstage(1), kg_base, 1, KTILE{});
+    dma_tile(vstage(0), vg_base, 0, VTILE_{});
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -349,7 +370,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   const float l_tot = sum_with_partner32(l_run);
   const float inv = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
   if (qi < lq) {
-    uint16_t* op = a.o + (size_t)(q0 + qi) * qstride + (size_t)h * D;
+    uint16_t* op = a.o + (size_t)(q0 + qi) * ostride + (size_t)h * DV;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
@@ -374,32 +395,34 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   }
 }
 
-template <int D, bool CAUSAL, bool VARLEN, int EXPMODE>
+template <int D, int DV, bool CAUSAL, bool VARLEN, int EXPMODE>
 static hipError_t launch_pp_t(const FwdArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((fwd_pp_kernel<D, CAUSAL, VARLEN, EXPMODE>), dim3(fwd_grid(a, VARLEN)), dim3(512), 0, s, a);
+  hipLaunchKernelGGL((fwd_pp_kernel<D, DV, CAUSAL, VARLEN, EXPMODE>), dim3(fwd_grid(a, VARLEN)), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, int DV, bool CAUSAL, bool VARLEN>
 static hipError_t launch_pp_e(const FwdArgs& a, int exp_mode, hipStream_t s) {
   switch (exp_mode) {
-    case 1: return launch_pp_t<D, CAUSAL, VARLEN, 1>(a, s);
-    case 2: return launch_pp_t<D, CAUSAL, VARLEN, 2>(a, s);
-    default: return launch_pp_t<D, CAUSAL, VARLEN, 0>(a, s);
+    case 1: return launch_pp_t<D, DV, CAUSAL, VARLEN, 1>(a, s);
+    case 2: return launch_pp_t<D, DV, CAUSAL, VARLEN, 2>(a, s);
+    default: return launch_pp_t<D, DV, CAUSAL, VARLEN, 0>(a, s);
   }
 }
 
-template <int D>
+template <int D, int DV>
 static hipError_t launch_pp_d(const FwdArgs& a, bool causal, bool varlen, int exp_mode, hipStream_t s) {
   if (causal) {
-    return varlen ? launch_pp_e<D, true, true>(a, exp_mode, s) : launch_pp_e<D, true, false>(a, exp_mode, s);
+    return varlen ? launch_pp_e<D, DV, true, true>(a, exp_mode, s) : launch_pp_e<D, DV, true, false>(a, exp_mode, s);
   }
-  return varlen ? launch_pp_e<D, false, true>(a, exp_mode, s) : launch_pp_e<D, false, false>(a, exp_mode, s);
+  return varlen ? launch_pp_e<D, DV, false, true>(a, exp_mode, s) : launch_pp_e<D, DV, false, false>(a, exp_mode, s);
 }
 
-hipError_t launch_fwd_pp(const FwdArgs& a, int d, bool causal, bool varlen, int exp_mode, hipStream_t s) {
-  if (d == 64) return launch_pp_d<64>(a, causal, varlen, exp_mode, s);
-  return launch_pp_d<128>(a, causal, varlen, exp_mode, s);
+hipError_t launch_fwd_pp(const FwdArgs& a, int d, int dv, bool causal, bool varlen, int exp_mode, hipStream_t s) {
+  if (d == 64 && dv == 64) return launch_pp_d<64, 64>(a, causal, varlen, exp_mode, s);
+  if (d == 192 && dv == 128) return launch_pp_d<192, 128>(a, causal, varlen, exp_mode, s);
+  if (d == 128 && dv == 128) return launch_pp_d<128, 128>(a, causal, varlen, exp_mode, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace ea

@@ -34,7 +34,8 @@ int fwd_grid(const FwdArgs& a, bool varlen);
 hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, bool varlen, int exp_mode,
                       hipStream_t s);
 // 8-wave ping-pong forward; a.n_mb counts kPpBlockM-row blocks
-hipError_t launch_fwd_pp(const FwdArgs& a, int d, bool causal, bool varlen, int exp_mode,
+// d: head dim of Q and K, dv: of V and O ((64, 64), (128, 128) or (192, 128))
+hipError_t launch_fwd_pp(const FwdArgs& a, int d, int dv, bool causal, bool varlen, int exp_mode,
                          hipStream_t s);
 // 8-wave software-pipelined forward; a.n_mb counts kPpBlockM-row blocks
 hipError_t launch_fwd_sp(const FwdArgs& a, int d, bool causal, bool varlen, int exp_mode,

@@ -111,6 +111,19 @@ ea_status ea_attn_fwd_tuned(const void* q, const void* k, const void* v, void* o
                             float scale, const ea_fwd_tuning* tuning, void* stream);
 
 /*
+ * ea_attn_fwd_hd -- ea_attn_fwd_tuned with separate head dims for the scores
+ * and the values: q [B, Nq, Hq, d_qk], k [B, Nk, Hkv, d_qk], v [B, Nk, Hkv,
+ * d_v], o [B, Nq, Hq, d_v]. (d_qk, d_v) is (64, 64), (128, 128) or (192, 128),
+ * the last being the non-standard pair "FlashAttention-4: algorithm-pipeline
+ * co-design for Blackwell" (kernel-level performance section) benchmarks for
+ * the DeepSeek V3 architecture; other pairs return EA_ERR_UNSUPPORTED.
+ * (192, 128) runs on the ping-pong kernel only (tuning->kernel AUTO or
+ * PINGPONG). The usual scale is 1/sqrt(d_qk).
+ */
+ea_status ea_attn_fwd_hd(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int Nq, int Nk, int Hq, int Hkv, int d_qk, int d_v, int causal,
+                         float scale, const ea_fwd_tuning* tuning, void* stream);
+/*
  * ea_attn_fwd_varlen -- packed variable-length sequences (THD layout).
  *   q [total_q, Hq, d], k/v [total_k, Hkv, d], o [total_q, Hq, d] bf16
  *   lse [Hq, total_q] fp32 or NULL

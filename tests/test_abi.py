@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("ea_attn_fwd", "ea_attn_fwd_varlen", "ea_attn_fwd_varlen_ordered", "ea_varlen_lpt_order",
+    for n in ("ea_attn_fwd", "ea_attn_fwd_hd", "ea_attn_fwd_varlen", "ea_attn_fwd_varlen_ordered", "ea_varlen_lpt_order",
               "ea_attn_fwd_mx8", "ea_attn_fwd_mx8_tuned", "ea_attn_fwd_mx8_fmt", "ea_attn_decode_paged",
               "ea_decode_workspace_size", "ea_last_error"):
         assert n in names
@@ -57,6 +57,19 @@ def test_fwd_argument_errors(lib):
     assert f(P, P, P, P, None, 1, 8, 8, 2, 2, 128, 0, float("nan"), None) == -1
     assert f(P, P, P, P, None, 1, 8, 8, 2, 2, 128, 0, -1.0, None) == -1
     assert f(P, P, P, P, None, 1, 8, 8, 2, 2, 128, 2, 0.1, None) == -1
+
+
+def test_fwd_head_dim_pair_errors(lib):
+    import exact_attention_amd as ea
+    g = lib.ea_attn_fwd_hd
+    assert g(P, P, P, P, None, 1, 8, 8, 2, 2, 192, 64, 0, 0.1, None, None) == -2 and "(192, 64)" in _err(lib)
+    assert g(P, P, P, P, None, 1, 8, 8, 2, 2, 128, 64, 0, 0.1, None, None) == -2
+    assert g(P, P, P, P, None, 1, 8, 8, 2, 2, 192, 0, 0, 0.1, None, None) == -1
+    assert g(None, P, P, P, None, 1, 8, 8, 2, 2, 192, 128, 0, 0.1, None, None) == -1
+    for kern in (1, 3):                                   # (192, 128): ping-pong kernel only
+        t = ea.tuning(kernel=kern)
+        assert g(P, P, P, P, None, 1, 8, 8, 2, 2, 192, 128, 0, 0.1, ctypes.byref(t), None) == -2
+    assert lib.ea_attn_fwd(P, P, P, P, None, 1, 8, 8, 2, 2, 192, 0, 0.1, None) == -2   # needs the _hd entry
 
 
 def test_tuning_errors(lib):

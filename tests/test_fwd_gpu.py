@@ -207,3 +207,47 @@ def test_eager_rescale_matches():
     e0, _ = check_full(inp, tuning=ea.tuning(rescale_log2=0.0))
     e8, _ = check_full(inp, tuning=ea.tuning(rescale_log2=8.0))
     log(f"  eager max|do|={e0:.2e} lazy max|do|={e8:.2e}")
+
+
+# ---------------------------------------------------------------- head dims (d_qk, d_v) = (192, 128)
+
+HD_SHAPES = [
+    # B, Nq, Nk, Hq, Hkv, causal
+    (2, 300, 300, 4, 2, True),           # ragged tail, GQA 2:1
+    (1, 256, 256, 2, 2, False),
+    (1, 129, 257, 2, 1, True),           # Nq < Nk, bottom-right causal
+    (1, 1, 1, 1, 1, True),
+    (1, 200, 50, 2, 2, True),            # Nq > Nk: leading rows have no key
+    (2, 640, 640, 3, 3, True),           # several row blocks
+]
+
+
+@pytest.mark.parametrize("shape", HD_SHAPES)
+def test_head_dims_192_128(shape):
+    """Scores over d_qk = 192, values and output of d_v = 128 (the pair the
+    pages benchmark for DeepSeek V3), on the ping-pong kernel."""
+    B, Nq, Nk, Hq, Hkv, causal = shape
+    log(f"fwd (192,128) shape {shape}")
+    inp = W.dense(B, Nq, Nk, Hq, Hkv, 192, causal, seed=177 + Nq + Nk, dv=128)
+    assert inp.v.shape[3] == 128 and abs(inp.scale - 1 / np.sqrt(192)) < 1e-12
+    e, el = check_full(inp)
+    log(f"  max|do|={e:.2e} max|dlse|={el:.2e}")
+
+
+def test_head_dims_192_128_prefill_sampled():
+    """(192, 128) at the prefill workload's size (B=4, H=16, N=8192, causal),
+    sampled rows; determinism and tile-order invariance."""
+    import exact_attention_amd as ea
+    inp = W.dense(4, 8192, 8192, 16, 16, 192, True, seed=1192, dv=128)
+    log(f"fwd (192,128) prefill shape q={inp.q.shape} v={inp.v.shape}")
+    o, lse = run_dense(inp)
+    B, N, H, _ = inp.q.shape
+    rng = np.random.default_rng(15)
+    rows = _sample_rows(N, rng, n=12)
+    for (b, h) in [(0, 0), (3, 15), (2, 5)]:
+        ro, rl = _rows(inp, b, h, rows)
+        assert_o_close(o[b, rows, h, :], ro, what=f"o[b={b},h={h}]")
+        assert_lse_close(lse[b, h, rows], rl, what=f"lse[b={b},h={h}]")
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    o2, l2 = run_dense(inp, tuning=ea.tuning(natural_order=1))
+    assert np.array_equal(o, o2) and np.array_equal(lse, l2)

@@ -105,6 +105,22 @@ def test_brute_force_small(causal, shape):
     np.testing.assert_allclose(lse, lb, rtol=1e-13, atol=1e-13)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_brute_force_value_dim_differs(causal):
+    """Scores over d_qk = 6, values of d_v = 4 (the (192, 128) head-dim pair in
+    miniature); GQA 2:1."""
+    q = _rand((1, 9, 2, 6), 21) * 2
+    k = _rand((1, 9, 1, 6), 22) * 2
+    v = _rand((1, 9, 1, 4), 23)
+    o, lse = oracle.attention(q, k, v, causal, 1 / np.sqrt(6), threads=2, row_block=4)
+    assert o.shape == (1, 9, 2, 4)
+    ob, lb = _brute(q, k, v, causal, 1 / np.sqrt(6))
+    np.testing.assert_allclose(o, ob, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, lb, rtol=1e-13, atol=1e-13)
+    ro, rl = oracle.attention_rows(q[:, :, 1:2], k, v, 0, 0, [0, 4, 8], causal, 1 / np.sqrt(6))
+    np.testing.assert_allclose(ro, ob[0, [0, 4, 8], 1], rtol=1e-12, atol=1e-13)
+
+
 def test_brute_force_rectangular_causal():
     # Nq != Nk: bottom-right aligned causal bound (a reading; unexercised by the workloads)
     q = _rand((1, 3, 2, 4), 4); k = _rand((1, 9, 2, 4), 5); v = _rand((1, 9, 2, 4), 6)

@@ -240,10 +240,11 @@ class Dense:
 
 
 def dense(B: int, Nq: int, Nk: int, Hq: int, Hkv: int, d: int, causal: bool,
-          seed: int, scale: float | None = None) -> Dense:
+          seed: int, scale: float | None = None, dv: int | None = None) -> Dense:
+    """Dense BSHD bf16 inputs; v has head dim ``dv`` (default d)."""
     q = normal_bf16_bits(seed, STREAM_Q, (B, Nq, Hq, d))
     k = normal_bf16_bits(seed, STREAM_K, (B, Nk, Hkv, d))
-    v = normal_bf16_bits(seed, STREAM_V, (B, Nk, Hkv, d))
+    v = normal_bf16_bits(seed, STREAM_V, (B, Nk, Hkv, dv or d))
     return Dense(q, k, v, causal, float(scale if scale is not None else 1.0 / np.sqrt(d)))
 
 
