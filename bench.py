@@ -114,6 +114,28 @@ def gemm_rate(torch, dev, dtype_name, n, reps=10):
         return None
 
 
+def mfma_loop_rate(torch, ea, dev, reps=5):
+    """TFLOP/s of the library's calibration loop (ea_test_mfma_loop: bf16
+    32x32x16 MFMAs from registers, 8 waves per workgroup, 1024 workgroups),
+    median of reps launches, or None."""
+    blocks, iters = 1024, 4000
+    out = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
+    s = torch.cuda.current_stream(dev)
+    ts = []
+    for i in range(reps + 1):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        if ea.lib().ea_test_mfma_loop(ea._ptr(out), blocks, iters, s.cuda_stream) != 0:
+            return None
+        e1.record(s)
+        torch.cuda.synchronize()
+        if i:
+            ts.append(e0.elapsed_time(e1))
+    flops = blocks * 8.0 * iters * 16 * 32768
+    return flops / (float(np.median(ts)) * 1e-3) / 1e12
+
+
 def prefill_flops(B, H, N, d, dv=None):
     """Causal forward FLOPs, counted as half of the full N x N work:
     2 N^2 d (scores) + 2 N^2 dv (P V) per (batch, head), halved."""
@@ -321,6 +343,11 @@ def main():
                 out[key]["sustained"] = {
                     "what": f"vendor BLAS {dt_name} GEMM {n}^3 on this GPU", "unit": "TFLOP/s",
                     "value": r, "frac": (out[key]["achieved"] / r) if r else None}
+        if "roofline" in out:
+            r = mfma_loop_rate(torch, ea, dev)
+            out["roofline"]["mfma_loop"] = {
+                "what": "register-operand bf16 MFMA loop on all CUs (ea_test_mfma_loop), this GPU",
+                "unit": "TFLOP/s", "value": r, "frac": (out["roofline"]["achieved"] / r) if r else None}
     props = torch.cuda.get_device_properties(dev)
     cfg["device"] = props.name
     cfg["cus"] = props.multi_processor_count

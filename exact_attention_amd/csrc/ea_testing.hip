@@ -11,7 +11,41 @@ __global__ void exp2_kernel(const float* x, float* y, int n, int mode) {
   y[i] = (mode == EA_EXP_POLY) ? ea::exp2_poly(x[i]) : ea::exp2_hw(x[i]);
 }
 
+// A calibration loop: each wave issues iters x 16 v_mfma_f32_32x32x16_bf16
+// into four independent accumulators from register operands (no memory
+// traffic), so the launch measures the rate the matrix cores sustain on this
+// device under full load. Each lane writes one sum so nothing is eliminated.
+__global__ __launch_bounds__(512) void mfma_loop_kernel(float* out, int iters) {
+  const int lane = threadIdx.x & 63;
+  ea::bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(1e-3f * (float)(lane + i));
+    b[i] = (__bf16)(1e-3f * (float)(lane - i));
+  }
+  ea::f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      c0 = ea::mfma32x32x16(a, b, c0);
+      c1 = ea::mfma32x32x16(a, b, c1);
+      c2 = ea::mfma32x32x16(a, b, c2);
+      c3 = ea::mfma32x32x16(a, b, c3);
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
 }  // namespace
+
+extern "C" ea_status ea_test_mfma_loop(float* out, int blocks, int iters, void* stream) {
+  if (out == nullptr || blocks <= 0 || iters <= 0 || blocks > 65536) return EA_ERR_INVALID;
+  hipLaunchKernelGGL(mfma_loop_kernel, dim3(blocks), dim3(512), 0, (hipStream_t)stream, out, iters);
+  return hipGetLastError() == hipSuccess ? EA_OK : EA_ERR_HIP;
+}
 
 extern "C" ea_status ea_test_exp2(const float* x, float* y, int n, int mode, void* stream) {
   if (n < 0 || (n > 0 && (x == nullptr || y == nullptr))) return EA_ERR_INVALID;

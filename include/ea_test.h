@@ -23,6 +23,17 @@ extern "C" {
  */
 ea_status ea_test_exp2(const float* x, float* y, int n, int mode, void* stream);
 
+/*
+ * ea_test_mfma_loop -- calibration of the bf16 matrix-core rate: blocks
+ * workgroups of 8 waves each issue iters x 16 v_mfma_f32_32x32x16_bf16 (32768
+ * FLOP each) from register operands into four independent accumulators, with
+ * no memory traffic. FLOPs per launch = blocks * 8 * iters * 16 * 32768.
+ *   out: device float array of blocks * 512 elements (written, one value per
+ *   lane, meaningless beyond keeping the work alive). 0 < blocks <= 65536,
+ *   iters > 0; otherwise EA_ERR_INVALID.
+ */
+ea_status ea_test_mfma_loop(float* out, int blocks, int iters, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

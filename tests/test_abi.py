@@ -140,6 +140,13 @@ def test_decode_argument_errors(lib):
     assert lib.ea_decode_workspace_size(4, 8, 2, 128, 1024, 16, 8) >= lib.ea_decode_workspace_size(4, 8, 2, 128, 1024, 16, 1)
 
 
+def test_mfma_loop_argument_errors(lib):
+    assert lib.ea_test_mfma_loop(None, 4, 10, None) == -1
+    assert lib.ea_test_mfma_loop(P, 0, 10, None) == -1
+    assert lib.ea_test_mfma_loop(P, 4, 0, None) == -1
+    assert lib.ea_test_mfma_loop(P, 1 << 17, 10, None) == -1
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     import exact_attention_amd as ea

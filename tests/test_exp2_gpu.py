@@ -46,3 +46,12 @@ def test_exp2_accuracy(mode):
         # clamp: far below -127 gives (almost) zero
         z = ea.test_exp2(torch.tensor([-200.0, -1e30, float("-inf")], device="cuda"), mode).cpu().numpy()
         assert np.all(np.abs(z) <= 2.0 ** -126)
+
+
+def test_mfma_loop_calibration_runs():
+    """The calibration loop used by bench.py launches and writes every lane."""
+    import exact_attention_amd as ea
+    out = torch.full((8 * 512,), float("nan"), dtype=torch.float32, device="cuda")
+    assert ea.lib().ea_test_mfma_loop(ea._ptr(out), 8, 10, None) == 0
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
