@@ -43,9 +43,9 @@ PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 # HBM bytes per launch measured by rocprofv3 (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0,
 # the factors a plain 1 GiB copy reads); None until measured for the current
 # kernels. Sources: profiles/*_counters.md.
-TRAFFIC_PREFILL = 582_522_880    # fwd_pp_kernel<128, causal>: 217,698 KiB fetched, 133,474 KiB written
-TRAFFIC_DECODE = 4_866_152_448   # decode_split_kernel<4> + combine: 2,373,145 KiB fetched, 5,812 KiB written
-TRAFFIC_FP8 = 491_217_920        # fwd_mx8_sp_kernel<causal>: 173,215 KiB fetched, 133,275 KiB written
+TRAFFIC_PREFILL = 618_255_360    # fwd_pp_kernel<128, 128, causal>: 234,836 KiB fetched, 134,093 KiB written
+TRAFFIC_DECODE = 4_866_191_360   # decode_split_kernel<true> + combine: 2,373,166 KiB fetched, 5,807 KiB written
+TRAFFIC_FP8 = 492_166_827        # fwd_mx8_sp_kernel<causal, e4m3>: 173,648 KiB fetched, 133,336 KiB written
 
 
 def parse():
@@ -309,8 +309,10 @@ def main():
         out["prefill"] = {"ms_mean": float(t_pf.mean()), "ms_min": float(t_pf.min()), "ms_median": float(np.median(t_pf)),
                           "tflops_best": flops / (t_pf.min() * 1e-3) / 1e12, "flop_per_launch": flops}
         out["roofline"] = {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                           "frac": tf / PEAK_BF16_TFLOPS, "traffic": TRAFFIC_PREFILL,
-                           "kernel": "ea::fwd_pp_kernel<128, causal>"}
+                           "frac": tf / PEAK_BF16_TFLOPS,
+                           "traffic": TRAFFIC_PREFILL if d_v == d == 128 else None,
+                           "kernel": "ea::fwd_pp_kernel<128, 128, causal>" if d_v == d else
+                                     f"ea::fwd_pp_kernel<{d}, {d_v}, causal>"}
     if run_decode:
         t_dc = np.array([e[2].elapsed_time(e[3]) for e in evs])
         nbytes = decode_bytes(pg.seq_lens, Hq, Hkv, dd, pg.page_size)
@@ -318,7 +320,8 @@ def main():
         out["decode"] = {"value": gbs, "unit": "GB/s", "ms_mean": float(t_dc.mean()), "ms_min": float(t_dc.min()),
                          "bytes_per_launch": nbytes, "gbs_best": nbytes / (t_dc.min() * 1e-3) / 1e9}
         out["roofline_decode"] = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                  "frac": gbs / PEAK_HBM_GBS, "traffic": TRAFFIC_DECODE,
+                                  "frac": gbs / PEAK_HBM_GBS,
+                                  "traffic": TRAFFIC_DECODE if pg.page_size == 16 else None,
                                   "kernel": f"ea::decode_split_kernel<{'true' if pg.page_size % 16 == 0 else 'false'}>"
                                             " + decode_combine_kernel"}
         if not run_prefill:
