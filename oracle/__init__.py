@@ -14,7 +14,10 @@ bf16 / e4m3-rounded input bits the GPU reads:
 
 (stated as exact attention in "FlashAttention: not less compute, less data
 movement", section 01; the tiled/online method reaches the same result up to
-rounding order, section 02 there). Every function here evaluates full score
+rounding order, section 02 there), and its gradients with respect to Q, K and V
+for a given output gradient dO (``attention_backward``: the five products of
+the backward in "Low-precision FlashAttention-4: end-to-end block-scaled
+attention for Blackwell", section 2.2, evaluated on full score rows). Every function here evaluates full score
 rows with a two-pass softmax; none of them use the streaming recurrence except
 ``online_softmax_row``, which restates that recurrence so the pins can compare
 the two formulations.
@@ -38,4 +41,5 @@ from .attention import (  # noqa: F401
     decode_paged_heads,
     online_softmax_row,
     lse_combine,
+    attention_backward,
 )

@@ -13,6 +13,13 @@ Citations name the page and its section:
   [P5 §2.1] "Low-precision FlashAttention-4: end-to-end block-scaled attention
             for Blackwell", section 2.1 (MX block scales along the GEMM K dim:
             Q, K along d; V along the sequence).
+  [P5 §2.2] same page, section 2.2 (the backward: the five GEMMs S = K Q^T,
+            dP = V dO^T, dV = P^T dO, dK = dS^T Q, dQ = dS K, with P = softmax(S)
+            and dS = dsoftmax(dP, P)).
+  [P1 bwd]  "FlashAttention-4: algorithm-pipeline co-design for Blackwell",
+            backward sections (five matrix products, the softmax recomputed from
+            the saved statistics, a deterministic mode with a fixed reduction
+            order).
 """
 from __future__ import annotations
 
@@ -362,3 +369,92 @@ def lse_combine(o_parts, lse_parts):
     lse = np.where(empty, -np.inf, mx_safe + np.log(tot_safe))
     o = ((w / tot_safe)[..., None] * o_parts).sum(axis=0)
     return o, lse
+
+
+# ----------------------------------------------------------------------------
+# backward
+# ----------------------------------------------------------------------------
+
+def _bwd_rows_block(qh, kh, vh, doh, r0, r1, Nq, causal, scale):
+    """Gradients of L = sum(dO * O) from query rows [r0, r1) of one head, by the
+    definition [P5 §2.2]: with S = scale Q K^T (masked), P = softmax(S) per row,
+    dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(P * dP)) (the softmax
+    Jacobian applied to dP), dQ = scale dS K, dK = scale dS^T Q.
+    Returns (dq [rows, d], dk [Nk, d], dv [Nk, dv]) -- dk / dv are this block's
+    contributions."""
+    Nk, d = kh.shape
+    dv_dim = vh.shape[1]
+    n_last = allowed_keys(r1 - 1, Nq, Nk, causal)
+    dq = np.zeros((r1 - r0, d))
+    dk = np.zeros((Nk, d))
+    dvv = np.zeros((Nk, dv_dim))
+    if n_last == 0:
+        return dq, dk, dvv
+    s = scale * (qh[r0:r1] @ kh[:n_last].T)
+    lim = np.array([allowed_keys(i, Nq, Nk, causal) for i in range(r0, r1)])
+    s[np.arange(n_last)[None, :] >= lim[:, None]] = -np.inf
+    ok = lim > 0
+    m = np.where(ok, s.max(axis=1), 0.0)
+    p = np.exp(s - m[:, None])
+    p[~ok] = 0.0
+    ell = p.sum(axis=1)
+    p[ok] /= ell[ok, None]                                   # P = softmax(S), rows with no key stay 0
+    do_blk = doh[r0:r1]
+    dvv[:n_last] = p.T @ do_blk                              # dV = P^T dO
+    dp = do_blk @ vh[:n_last].T                              # dP = dO V^T
+    ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))     # dS = dsoftmax(dP, P)
+    dq[:] = scale * (ds @ kh[:n_last])                       # dQ = scale dS K
+    dk[:n_last] = scale * (ds.T @ qh[r0:r1])                 # dK = scale dS^T Q
+    return dq, dk, dvv
+
+
+def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, causal: bool,
+                       scale: float, threads: int | None = None, row_block: int = 512, heads=None):
+    """Gradients of exact attention [P5 §2.2; P1 bwd] for dense BSHD inputs:
+    q [B,Nq,Hq,d], k [B,Nk,Hkv,d], v [B,Nk,Hkv,dv], do [B,Nq,Hq,dv] (the
+    gradient of the output). Returns (dq [B,Nq,Hq,d], dk [B,Nk,Hkv,d],
+    dv [B,Nk,Hkv,dv]) in float64. GQA: the gradients of a KV head are summed
+    over the query heads that read it. The softmax is recomputed from the
+    inputs (no saved statistics), rows with no allowed key contribute nothing.
+    ``heads`` restricts the work to a list of (b, hq) pairs (the other
+    gradients are left at zero), for spot checks of large inputs."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, Nq, Hq, d = q.shape
+    _, Nk, Hkv, _ = k.shape
+    if Hq % Hkv:
+        raise ValueError("Hq must be divisible by Hkv")
+    g = Hq // Hkv
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    pairs = [(b, h) for b in range(B) for h in range(Hq)] if heads is None else list(heads)
+    tasks = [(b, h, r0, min(Nq, r0 + row_block)) for (b, h) in pairs for r0 in range(0, Nq, row_block)]
+    res = [None] * len(tasks)
+
+    def run(t):
+        b, h, r0, r1 = tasks[t]
+        res[t] = _bwd_rows_block(q[b, :, h, :], k[b, :, h // g, :], v[b, :, h // g, :], do[b, :, h, :],
+                                 r0, r1, Nq, causal, scale)
+
+    n = threads or _pool_threads()
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            if n == 1:
+                for t in range(len(tasks)):
+                    run(t)
+            else:
+                with ThreadPoolExecutor(n) as ex:
+                    list(ex.map(run, range(len(tasks))))
+    else:  # pragma: no cover
+        for t in range(len(tasks)):
+            run(t)
+    # sums in a fixed order (task order), so the oracle is deterministic
+    for t, (b, h, r0, r1) in enumerate(tasks):
+        bq, bk, bv = res[t]
+        dq[b, r0:r1, h, :] = bq
+        dk[b, :, h // g, :] += bk
+        dv[b, :, h // g, :] += bv
+    return dq, dk, dv
