@@ -52,6 +52,8 @@ _SIGNATURES = {
                               _c_int),
     "ea_attn_fwd_mx8_fmt": ([_c_void_p] * 8 + [_c_int] * 6 + [_c_float, _c_int, ctypes.POINTER(FwdTuning), _c_void_p],
                             _c_int),
+    "ea_attn_bwd_workspace_size": ([_c_int] * 3, _c_size_t),
+    "ea_attn_bwd": ([_c_void_p] * 9 + [_c_int] * 7 + [_c_float, _c_void_p, _c_size_t, _c_void_p], _c_int),
     "ea_decode_workspace_size": ([_c_int] * 7, _c_size_t),
     "ea_attn_decode_paged": ([_c_void_p] * 7 + [_c_int] * 7 + [_c_float, _c_int, _c_void_p, _c_size_t, _c_void_p], _c_int),
     "ea_test_exp2": ([_c_void_p, _c_void_p, _c_int, _c_int, _c_void_p], _c_int),
@@ -214,6 +216,32 @@ def attn_fwd_mx8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = True, sca
                                    _stream(q8))
     _check(st, "ea_attn_fwd_mx8")
     return o, lse
+
+
+def attn_bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None, *,
+             workspace: torch.Tensor | None = None):
+    """Backward of attn_fwd. q, o, dout [B,Nq,Hq,d], k, v [B,Nk,Hkv,d] bf16;
+    lse [B,Hq,Nq] fp32 from the forward. Returns (dq, dk, dv) bf16."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _need(t, n, torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    B, Nq, Hq, d = q.shape
+    _, Nk, Hkv, _ = k.shape
+    if tuple(v.shape) != tuple(k.shape) or tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("shapes: q, o, dout [B,Nq,Hq,d]; k, v [B,Nk,Hkv,d]")
+    if tuple(lse.shape) != (B, Hq, Nq):
+        raise ValueError("lse must be [B, Hq, Nq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = int(lib().ea_attn_bwd_workspace_size(B, Hq, Nq))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    st = lib().ea_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                           B, Nq, Nk, Hq, Hkv, d, int(bool(causal)), float(scale), _ptr(workspace),
+                           workspace.numel() * workspace.element_size(), _stream(q))
+    _check(st, "ea_attn_bwd")
+    return dq, dk, dv
 
 
 def decode_workspace_size(B: int, Hq: int, Hkv: int, d: int, max_seqlen: int, page_size: int,

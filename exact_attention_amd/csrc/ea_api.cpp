@@ -282,6 +282,60 @@ ea_status ea_attn_fwd_mx8(const void* q8, const void* k8, const void* v8, const 
 }  // extern "C"
 
 // ---------------------------------------------------------------------------
+// backward
+// ---------------------------------------------------------------------------
+extern "C" {
+
+size_t ea_attn_bwd_workspace_size(int B, int Hq, int Nq) {
+  if (B <= 0 || Hq <= 0 || Nq <= 0) return 0;
+  return ea::bwd_workspace_bytes(B, Hq, Nq);
+}
+
+ea_status ea_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                      const float* lse, void* dq, void* dk, void* dv, int B, int Nq, int Nk, int Hq, int Hkv,
+                      int d, int causal, float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv)
+    return fail(EA_ERR_INVALID, "tensor pointers must be non-null");
+  if (B <= 0 || Nq <= 0 || Nk <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0)
+    return fail(EA_ERR_INVALID, "B, Nq, Nk, Hq, Hkv and d must be positive");
+  if (Hq % Hkv) return fail(EA_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if (d != 64 && d != 128) return fail(EA_ERR_UNSUPPORTED, "backward head dim %d not supported (64 or 128)", d);
+  if (!finite_pos(scale)) return fail(EA_ERR_INVALID, "scale must be finite and positive");
+  if (causal != 0 && causal != 1) return fail(EA_ERR_INVALID, "causal must be 0 or 1");
+  if ((long long)B * Nq * Hq >= (1LL << 31) || (long long)B * Nk * Hkv >= (1LL << 31))
+    return fail(EA_ERR_UNSUPPORTED, "B * N * H must be below 2^31");
+  const size_t need = ea::bwd_workspace_bytes(B, Hq, Nq);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(EA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  ea::BwdArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.o = (const uint16_t*)o;
+  a.dout = (const uint16_t*)dout;
+  a.lse = lse;
+  a.dq = (uint16_t*)dq;
+  a.dk = (uint16_t*)dk;
+  a.dv = (uint16_t*)dv;
+  a.B = B;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.group = Hq / Hkv;
+  a.n_mb = (Nq + 127) / 128;
+  a.n_kb = (Nk + 127) / 128;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.natural = 0;
+  ea::bwd_bind_workspace(a, workspace);
+  return hip_status(ea::launch_bwd(a, d, causal != 0, (hipStream_t)stream), "attention backward launch");
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
 // paged decode
 // ---------------------------------------------------------------------------
 namespace {

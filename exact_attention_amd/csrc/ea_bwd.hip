@@ -1,0 +1,496 @@
+// Exact attention backward for gfx950 (bf16 in, fp32 accumulate, bf16 out).
+//
+// Method: the gradients of the forward O = softmax(scale Q K^T) V for an output
+// gradient dO are the five products the pages list for the backward
+// ("Low-precision FlashAttention-4: end-to-end block-scaled attention for
+// Blackwell", section 2.2; "FlashAttention-4: algorithm-pipeline co-design for
+// Blackwell", backward sections): S = Q K^T, P = softmax(S) recomputed from
+// the forward's saved log-sum-exp, dP = dO V^T, dS = P (dP - D) with
+// D_i = dO_i . O_i, dV = P^T dO, dK = scale dS^T Q, dQ = scale dS K. The N x N
+// matrices S, P, dP and dS never leave registers.
+//
+// gfx950 mapping (this file's own design):
+//  * No atomics. The pages accumulate dQ over key blocks with atomic adds to a
+//    global fp32 buffer (and serialise them for the deterministic mode). At
+//    N = 8192 with 128-key blocks that is 64 read-modify-writes per dQ element.
+//    Here two kernels split the work instead, each owning its outputs:
+//      - bwd_dkdv_kernel: one workgroup per (sequence, KV head, 128 keys), 4
+//        waves x 32 keys, loops over every query tile of every query head of
+//        the KV head's group; dK and dV accumulate in registers (4 products:
+//        S, dP, dV, dK);
+//      - bwd_dq_kernel: one workgroup per (sequence, head, 128 query rows), 4
+//        waves x 32 rows, loops over the key tiles (3 products: S, dP, dQ).
+//    S and dP are computed twice (7 products instead of 5); in exchange every
+//    output is written once, in a fixed order, so the result is
+//    deterministic run to run and independent of the tile order.
+//  * bwd_prep_kernel computes D_i = dO_i . O_i and lse_i * log2(e) once per
+//    row into a caller workspace, read by both kernels.
+//  * Operand layouts follow the forward's (lane layouts in ea_device.h):
+//      dQ kernel:   S^T = K Q^T and dP^T = V dO^T (K, V from LDS, Q^T and dO^T
+//                   in VGPRs), so a lane owns one query row and its D and lse
+//                   are one register each; dQ^T += K^T dS^T with K^T read by
+//                   ds_read_b64_tr_b16 and dS^T packed straight from the
+//                   accumulator layout (the permuted-key trick of the forward);
+//      dK/dV kernel: S = Q K^T and dP = dO V^T (Q, dO from LDS, K and V held as
+//                   B operands), so a lane owns one key; dV^T += dO^T P and
+//                   dK^T += Q^T dS with dO^T and Q^T read transposed.
+//  * Tiles arrive by LDS DMA (buffer_load ... lds) into two stages, issued a
+//    tile ahead; rows past the sequence land as zeros.
+#include "ea_device.h"
+#include "ea_fwd_common.h"
+#include "ea_internal.h"
+
+namespace ea {
+
+namespace {
+constexpr int kBwdTileQ = 64;   // query rows per dK/dV step
+constexpr int kBwdTileK = 64;   // keys per dQ step
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// D_i = sum_c dO[i,c] O[i,c] and lse2_i = lse_i log2(e), for every (b, h, i):
+// 16 lanes per row, 16 bytes each (d = 128: 8 values; d = 64: lanes 8..15
+// idle). Outputs [B, Hq, Nq] fp32.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
+  const int t = blockIdx.x * 16 + (threadIdx.x >> 4);  // (b, n, h) row, BSHD order
+  const int l16 = threadIdx.x & 15;
+  const int rows = a.B * a.Nq * a.Hq;
+  float acc = 0.f;
+  if (t < rows && 8 * l16 < D) {
+    const size_t base = (size_t)t * D + 8 * l16;
+    const bf16x8 o = *(const bf16x8*)(a.o + base);
+    const bf16x8 g = *(const bf16x8*)(a.dout + base);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = __builtin_fmaf((float)o[i], (float)g[i], acc);
+  }
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) acc += __shfl_xor(acc, m);
+  if (t < rows && l16 == 0) {
+    const int h = t % a.Hq;
+    const int n = (t / a.Hq) % a.Nq;
+    const int b = t / (a.Hq * a.Nq);
+    const size_t idx = ((size_t)b * a.Hq + h) * a.Nq + n;
+    a.dd[idx] = acc;
+    a.lse2[idx] = a.lse[idx] * kLog2e;
+  }
+}
+
+// DMA of one tile of R rows x D bf16 (row stride `stride` elements in global
+// memory) into a swizzled LDS stage: wave w of NWAVES issues pieces w, w +
+// NWAVES, ... of 1 KB; lane s of piece p lands at stage byte 1024 p + 16 s =
+// (row r, slot sl) and fetches the global chunk sl ^ swz(r) of row r. Rows
+// past `rows` read as zeros (buffer range).
+template <int D, int R, int NWAVES>
+struct TileDma {
+  static constexpr int NP = R * D * 2 / 1024;  // pieces per tile
+  static constexpr int PPW = NP / NWAVES;      // pieces per wave
+  static_assert(NP % NWAVES == 0 && PPW >= 1, "tile must split evenly into 1 KB pieces");
+  uint32_t off[PPW];
+  __device__ __forceinline__ void init(int w, int lane, size_t stride) {
+#pragma unroll
+    for (int i = 0; i < PPW; ++i) {
+      const int p = 1024 * (w * PPW + i) + 16 * lane;
+      const int r = p / (D * 2), sl = (p % (D * 2)) / 16;
+      off[i] = (uint32_t)(r * (int)stride * 2 + ((sl ^ swz<D>(r)) << 4));
+    }
+  }
+  // stage: LDS tile base; gbase: global row 0 of the tile; rows: valid rows
+  __device__ __forceinline__ void issue(EA_LDS uint16_t* stage, const uint16_t* gbase, int rows, size_t stride,
+                                        int w) const {
+    const uint32_t nrec = rows > 0 ? (uint32_t)((rows - 1) * (int)stride * 2 + D * 2) : 0u;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(gbase, nrec);
+#pragma unroll
+    for (int i = 0; i < PPW; ++i) buffer_load16_lds(rs, (EA_LDS void*)(stage + 512 * (w * PPW + i)), off[i]);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// dQ: one workgroup = 4 waves x 32 query rows of one (sequence, head); key
+// tiles of 64 in two LDS stages.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int BM = 128, BN = kBwdTileK, NDT = D / 32;
+  constexpr int TILE = BN * D;
+  __shared__ __attribute__((aligned(1024))) uint16_t smem_raw[2 * 2 * TILE];
+  EA_LDS uint16_t* sm = (EA_LDS uint16_t*)smem_raw;
+
+  // XCD-grouped, heaviest first: all row blocks of one (sequence, head) on one XCD
+  const int xcd = blockIdx.x & 7;
+  const int j = blockIdx.x >> 3;
+  const int kg = j / a.n_mb;
+  const int r = j - kg * a.n_mb;
+  const int g = xcd + 8 * kg;
+  if (g >= a.B * a.Hq) return;
+  const int seq = uniform(g / a.Hq);
+  const int h = uniform(g - seq * a.Hq);
+  const int mb = uniform(a.natural ? r : a.n_mb - 1 - r);
+  const int hk = uniform(h / a.group);
+  const int lq = a.Nq, lk = a.Nk;
+  const int off = lk - lq;  // bottom-right causal alignment
+  const int row_lo = mb * BM;
+  int nkeys = lk;
+  if constexpr (CAUSAL) nkeys = min(lk, row_lo + BM + off);
+  if (nkeys < 0) nkeys = 0;
+  const int nkb = uniform((nkeys + BN - 1) / BN);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = uniform(tid >> 6), hh = lane >> 5, c = lane & 31;
+  const int qi = row_lo + w * 32 + c;
+  const size_t qstride = (size_t)a.Hq * D, kstride = (size_t)a.Hkv * D;
+  const size_t q0 = (size_t)seq * lq, k0 = (size_t)seq * lk;
+
+  // Q^T and dO^T operands (B of S^T = K Q^T and dP^T = V dO^T), and the row's
+  // lse2 and D (rows past the end: lse2 = +inf makes P = 0)
+  bf16x8 qf[D / 16], gf[D / 16];
+  {
+    const size_t ro = (q0 + qi) * qstride + (size_t)h * D + 8 * hh;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      qf[kk] = (qi < lq) ? *(const bf16x8*)(a.q + ro + 16 * kk) : bf16x8{};
+      gf[kk] = (qi < lq) ? *(const bf16x8*)(a.dout + ro + 16 * kk) : bf16x8{};
+    }
+  }
+  const size_t rowidx = ((size_t)seq * a.Hq + h) * lq + qi;
+  const float lse2 = (qi < lq) ? a.lse2[rowidx] : __builtin_inff();
+  const float dval = (qi < lq) ? a.dd[rowidx] : 0.f;
+
+  TileDma<D, BN, 4> dma;
+  dma.init(w, lane, kstride);
+  const uint16_t* kg_base = a.k + k0 * kstride + (size_t)hk * D;
+  const uint16_t* vg_base = a.v + k0 * kstride + (size_t)hk * D;
+  auto issue = [&](int kb) {
+    EA_LDS uint16_t* ks = sm + (kb & 1) * 2 * TILE;
+    const int rows = min(lk - kb * BN, BN);
+    dma.issue(ks, kg_base + (size_t)kb * BN * kstride, rows, kstride, w);
+    dma.issue(ks + TILE, vg_base + (size_t)kb * BN * kstride, rows, kstride, w);
+  };
+
+  int k_off[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) k_off[kk] = tile_off<D>(c, 16 * kk + 8 * hh);
+  const int tr_row = 4 * hh + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  int t_off[NDT][2];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    t_off[dt][0] = tile_off<D>(tr_row, 32 * dt + tr_col);
+    t_off[dt][1] = tile_off<D>(tr_row + 8, 32 * dt + tr_col);
+  }
+  const int wave_last_q = row_lo + w * 32 + 31;
+  const int wave_first_q = row_lo + w * 32;
+  const float sl = a.scale_log2;
+
+  f32x16 dq[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) dq[dt] = f32x16{};
+
+  // one 32-key half of a tile: S^T and dP^T, P, dS^T, packed as two B operands
+  auto half = [&](const EA_LDS uint16_t* ks, const EA_LDS uint16_t* vs, int kbase, int hk32, bf16x8& d0,
+                  bf16x8& d1) {
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      s = mfma32x32x16(lds_load<bf16x8>(ks + k_off[kk] + 32 * hk32 * D), qf[kk], s);
+      dp = mfma32x32x16(lds_load<bf16x8>(vs + k_off[kk] + 32 * hk32 * D), gf[kk], dp);
+    }
+    bool need_mask = kbase + 32 * hk32 + 32 > lk;
+    if constexpr (CAUSAL) need_mask = need_mask || (kbase + 32 * hk32 + 31 > wave_first_q + off);
+    int rel = 64;
+    if (need_mask) {
+      int lim = lk;
+      if constexpr (CAUSAL) lim = min(lk, qi + off + 1);
+      rel = lim - kbase - 32 * hk32 - 4 * hh;  // element i valid iff its key offset < rel
+    }
+    float ds[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int ko = 8 * (i >> 2) + (i & 3);
+      const float p = (ko < rel) ? exp2_hw(__builtin_fmaf(s[i], sl, -lse2)) : 0.f;
+      ds[i] = p * (dp[i] - dval);
+    }
+    const i32x4 t0 = {(int)pack_bf16x2(ds[0], ds[1]), (int)pack_bf16x2(ds[2], ds[3]),
+                      (int)pack_bf16x2(ds[4], ds[5]), (int)pack_bf16x2(ds[6], ds[7])};
+    const i32x4 t1 = {(int)pack_bf16x2(ds[8], ds[9]), (int)pack_bf16x2(ds[10], ds[11]),
+                      (int)pack_bf16x2(ds[12], ds[13]), (int)pack_bf16x2(ds[14], ds[15])};
+    d0 = __builtin_bit_cast(bf16x8, t0);
+    d1 = __builtin_bit_cast(bf16x8, t1);
+  };
+
+  if (nkb > 0) issue(0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int kb = 0; kb < nkb; ++kb) {
+    if (kb + 1 < nkb) issue(kb + 1);
+    const EA_LDS uint16_t* ks = sm + (kb & 1) * 2 * TILE;
+    const EA_LDS uint16_t* vs = ks + TILE;
+    const int kbase = kb * BN;
+    if (!(CAUSAL && kbase > wave_last_q + off)) {
+      bf16x8 dsb[4];
+      half(ks, vs, kbase, 0, dsb[0], dsb[1]);
+      half(ks, vs, kbase, 1, dsb[2], dsb[3]);
+      // dQ^T += K^T dS^T
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const i16x4 lo = ds_read_tr16(ks + t_off[dt][0] + 16 * st * D);
+          const i16x4 hi = ds_read_tr16(ks + t_off[dt][1] + 16 * st * D);
+          const i32x4 t = {__builtin_bit_cast(i32x2, lo)[0], __builtin_bit_cast(i32x2, lo)[1],
+                           __builtin_bit_cast(i32x2, hi)[0], __builtin_bit_cast(i32x2, hi)[1]};
+          dq[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, t), dsb[st], dq[dt]);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  // dQ = scale * acc, rows in lanes, d in elements (the forward's O layout)
+  if (qi < lq) {
+    uint16_t* op = a.dq + (q0 + qi) * qstride + (size_t)h * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * dt + 8 * g4 + 4 * hh;
+        uint2 val;
+        val.x = pack_bf16x2(dq[dt][4 * g4] * a.scale, dq[dt][4 * g4 + 1] * a.scale);
+        val.y = pack_bf16x2(dq[dt][4 * g4 + 2] * a.scale, dq[dt][4 * g4 + 3] * a.scale);
+        *(uint2*)(op + d0) = val;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: one workgroup = 4 waves x 32 keys of one (sequence, KV head); it
+// walks every query tile (64 rows) of every query head of the group.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int BK = 128, BQ = kBwdTileQ, NDT = D / 32;
+  constexpr int TILE = BQ * D;
+  __shared__ __attribute__((aligned(1024))) uint16_t smem_raw[2 * 2 * TILE];
+  __shared__ __attribute__((aligned(16))) float rowstat[2][2][BQ];  // [stage][lse2, D][row]
+  EA_LDS uint16_t* sm = (EA_LDS uint16_t*)smem_raw;
+
+  // XCD-grouped; causal: the key blocks with the most query rows (lowest) first
+  const int xcd = blockIdx.x & 7;
+  const int j = blockIdx.x >> 3;
+  const int kg = j / a.n_kb;
+  const int r = j - kg * a.n_kb;
+  const int g = xcd + 8 * kg;
+  if (g >= a.B * a.Hkv) return;
+  const int seq = uniform(g / a.Hkv);
+  const int hk = uniform(g - seq * a.Hkv);
+  const int kblk = uniform(a.natural ? a.n_kb - 1 - r : r);
+  const int lq = a.Nq, lk = a.Nk;
+  const int off = lk - lq;
+  const int k_lo = kblk * BK;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = uniform(tid >> 6), hh = lane >> 5, c = lane & 31;
+  const int kj = k_lo + w * 32 + c;  // this lane's key
+  const size_t qstride = (size_t)a.Hq * D, kstride = (size_t)a.Hkv * D;
+  const size_t q0 = (size_t)seq * lq, k0 = (size_t)seq * lk;
+
+  // K and V as B operands of S = Q K^T and dP = dO V^T: column = key, k = d
+  bf16x8 kf[D / 16], vf[D / 16];
+  {
+    const size_t ro = (k0 + kj) * kstride + (size_t)hk * D + 8 * hh;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      kf[kk] = (kj < lk) ? *(const bf16x8*)(a.k + ro + 16 * kk) : bf16x8{};
+      vf[kk] = (kj < lk) ? *(const bf16x8*)(a.v + ro + 16 * kk) : bf16x8{};
+    }
+  }
+
+  // query tiles: causal rows i see key k_lo iff i + off >= k_lo
+  int qt0 = 0;
+  if constexpr (CAUSAL) qt0 = max(0, k_lo - off) / BQ;
+  const int nqt = uniform(max(0, (lq + BQ - 1) / BQ - qt0));
+  const int ntiles = uniform(nqt * a.group);
+  const int wave_first_k = k_lo + w * 32;
+
+  TileDma<D, BQ, 4> dma;
+  dma.init(w, lane, qstride);
+  auto tile_of = [&](int t, int& hq, int& qt) {
+    hq = hk * a.group + t / nqt;
+    qt = qt0 + t % nqt;
+  };
+  float st_lse = 0.f, st_d = 0.f;  // wave 0: next tile's row statistics, one row per lane
+  auto issue = [&](int t) {
+    int hq, qt;
+    tile_of(t, hq, qt);
+    EA_LDS uint16_t* qs = sm + (t & 1) * 2 * TILE;
+    const int rows = min(lq - qt * BQ, BQ);
+    const size_t go = (q0 + (size_t)qt * BQ) * qstride + (size_t)hq * D;
+    dma.issue(qs, a.q + go, rows, qstride, w);
+    dma.issue(qs + TILE, a.dout + go, rows, qstride, w);
+    if (w == 0) {
+      const int row = qt * BQ + lane;
+      const size_t idx = ((size_t)seq * a.Hq + hq) * lq + row;
+      st_lse = row < lq ? a.lse2[idx] : __builtin_inff();  // rows past the end: P = 0
+      st_d = row < lq ? a.dd[idx] : 0.f;
+    }
+  };
+  auto park_stats = [&](int t) {
+    if (w == 0) {
+      lds_store<float>((EA_LDS float*)rowstat[t & 1][0] + lane, st_lse);
+      lds_store<float>((EA_LDS float*)rowstat[t & 1][1] + lane, st_d);
+    }
+  };
+
+  int q_off[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) q_off[kk] = tile_off<D>(c, 16 * kk + 8 * hh);
+  const int tr_row = 4 * hh + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  int t_off[NDT][2];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    t_off[dt][0] = tile_off<D>(tr_row, 32 * dt + tr_col);
+    t_off[dt][1] = tile_off<D>(tr_row + 8, 32 * dt + tr_col);
+  }
+  const float sl = a.scale_log2;
+
+  f32x16 dk[NDT], dv[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    dk[dt] = f32x16{};
+    dv[dt] = f32x16{};
+  }
+
+  if (ntiles > 0) {
+    issue(0);
+    __builtin_amdgcn_s_waitcnt(0);
+    park_stats(0);
+  }
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 1 < ntiles) issue(t + 1);
+    int hq, qt;
+    tile_of(t, hq, qt);
+    const EA_LDS uint16_t* qs = sm + (t & 1) * 2 * TILE;
+    const EA_LDS uint16_t* gs = qs + TILE;
+    const EA_LDS float* lse_s = (const EA_LDS float*)rowstat[t & 1][0];
+    const EA_LDS float* d_s = (const EA_LDS float*)rowstat[t & 1][1];
+#pragma unroll
+    for (int rs = 0; rs < BQ / 32; ++rs) {
+      const int rbase = qt * BQ + 32 * rs;  // first row of this 32-row slice
+      // causal: the slice's last row sees none of this wave's keys
+      if (CAUSAL && rbase + 31 + off < wave_first_k) continue;
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        s = mfma32x32x16(lds_load<bf16x8>(qs + q_off[kk] + 32 * rs * D), kf[kk], s);
+        dp = mfma32x32x16(lds_load<bf16x8>(gs + q_off[kk] + 32 * rs * D), vf[kk], dp);
+      }
+      // element i holds row rbase + 8 (i / 4) + 4 hh + i % 4 of key kj
+      float p[16], ds[16];
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int rloc = 32 * rs + 8 * i4 + 4 * hh;
+        const f32x4 l4 = lds_load<f32x4>(lse_s + rloc);
+        const f32x4 d4 = lds_load<f32x4>(d_s + rloc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * i4 + e;
+          bool ok = true;
+          if constexpr (CAUSAL) ok = kj <= rbase + 8 * i4 + 4 * hh + e + off;
+          p[i] = ok ? exp2_hw(__builtin_fmaf(s[i], sl, -l4[e])) : 0.f;
+          ds[i] = p[i] * (dp[i] - d4[e]);
+        }
+      }
+      bf16x8 pb[2], db[2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int b0 = 8 * st;
+        const i32x4 tp = {(int)pack_bf16x2(p[b0], p[b0 + 1]), (int)pack_bf16x2(p[b0 + 2], p[b0 + 3]),
+                          (int)pack_bf16x2(p[b0 + 4], p[b0 + 5]), (int)pack_bf16x2(p[b0 + 6], p[b0 + 7])};
+        const i32x4 td = {(int)pack_bf16x2(ds[b0], ds[b0 + 1]), (int)pack_bf16x2(ds[b0 + 2], ds[b0 + 3]),
+                          (int)pack_bf16x2(ds[b0 + 4], ds[b0 + 5]), (int)pack_bf16x2(ds[b0 + 6], ds[b0 + 7])};
+        pb[st] = __builtin_bit_cast(bf16x8, tp);
+        db[st] = __builtin_bit_cast(bf16x8, td);
+      }
+      // dV^T += dO^T P, dK^T += Q^T dS (A operands read transposed, rows
+      // permuted like the packed B operands)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const int ro = (32 * rs + 16 * st) * D;
+          const i16x4 glo = ds_read_tr16(gs + t_off[dt][0] + ro);
+          const i16x4 ghi = ds_read_tr16(gs + t_off[dt][1] + ro);
+          const i32x4 ga = {__builtin_bit_cast(i32x2, glo)[0], __builtin_bit_cast(i32x2, glo)[1],
+                            __builtin_bit_cast(i32x2, ghi)[0], __builtin_bit_cast(i32x2, ghi)[1]};
+          dv[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, ga), pb[st], dv[dt]);
+          const i16x4 qlo = ds_read_tr16(qs + t_off[dt][0] + ro);
+          const i16x4 qhi = ds_read_tr16(qs + t_off[dt][1] + ro);
+          const i32x4 qa = {__builtin_bit_cast(i32x2, qlo)[0], __builtin_bit_cast(i32x2, qlo)[1],
+                            __builtin_bit_cast(i32x2, qhi)[0], __builtin_bit_cast(i32x2, qhi)[1]};
+          dk[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, qa), db[st], dk[dt]);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    if (t + 1 < ntiles) park_stats(t + 1);
+    __syncthreads();
+  }
+
+  // dK = scale * acc, dV = acc: keys in lanes, d in elements
+  if (kj < lk) {
+    const size_t ro = (k0 + kj) * kstride + (size_t)hk * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * dt + 8 * g4 + 4 * hh;
+        uint2 kv, vv;
+        kv.x = pack_bf16x2(dk[dt][4 * g4] * a.scale, dk[dt][4 * g4 + 1] * a.scale);
+        kv.y = pack_bf16x2(dk[dt][4 * g4 + 2] * a.scale, dk[dt][4 * g4 + 3] * a.scale);
+        vv.x = pack_bf16x2(dv[dt][4 * g4], dv[dt][4 * g4 + 1]);
+        vv.y = pack_bf16x2(dv[dt][4 * g4 + 2], dv[dt][4 * g4 + 3]);
+        *(uint2*)(a.dk + ro + d0) = kv;
+        *(uint2*)(a.dv + ro + d0) = vv;
+      }
+    }
+  }
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
+  const int rows = a.B * a.Nq * a.Hq;
+  hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((rows + 15) / 16), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int gq = 8 * ((a.B * a.Hq + 7) / 8) * a.n_mb;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(gq), dim3(256), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int gk = 8 * ((a.B * a.Hkv + 7) / 8) * a.n_kb;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(gk), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdArgs& a, int d, bool causal, hipStream_t s) {
+  if (d == 64) return causal ? launch_bwd_t<64, true>(a, s) : launch_bwd_t<64, false>(a, s);
+  return causal ? launch_bwd_t<128, true>(a, s) : launch_bwd_t<128, false>(a, s);
+}
+
+size_t bwd_workspace_bytes(int B, int Hq, int Nq) {
+  const size_t n = (size_t)B * Hq * Nq * sizeof(float);
+  return 2 * ((n + 255) & ~(size_t)255);
+}
+
+void bwd_bind_workspace(BwdArgs& a, void* workspace) {
+  const size_t n = (size_t)a.B * a.Hq * a.Nq * sizeof(float);
+  char* p = (char*)workspace;
+  a.dd = (float*)p;
+  a.lse2 = (float*)(p + ((n + 255) & ~(size_t)255));
+}
+
+}  // namespace ea

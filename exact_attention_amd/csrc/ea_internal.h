@@ -65,6 +65,30 @@ hipError_t launch_fwd_mx8(const Mx8Args& a, bool causal, hipStream_t s);
 // 8-wave software-pipelined MX fp8 forward; a.n_mb counts kPpBlockM-row blocks
 hipError_t launch_fwd_mx8_sp(const Mx8Args& a, bool causal, hipStream_t s);
 
+// Backward (bf16, dense BSHD): dQ, dK, dV of O = softmax(scale Q K^T) V for
+// the output gradient dout, from the forward's O and lse.
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;    // [B, Hq, Nq] natural log, scale included
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* dd;           // workspace [B, Hq, Nq]: dO . O per row
+  float* lse2;         // workspace [B, Hq, Nq]: lse * log2(e)
+  int B, Nq, Nk, Hq, Hkv, group;
+  int n_mb;            // 128-row query blocks (dQ kernel)
+  int n_kb;            // 128-key blocks (dK/dV kernel)
+  float scale, scale_log2;
+  int natural;         // 1: ascending block order (results do not depend on it)
+};
+hipError_t launch_bwd(const BwdArgs& a, int d, bool causal, hipStream_t s);
+size_t bwd_workspace_bytes(int B, int Hq, int Nq);
+void bwd_bind_workspace(BwdArgs& a, void* workspace);
+
 // Paged split-KV decode
 struct DecodeArgs {
   const uint16_t* q;

@@ -208,6 +208,30 @@ ea_status ea_attn_fwd_mx8_tuned(const void* q8, const void* k8, const void* v8,
                                 void* o, float* lse, int B, int N, int Hq, int Hkv, int d, int causal,
                                 float scale, const ea_fwd_tuning* tuning, void* stream);
 
+/*
+ * Backward of the dense bf16 forward ("Low-precision FlashAttention-4:
+ * end-to-end block-scaled attention for Blackwell", section 2.2, lists its
+ * five products; "FlashAttention-4: algorithm-pipeline co-design for
+ * Blackwell", backward sections): for the output gradient dout it writes
+ *   dq = scale dS K,  dk = scale dS^T Q,  dv = P^T dout,
+ * with P = softmax(scale Q K^T) recomputed from lse, dP = dout V^T and
+ * dS = P (dP - rowsum(dout * o)). GQA: dk / dv of a KV head sum over the query
+ * heads that read it. Deterministic: every output element is written once by
+ * one workgroup, in a fixed order (no atomics), so repeated calls give the
+ * same bits.
+ *   q, o, dout, dq [B, Nq, Hq, d] bf16; k, v, dk, dv [B, Nk, Hkv, d] bf16
+ *     (dq, dk, dv written);
+ *   lse [B, Hq, Nq] fp32: the forward's log-sum-exp (natural log, scale
+ *     included), as ea_attn_fwd writes it; rows with no allowed key (lse =
+ *     -inf) get dq = 0;
+ *   d in {64, 128}; causal / scale as for the forward that produced o and lse;
+ *   workspace: device memory of at least ea_attn_bwd_workspace_size(B, Hq, Nq)
+ *     bytes (per-row statistics), owned by the caller, contents ignored.
+ */
+size_t ea_attn_bwd_workspace_size(int B, int Hq, int Nq);
+ea_status ea_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                      const float* lse, void* dq, void* dk, void* dv, int B, int Nq, int Nk, int Hq, int Hkv,
+                      int d, int causal, float scale, void* workspace, size_t workspace_bytes, void* stream);
 /* FP8 element formats of the MX inputs (OCP FP8): e4m3 = 4 exponent bits
  * (bias 7), 3 mantissa bits, largest finite 448, no infinities; e5m2 = 5
  * exponent bits (bias 15), 2 mantissa bits, largest finite 57344, with

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("ea_attn_fwd", "ea_attn_fwd_hd", "ea_attn_fwd_varlen", "ea_attn_fwd_varlen_ordered", "ea_varlen_lpt_order",
+    for n in ("ea_attn_fwd", "ea_attn_fwd_hd", "ea_attn_bwd", "ea_attn_bwd_workspace_size", "ea_attn_fwd_varlen", "ea_attn_fwd_varlen_ordered", "ea_varlen_lpt_order",
               "ea_attn_fwd_mx8", "ea_attn_fwd_mx8_tuned", "ea_attn_fwd_mx8_fmt", "ea_attn_decode_paged",
               "ea_decode_workspace_size", "ea_last_error"):
         assert n in names
@@ -145,6 +145,25 @@ def test_mfma_loop_argument_errors(lib):
     assert lib.ea_test_mfma_loop(P, 0, 10, None) == -1
     assert lib.ea_test_mfma_loop(P, 4, 0, None) == -1
     assert lib.ea_test_mfma_loop(P, 1 << 17, 10, None) == -1
+
+
+def test_bwd_argument_errors(lib):
+    ws = lib.ea_attn_bwd_workspace_size(1, 2, 8)
+    assert ws >= 2 * 2 * 8 * 4 and lib.ea_attn_bwd_workspace_size(0, 2, 8) == 0
+    f = lib.ea_attn_bwd
+
+    def call(q=P, lse=P, B=1, Nq=8, Nk=8, Hq=2, Hkv=2, d=128, causal=0, scale=0.1, wsp=P, wsb=ws):
+        return f(q, P, P, P, P, lse, P, P, P, B, Nq, Nk, Hq, Hkv, d, causal, scale, wsp, wsb, None)
+
+    assert call(q=None) == -1 and "non-null" in _err(lib)
+    assert call(lse=None) == -1
+    assert call(Nk=0) == -1
+    assert call(Hq=3) == -1 and "multiple" in _err(lib)
+    assert call(d=96) == -2
+    assert call(scale=float("inf")) == -1
+    assert call(causal=3) == -1
+    assert call(wsb=ws - 1) == -4 and "workspace" in _err(lib)
+    assert call(wsp=None) == -4
 
 
 def test_binding_refuses_cpu_tensors():

@@ -31,6 +31,7 @@ import numpy as np
 
 CHUNK = 1 << 22
 STREAM_Q, STREAM_K, STREAM_V, STREAM_KC, STREAM_VC, STREAM_META = 0, 1, 2, 3, 4, 9
+STREAM_DO = 5   # output gradients for the backward
 
 
 def _threads() -> int:
