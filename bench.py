@@ -54,8 +54,10 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--exp-mode", type=int, default=0)
-    p.add_argument("--only", choices=["prefill", "decode", "fp8"], default=None,
+    p.add_argument("--only", choices=["prefill", "decode", "fp8", "bwd"], default=None,
                    help="time one kernel family only (profiling runs)")
+    p.add_argument("--with-bwd", action="store_true",
+                   help="also time the backward (dQ, dK, dV) on the prefill workload; reported under 'bwd'")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-gemm-calibration", action="store_true",
                    help="skip the vendor-GEMM rate measured after the timed region")
@@ -220,6 +222,7 @@ def main():
     run_prefill = args.only in (None, "prefill")
     run_decode = args.only in (None, "decode")
     run_fp8 = args.only in (None, "fp8")
+    run_bwd = args.only == "bwd" or (args.only is None and args.with_bwd)
     t_gen = time.perf_counter()
     if run_prefill:
         d_qk, d_v = (int(x) for x in args.prefill_dims.split(","))
@@ -251,6 +254,14 @@ def main():
         pools = [(pg.k_cache, pg.v_cache, bt), (kc2, vc2, bt2)]
         do = torch.empty_like(dq)
         dlse = torch.empty((Bd, Hq), dtype=torch.float32, device=dev)
+    if run_bwd:
+        bin_ = W.prefill(True)
+        bq, bk, bv = dev_bf16(bin_.q), dev_bf16(bin_.k), dev_bf16(bin_.v)
+        bB, bN, bH, bd = bin_.q.shape
+        bdo = dev_bf16(W.normal_bf16_bits(1002, W.STREAM_DO, (bB, bN, bH, bd)))
+        bo, blse = ea.attn_fwd(bq, bk, bv, True, bin_.scale)
+        bws = torch.empty(ea.lib().ea_attn_bwd_workspace_size(bB, bH, bN), dtype=torch.uint8, device=dev)
+        bdq, bdk, bdv = torch.empty_like(bq), torch.empty_like(bk), torch.empty_like(bv)
     if run_fp8:
         m8 = W.fp8_prefill(args.fp8_format)
         t8 = [torch.from_numpy(np.ascontiguousarray(x)).to(dev)
@@ -262,6 +273,13 @@ def main():
     t_gen = time.perf_counter() - t_gen
 
     def step(i, ev):
+        if run_bwd:
+            ev[6].record(stream)
+            r = ea.lib().ea_attn_bwd(ea._ptr(bq), ea._ptr(bk), ea._ptr(bv), ea._ptr(bo), ea._ptr(bdo), ea._ptr(blse),
+                                     ea._ptr(bdq), ea._ptr(bdk), ea._ptr(bdv), bB, bN, bN, bH, bH, bd, 1, bin_.scale,
+                                     ea._ptr(bws), bws.numel(), stream.cuda_stream)
+            ea._check(r, "ea_attn_bwd")
+            ev[7].record(stream)
         if run_prefill:
             ev[0].record(stream)
             ea.attn_fwd(q, k, v, True, inp.scale, tuning=tun, out=o, lse=lse)
@@ -282,8 +300,8 @@ def main():
             ea._check(r, "ea_attn_fwd_mx8_fmt")
             ev[5].record(stream)
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
-    wev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
+    wev = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
     for i in range(args.warmup):
         step(i, wev)
     torch.cuda.synchronize()
@@ -339,6 +357,19 @@ def main():
                                "kernel": f"ea::fwd_mx8_sp_kernel<causal, {m8.fmt}>"}
         if not (run_prefill or run_decode):
             out["value"], out["unit"], out["dtype"] = tf8, "TFLOP/s", f"fp8_{m8.fmt}"
+    if run_bwd:
+        t_bw = np.array([e[6].elapsed_time(e[7]) for e in evs])
+        # algorithmic FLOPs of the backward: its five products (S, dP, dV, dK,
+        # dQ), 2 N^2 d each, causal half
+        flops_b = 5 * 2.0 * bB * bH * bN * bN * bd / 2.0
+        tfb = flops_b / (t_bw.mean() * 1e-3) / 1e12
+        out["bwd"] = {"value": tfb, "unit": "TFLOP/s", "ms_mean": float(t_bw.mean()), "ms_min": float(t_bw.min()),
+                      "flop_per_launch": flops_b, "workload": "B=4 H=16 N=8192 d=128 causal bf16 (dQ, dK, dV)",
+                      "flop_convention": "5 products x 2 N^2 d, causal half; the kernels compute 7 (S and dP twice)",
+                      "kernels": "ea::bwd_prep_kernel + ea::bwd_dq_kernel + ea::bwd_dkdv_kernel",
+                      "frac_of_peak": tfb / PEAK_BF16_TFLOPS}
+        if not (run_prefill or run_decode or run_fp8):
+            out["value"], out["unit"] = tfb, "TFLOP/s"
     if not args.no_gemm_calibration:
         for key, dt_name, n in (("roofline", "bf16", 8192), ("roofline_fp8", "fp8", 16384)):
             if key in out:

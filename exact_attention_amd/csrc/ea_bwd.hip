@@ -14,10 +14,10 @@
 //    global fp32 buffer (and serialise them for the deterministic mode). At
 //    N = 8192 with 128-key blocks that is 64 read-modify-writes per dQ element.
 //    Here two kernels split the work instead, each owning its outputs:
-//      - bwd_dkdv_kernel: one workgroup per (sequence, KV head, 128 keys), 4
-//        waves x 32 keys, loops over every query tile of every query head of
-//        the KV head's group; dK and dV accumulate in registers (4 products:
-//        S, dP, dV, dK);
+//      - bwd_dkdv_kernel: one workgroup per (sequence, KV head, 128 keys), 8
+//        waves in two roles on each 32-key block (below), loops over every
+//        query tile of every query head of the KV head's group; dK and dV
+//        accumulate in registers (4 products: S, dP, dV, dK);
 //      - bwd_dq_kernel: one workgroup per (sequence, head, 128 query rows), 4
 //        waves x 32 rows, loops over the key tiles (3 products: S, dP, dQ).
 //    S and dP are computed twice (7 products instead of 5); in exchange every
@@ -33,9 +33,14 @@
 //                   accumulator layout (the permuted-key trick of the forward);
 //      dK/dV kernel: S = Q K^T and dP = dO V^T (Q, dO from LDS, K and V held as
 //                   B operands), so a lane owns one key; dV^T += dO^T P and
-//                   dK^T += Q^T dS with dO^T and Q^T read transposed.
+//                   dK^T += Q^T dS with dO^T and Q^T read transposed. The
+//                   two waves on a SIMD take one role each (S, P, dV / dP,
+//                   dS, dK) and hand P over through LDS, so one wave's vector
+//                   work overlaps the other's matrix products.
 //  * Tiles arrive by LDS DMA (buffer_load ... lds) into two stages, issued a
 //    tile ahead; rows past the sequence land as zeros.
+#include <type_traits>
+
 #include "ea_device.h"
 #include "ea_fwd_common.h"
 #include "ea_internal.h"
@@ -231,11 +236,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       bf16x8 dsb[4];
       half(ks, vs, kbase, 0, dsb[0], dsb[1]);
       half(ks, vs, kbase, 1, dsb[2], dsb[3]);
-      // dQ^T += K^T dS^T
+      // dQ^T += K^T dS^T (the d tiles inner, so consecutive MFMAs use
+      // different accumulators)
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
+      for (int st = 0; st < 4; ++st) {
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
+        for (int dt = 0; dt < NDT; ++dt) {
           const i16x4 lo = ds_read_tr16(ks + t_off[dt][0] + 16 * st * D);
           const i16x4 hi = ds_read_tr16(ks + t_off[dt][1] + 16 * st * D);
           const i32x4 t = {__builtin_bit_cast(i32x2, lo)[0], __builtin_bit_cast(i32x2, lo)[1],
@@ -266,15 +272,28 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: one workgroup = 4 waves x 32 keys of one (sequence, KV head); it
-// walks every query tile (64 rows) of every query head of the group.
+// dK, dV: one workgroup = 8 waves for 128 keys of one (sequence, KV head); it
+// walks every query tile (64 rows, two 32-row slices) of every query head of
+// the group. Waves w and w + 4 share a SIMD and a 32-key block and split the
+// products by role, half a step apart:
+//   phase k, role A (w < 4):  dV^T += dO^T P(k-1), then S(k) = Q K^T,
+//                             P(k) = 2^(S scale log2e - lse2) -> LDS;
+//   phase k, role B (w >= 4): dS(k-1) = P(k-1) (dP(k-1) - D) with P from LDS,
+//                             dK^T += Q^T dS(k-1), then dP(k) = dO V^T.
+// One workgroup barrier ends each phase. On every SIMD role A's matrix
+// products run beside role B's vector work at the start of a phase and the
+// other way round at its end. A tile serves three phases (its two slices and
+// the deferred second products of the last), so tiles sit in three LDS stages
+// and each one's DMA is issued three phases before its first use.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int BK = 128, BQ = kBwdTileQ, NDT = D / 32;
   constexpr int TILE = BQ * D;
-  __shared__ __attribute__((aligned(1024))) uint16_t smem_raw[2 * 2 * TILE];
-  __shared__ __attribute__((aligned(16))) float rowstat[2][2][BQ];  // [stage][lse2, D][row]
+  constexpr int NSTAGE = 3;
+  __shared__ __attribute__((aligned(1024))) uint16_t smem_raw[NSTAGE * 2 * TILE];
+  __shared__ __attribute__((aligned(16))) float rowstat[NSTAGE][2][BQ];  // [stage][lse2, D][row]
+  __shared__ __attribute__((aligned(16))) float pxch[2][4][4 * 64 * 4];  // [parity][pair][chunk][lane][4]
   EA_LDS uint16_t* sm = (EA_LDS uint16_t*)smem_raw;
 
   // XCD-grouped; causal: the key blocks with the most query rows (lowest) first
@@ -293,19 +312,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = uniform(tid >> 6), hh = lane >> 5, c = lane & 31;
-  const int kj = k_lo + w * 32 + c;  // this lane's key
+  const int pr = w & 3;              // 32-key block of this wave pair
+  const bool role_b = w >= 4;        // wave-uniform
+  const int kj = k_lo + pr * 32 + c;  // this lane's key
   const size_t qstride = (size_t)a.Hq * D, kstride = (size_t)a.Hkv * D;
   const size_t q0 = (size_t)seq * lq, k0 = (size_t)seq * lk;
 
-  // K and V as B operands of S = Q K^T and dP = dO V^T: column = key, k = d
-  bf16x8 kf[D / 16], vf[D / 16];
+  // the pair's stationary operand (B of the first product): K for role A, V for role B
+  bf16x8 opnd[D / 16];
   {
+    const uint16_t* src = role_b ? a.v : a.k;
     const size_t ro = (k0 + kj) * kstride + (size_t)hk * D + 8 * hh;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      kf[kk] = (kj < lk) ? *(const bf16x8*)(a.k + ro + 16 * kk) : bf16x8{};
-      vf[kk] = (kj < lk) ? *(const bf16x8*)(a.v + ro + 16 * kk) : bf16x8{};
-    }
+    for (int kk = 0; kk < D / 16; ++kk) opnd[kk] = (kj < lk) ? *(const bf16x8*)(src + ro + 16 * kk) : bf16x8{};
   }
 
   // query tiles: causal rows i see key k_lo iff i + off >= k_lo
@@ -313,19 +332,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   if constexpr (CAUSAL) qt0 = max(0, k_lo - off) / BQ;
   const int nqt = uniform(max(0, (lq + BQ - 1) / BQ - qt0));
   const int ntiles = uniform(nqt * a.group);
-  const int wave_first_k = k_lo + w * 32;
+  const int nslices = 2 * ntiles;
 
-  TileDma<D, BQ, 4> dma;
+  TileDma<D, BQ, 8> dma;
   dma.init(w, lane, qstride);
+  constexpr int kDmaOps = 2 * TileDma<D, BQ, 8>::PPW;  // vector memory ops per wave per tile
   auto tile_of = [&](int t, int& hq, int& qt) {
     hq = hk * a.group + t / nqt;
     qt = qt0 + t % nqt;
   };
-  float st_lse = 0.f, st_d = 0.f;  // wave 0: next tile's row statistics, one row per lane
+  // wave 0 also loads the tile's row statistics (two more vector memory ops)
+  float st_lse[2] = {0.f, 0.f}, st_d[2] = {0.f, 0.f};
   auto issue = [&](int t) {
     int hq, qt;
     tile_of(t, hq, qt);
-    EA_LDS uint16_t* qs = sm + (t & 1) * 2 * TILE;
+    EA_LDS uint16_t* qs = sm + (t % NSTAGE) * 2 * TILE;
     const int rows = min(lq - qt * BQ, BQ);
     const size_t go = (q0 + (size_t)qt * BQ) * qstride + (size_t)hq * D;
     dma.issue(qs, a.q + go, rows, qstride, w);
@@ -333,14 +354,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     if (w == 0) {
       const int row = qt * BQ + lane;
       const size_t idx = ((size_t)seq * a.Hq + hq) * lq + row;
-      st_lse = row < lq ? a.lse2[idx] : __builtin_inff();  // rows past the end: P = 0
-      st_d = row < lq ? a.dd[idx] : 0.f;
+      st_lse[t & 1] = row < lq ? a.lse2[idx] : __builtin_inff();  // rows past the end: P = 0
+      st_d[t & 1] = row < lq ? a.dd[idx] : 0.f;
     }
   };
   auto park_stats = [&](int t) {
     if (w == 0) {
-      lds_store<float>((EA_LDS float*)rowstat[t & 1][0] + lane, st_lse);
-      lds_store<float>((EA_LDS float*)rowstat[t & 1][1] + lane, st_d);
+      lds_store<float>((EA_LDS float*)rowstat[t % NSTAGE][0] + lane, st_lse[t & 1]);
+      lds_store<float>((EA_LDS float*)rowstat[t % NSTAGE][1] + lane, st_d[t & 1]);
     }
   };
 
@@ -357,105 +378,176 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   }
   const float sl = a.scale_log2;
 
-  f32x16 dk[NDT], dv[NDT];
+  f32x16 acc[NDT];  // dV^T (role A) or dK^T (role B)
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) {
-    dk[dt] = f32x16{};
-    dv[dt] = f32x16{};
-  }
+  for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x16{};
 
-  if (ntiles > 0) {
-    issue(0);
-    __builtin_amdgcn_s_waitcnt(0);
-    park_stats(0);
-  }
+  if (ntiles > 0) issue(0);
+  if (ntiles > 1) issue(1);
+  __builtin_amdgcn_s_waitcnt(0);
+  if (ntiles > 0) park_stats(0);
+  if (ntiles > 1) park_stats(1);
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) issue(t + 1);
-    int hq, qt;
-    tile_of(t, hq, qt);
-    const EA_LDS uint16_t* qs = sm + (t & 1) * 2 * TILE;
-    const EA_LDS uint16_t* gs = qs + TILE;
-    const EA_LDS float* lse_s = (const EA_LDS float*)rowstat[t & 1][0];
-    const EA_LDS float* d_s = (const EA_LDS float*)rowstat[t & 1][1];
-#pragma unroll
-    for (int rs = 0; rs < BQ / 32; ++rs) {
-      const int rbase = qt * BQ + 32 * rs;  // first row of this 32-row slice
-      // causal: the slice's last row sees none of this wave's keys
-      if (CAUSAL && rbase + 31 + off < wave_first_k) continue;
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        s = mfma32x32x16(lds_load<bf16x8>(qs + q_off[kk] + 32 * rs * D), kf[kk], s);
-        dp = mfma32x32x16(lds_load<bf16x8>(gs + q_off[kk] + 32 * rs * D), vf[kk], dp);
+
+  // phase k opens by issuing tile k / 2 + 2 on the second slice of tile k / 2
+  // (its stage was freed by the barrier that ended phase k - 1, the last one
+  // tile k / 2 - 1 used)
+  auto phase_begin = [&](int k) __attribute__((always_inline)) {
+    if ((k & 1) && (k >> 1) + 2 < ntiles) issue((k >> 1) + 2);
+  };
+  // phase k closes: P stores done; before the first phase of tile u =
+  // (k + 1) / 2 >= 2 its DMA (issued at phase 2u - 3) has landed -- only tile
+  // u + 1's, issued at this phase's start, may still be in flight
+  auto phase_end = [&](int k) __attribute__((always_inline)) {
+    wait_lgkm0();
+    if ((k & 1) && (k >> 1) + 1 < ntiles && (k >> 1) + 1 >= 2) {
+      const int u = (k >> 1) + 1;
+      if (u + 1 < ntiles) {
+        if (w == 0) wait_vmcnt<kDmaOps + 2>(); else wait_vmcnt<kDmaOps>();
+      } else {
+        __builtin_amdgcn_s_waitcnt(0);
       }
-      // element i holds row rbase + 8 (i / 4) + 4 hh + i % 4 of key kj
-      float p[16], ds[16];
+      park_stats(u);
+      wait_lgkm0();
+    }
+    pp_barrier();
+  };
+  // first product of slice k: X = T1 opnd^T over the 32 rows, two independent
+  // accumulation chains (even and odd d chunks)
+  auto first_product = [&](int k, const EA_LDS uint16_t* t1) __attribute__((always_inline)) -> f32x16 {
+    const int rs = k & 1;
+    f32x16 x0 = f32x16{}, x1 = f32x16{};
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int rloc = 32 * rs + 8 * i4 + 4 * hh;
-        const f32x4 l4 = lds_load<f32x4>(lse_s + rloc);
-        const f32x4 d4 = lds_load<f32x4>(d_s + rloc);
+    for (int kk = 0; kk < D / 16; kk += 2) {
+      x0 = mfma32x32x16(lds_load<bf16x8>(t1 + q_off[kk] + 32 * rs * D), opnd[kk], x0);
+      x1 = mfma32x32x16(lds_load<bf16x8>(t1 + q_off[kk + 1] + 32 * rs * D), opnd[kk + 1], x1);
+    }
+    return x0 + x1;
+  };
+  // second product of slice kp: acc += T2^T Y (T2 read transposed, rows permuted
+  // like the packed B operand)
+  auto second_product = [&](int kp, const EA_LDS uint16_t* t2, const bf16x8 (&yb)[2]) __attribute__((always_inline)) {
+    const int rs = kp & 1;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * i4 + e;
-          bool ok = true;
-          if constexpr (CAUSAL) ok = kj <= rbase + 8 * i4 + 4 * hh + e + off;
-          p[i] = ok ? exp2_hw(__builtin_fmaf(s[i], sl, -l4[e])) : 0.f;
-          ds[i] = p[i] * (dp[i] - d4[e]);
-        }
-      }
-      bf16x8 pb[2], db[2];
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const int b0 = 8 * st;
-        const i32x4 tp = {(int)pack_bf16x2(p[b0], p[b0 + 1]), (int)pack_bf16x2(p[b0 + 2], p[b0 + 3]),
-                          (int)pack_bf16x2(p[b0 + 4], p[b0 + 5]), (int)pack_bf16x2(p[b0 + 6], p[b0 + 7])};
-        const i32x4 td = {(int)pack_bf16x2(ds[b0], ds[b0 + 1]), (int)pack_bf16x2(ds[b0 + 2], ds[b0 + 3]),
-                          (int)pack_bf16x2(ds[b0 + 4], ds[b0 + 5]), (int)pack_bf16x2(ds[b0 + 6], ds[b0 + 7])};
-        pb[st] = __builtin_bit_cast(bf16x8, tp);
-        db[st] = __builtin_bit_cast(bf16x8, td);
-      }
-      // dV^T += dO^T P, dK^T += Q^T dS (A operands read transposed, rows
-      // permuted like the packed B operands)
+    for (int st = 0; st < 2; ++st) {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const int ro = (32 * rs + 16 * st) * D;
-          const i16x4 glo = ds_read_tr16(gs + t_off[dt][0] + ro);
-          const i16x4 ghi = ds_read_tr16(gs + t_off[dt][1] + ro);
-          const i32x4 ga = {__builtin_bit_cast(i32x2, glo)[0], __builtin_bit_cast(i32x2, glo)[1],
-                            __builtin_bit_cast(i32x2, ghi)[0], __builtin_bit_cast(i32x2, ghi)[1]};
-          dv[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, ga), pb[st], dv[dt]);
-          const i16x4 qlo = ds_read_tr16(qs + t_off[dt][0] + ro);
-          const i16x4 qhi = ds_read_tr16(qs + t_off[dt][1] + ro);
-          const i32x4 qa = {__builtin_bit_cast(i32x2, qlo)[0], __builtin_bit_cast(i32x2, qlo)[1],
-                            __builtin_bit_cast(i32x2, qhi)[0], __builtin_bit_cast(i32x2, qhi)[1]};
-          dk[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, qa), db[st], dk[dt]);
-        }
+        const int ro = (32 * rs + 16 * st) * D;
+        const i16x4 lo = ds_read_tr16(t2 + t_off[dt][0] + ro);
+        const i16x4 hi = ds_read_tr16(t2 + t_off[dt][1] + ro);
+        const i32x4 ta = {__builtin_bit_cast(i32x2, lo)[0], __builtin_bit_cast(i32x2, lo)[1],
+                          __builtin_bit_cast(i32x2, hi)[0], __builtin_bit_cast(i32x2, hi)[1]};
+        acc[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, ta), yb[st], acc[dt]);
       }
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    if (t + 1 < ntiles) park_stats(t + 1);
-    __syncthreads();
+  };
+  auto pack16 = [&](const float (&y)[16], bf16x8 (&yb)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int b0 = 8 * st;
+      const i32x4 t = {(int)pack_bf16x2(y[b0], y[b0 + 1]), (int)pack_bf16x2(y[b0 + 2], y[b0 + 3]),
+                       (int)pack_bf16x2(y[b0 + 4], y[b0 + 5]), (int)pack_bf16x2(y[b0 + 6], y[b0 + 7])};
+      yb[st] = __builtin_bit_cast(bf16x8, t);
+    }
+  };
+  auto stage_of = [&](int k) { return sm + ((k >> 1) % NSTAGE) * 2 * TILE; };
+
+  // The phases are straight-line code: a slice that causal masking hides from
+  // the pair still runs its products (P = 0 there, so they add exact zeros).
+  if (!role_b) {
+    // ---------------- role A: S, P (to LDS), dV
+    bf16x8 pk[2];
+    int hq = hk * a.group, qt = qt0;  // tile of the current slice
+    auto phase_a = [&](int k, auto has_prev, auto has_cur) __attribute__((always_inline)) {
+      phase_begin(k);
+      if constexpr (decltype(has_prev)::value) second_product(k - 1, stage_of(k - 1) + TILE, pk);  // dO^T P
+      if constexpr (decltype(has_cur)::value) {
+        const EA_LDS uint16_t* qs = stage_of(k);
+        const f32x16 x = first_product(k, qs);  // S = Q K^T
+        const int rs = k & 1;
+        const int rbase = qt * BQ + 32 * rs;
+        const EA_LDS float* lst = (const EA_LDS float*)rowstat[(k >> 1) % NSTAGE][0];
+        EA_LDS f32x4* xp = (EA_LDS f32x4*)pxch[k & 1][pr];
+        float p[16];
+        // element i = row rbase + 8 (i / 4) + 4 hh + i % 4 of key kj
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const f32x4 l4 = lds_load<f32x4>(lst + 32 * rs + 8 * i4 + 4 * hh);
+          f32x4 p4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            bool ok = true;
+            if constexpr (CAUSAL) ok = kj <= rbase + 8 * i4 + 4 * hh + e + off;
+            p4[e] = ok ? exp2_hw(__builtin_fmaf(x[4 * i4 + e], sl, -l4[e])) : 0.f;
+            p[4 * i4 + e] = p4[e];
+          }
+          lds_store<f32x4>(xp + 64 * i4 + lane, p4);
+        }
+        pack16(p, pk);
+        if (rs == 1 && ++qt == qt0 + nqt) {
+          qt = qt0;
+          ++hq;
+        }
+      }
+      phase_end(k);
+    };
+    using T = std::integral_constant<bool, true>;
+    using F = std::integral_constant<bool, false>;
+    if (nslices > 0) {
+      phase_a(0, F{}, T{});
+      for (int k = 1; k < nslices; ++k) phase_a(k, T{}, T{});
+      phase_a(nslices, T{}, F{});
+    }
+    (void)hq;
+  } else {
+    // ---------------- role B: dP, dS (P from LDS), dK
+    f32x16 dpk = f32x16{};
+    auto phase_b = [&](int k, auto has_prev, auto has_cur) __attribute__((always_inline)) {
+      phase_begin(k);
+      if constexpr (decltype(has_prev)::value) {
+        const int kp = k - 1, rs = kp & 1;
+        const EA_LDS float* dst_ = (const EA_LDS float*)rowstat[(kp >> 1) % NSTAGE][1];
+        const EA_LDS f32x4* xp = (const EA_LDS f32x4*)pxch[kp & 1][pr];
+        float y[16];
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const f32x4 d4 = lds_load<f32x4>(dst_ + 32 * rs + 8 * i4 + 4 * hh);
+          const f32x4 p4 = lds_load<f32x4>(xp + 64 * i4 + lane);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[4 * i4 + e] = p4[e] * (dpk[4 * i4 + e] - d4[e]);
+        }
+        bf16x8 yb[2];
+        pack16(y, yb);
+        second_product(kp, stage_of(kp), yb);  // Q^T dS
+      }
+      if constexpr (decltype(has_cur)::value) dpk = first_product(k, stage_of(k) + TILE);  // dP = dO V^T
+      phase_end(k);
+    };
+    using T = std::integral_constant<bool, true>;
+    using F = std::integral_constant<bool, false>;
+    if (nslices > 0) {
+      phase_b(0, F{}, T{});
+      for (int k = 1; k < nslices; ++k) phase_b(k, T{}, T{});
+      phase_b(nslices, T{}, F{});
+    }
   }
 
-  // dK = scale * acc, dV = acc: keys in lanes, d in elements
+  // no DMA may still be writing this workgroup's LDS when it exits
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // dV = acc (role A), dK = scale * acc (role B): keys in lanes, d in elements
   if (kj < lk) {
-    const size_t ro = (k0 + kj) * kstride + (size_t)hk * D;
+    uint16_t* dst = (role_b ? a.dk : a.dv) + (k0 + kj) * kstride + (size_t)hk * D;
+    const float f = role_b ? a.scale : 1.0f;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d0 = 32 * dt + 8 * g4 + 4 * hh;
-        uint2 kv, vv;
-        kv.x = pack_bf16x2(dk[dt][4 * g4] * a.scale, dk[dt][4 * g4 + 1] * a.scale);
-        kv.y = pack_bf16x2(dk[dt][4 * g4 + 2] * a.scale, dk[dt][4 * g4 + 3] * a.scale);
-        vv.x = pack_bf16x2(dv[dt][4 * g4], dv[dt][4 * g4 + 1]);
-        vv.y = pack_bf16x2(dv[dt][4 * g4 + 2], dv[dt][4 * g4 + 3]);
-        *(uint2*)(a.dk + ro + d0) = kv;
-        *(uint2*)(a.dv + ro + d0) = vv;
+        uint2 val;
+        val.x = pack_bf16x2(acc[dt][4 * g4] * f, acc[dt][4 * g4 + 1] * f);
+        val.y = pack_bf16x2(acc[dt][4 * g4 + 2] * f, acc[dt][4 * g4 + 3] * f);
+        *(uint2*)(dst + d0) = val;
       }
     }
   }
@@ -472,7 +564,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int gk = 8 * ((a.B * a.Hkv + 7) / 8) * a.n_kb;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(gk), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(gk), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

@@ -19,6 +19,12 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Waits for this wave's LDS accesses (and scalar loads) only: lgkmcnt = 0,
+// vmcnt and expcnt left at their maxima.
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
+}
+
 // Workgroup barrier that neither the compiler nor the scheduler moves memory
 // operations across, and that adds no wait of its own (a __syncthreads would
 // also wait for the DMA still in flight).
