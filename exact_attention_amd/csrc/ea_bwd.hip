@@ -337,16 +337,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   TileDma<D, BQ, 8> dma;
   dma.init(w, lane, qstride);
   constexpr int kDmaOps = 2 * TileDma<D, BQ, 8>::PPW;  // vector memory ops per wave per tile
-  auto tile_of = [&](int t, int& hq, int& qt) {
-    hq = hk * a.group + t / nqt;
-    qt = qt0 + t % nqt;
-  };
+  // tiles are issued in order; the next one's (head, row block, stage) advance
+  // incrementally (no divisions in the loop)
+  int iss_t = 0, iss_hq = hk * a.group, iss_qt = qt0, iss_st = 0;
+  auto next_stage = [](int st) { return st == NSTAGE - 1 ? 0 : st + 1; };
   // wave 0 also loads the tile's row statistics (two more vector memory ops)
   float st_lse[2] = {0.f, 0.f}, st_d[2] = {0.f, 0.f};
-  auto issue = [&](int t) {
-    int hq, qt;
-    tile_of(t, hq, qt);
-    EA_LDS uint16_t* qs = sm + (t % NSTAGE) * 2 * TILE;
+  auto issue_next = [&]() {
+    const int t = iss_t, hq = iss_hq, qt = iss_qt;
+    EA_LDS uint16_t* qs = sm + iss_st * 2 * TILE;
     const int rows = min(lq - qt * BQ, BQ);
     const size_t go = (q0 + (size_t)qt * BQ) * qstride + (size_t)hq * D;
     dma.issue(qs, a.q + go, rows, qstride, w);
@@ -357,11 +356,18 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
       st_lse[t & 1] = row < lq ? a.lse2[idx] : __builtin_inff();  // rows past the end: P = 0
       st_d[t & 1] = row < lq ? a.dd[idx] : 0.f;
     }
+    ++iss_t;
+    iss_st = next_stage(iss_st);
+    if (++iss_qt == qt0 + nqt) {
+      iss_qt = qt0;
+      ++iss_hq;
+    }
   };
-  auto park_stats = [&](int t) {
+  // tile t's statistics into its stage st
+  auto park_stats = [&](int t, int st) {
     if (w == 0) {
-      lds_store<float>((EA_LDS float*)rowstat[t % NSTAGE][0] + lane, st_lse[t & 1]);
-      lds_store<float>((EA_LDS float*)rowstat[t % NSTAGE][1] + lane, st_d[t & 1]);
+      lds_store<float>((EA_LDS float*)rowstat[st][0] + lane, st_lse[t & 1]);
+      lds_store<float>((EA_LDS float*)rowstat[st][1] + lane, st_d[t & 1]);
     }
   };
 
@@ -382,18 +388,24 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x16{};
 
-  if (ntiles > 0) issue(0);
-  if (ntiles > 1) issue(1);
+  if (ntiles > 0) issue_next();
+  if (ntiles > 1) issue_next();
   __builtin_amdgcn_s_waitcnt(0);
-  if (ntiles > 0) park_stats(0);
-  if (ntiles > 1) park_stats(1);
+  if (ntiles > 0) park_stats(0, 0);
+  if (ntiles > 1) park_stats(1, 1);
   __syncthreads();
 
+  // stages of the current slice's tile and of the previous tile
+  int st_cur = 0, st_prev = NSTAGE - 1;
   // phase k opens by issuing tile k / 2 + 2 on the second slice of tile k / 2
   // (its stage was freed by the barrier that ended phase k - 1, the last one
-  // tile k / 2 - 1 used)
+  // tile k / 2 - 1 used); the first slice of a tile moves the stages on
   auto phase_begin = [&](int k) __attribute__((always_inline)) {
-    if ((k & 1) && (k >> 1) + 2 < ntiles) issue((k >> 1) + 2);
+    if ((k & 1) && iss_t < ntiles) issue_next();
+    if (!(k & 1) && k > 0) {
+      st_prev = st_cur;
+      st_cur = next_stage(st_cur);
+    }
   };
   // phase k closes: P stores done; before the first phase of tile u =
   // (k + 1) / 2 >= 2 its DMA (issued at phase 2u - 3) has landed -- only tile
@@ -407,7 +419,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
       } else {
         __builtin_amdgcn_s_waitcnt(0);
       }
-      park_stats(u);
+      park_stats(u, next_stage(st_cur));
       wait_lgkm0();
     }
     pp_barrier();
@@ -450,7 +462,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
       yb[st] = __builtin_bit_cast(bf16x8, t);
     }
   };
-  auto stage_of = [&](int k) { return sm + ((k >> 1) % NSTAGE) * 2 * TILE; };
+  // LDS tile of slice k (the current one) or of slice k - 1 (deferred product)
+  auto stage_cur = [&]() { return sm + st_cur * 2 * TILE; };
+  auto stage_prev_slice = [&](int k) { return sm + ((k & 1) ? st_cur : st_prev) * 2 * TILE; };
 
   // The phases are straight-line code: a slice that causal masking hides from
   // the pair still runs its products (P = 0 there, so they add exact zeros).
@@ -460,13 +474,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
     int hq = hk * a.group, qt = qt0;  // tile of the current slice
     auto phase_a = [&](int k, auto has_prev, auto has_cur) __attribute__((always_inline)) {
       phase_begin(k);
-      if constexpr (decltype(has_prev)::value) second_product(k - 1, stage_of(k - 1) + TILE, pk);  // dO^T P
+      if constexpr (decltype(has_prev)::value) second_product(k - 1, stage_prev_slice(k) + TILE, pk);  // dO^T P
       if constexpr (decltype(has_cur)::value) {
-        const EA_LDS uint16_t* qs = stage_of(k);
+        const EA_LDS uint16_t* qs = stage_cur();
         const f32x16 x = first_product(k, qs);  // S = Q K^T
         const int rs = k & 1;
         const int rbase = qt * BQ + 32 * rs;
-        const EA_LDS float* lst = (const EA_LDS float*)rowstat[(k >> 1) % NSTAGE][0];
+        const EA_LDS float* lst = (const EA_LDS float*)rowstat[st_cur][0];
         EA_LDS f32x4* xp = (EA_LDS f32x4*)pxch[k & 1][pr];
         float p[16];
         // element i = row rbase + 8 (i / 4) + 4 hh + i % 4 of key kj
@@ -506,7 +520,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
       phase_begin(k);
       if constexpr (decltype(has_prev)::value) {
         const int kp = k - 1, rs = kp & 1;
-        const EA_LDS float* dst_ = (const EA_LDS float*)rowstat[(kp >> 1) % NSTAGE][1];
+        const EA_LDS float* dst_ = (const EA_LDS float*)rowstat[(k & 1) ? st_cur : st_prev][1];
         const EA_LDS f32x4* xp = (const EA_LDS f32x4*)pxch[kp & 1][pr];
         float y[16];
 #pragma unroll
@@ -518,9 +532,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
         }
         bf16x8 yb[2];
         pack16(y, yb);
-        second_product(kp, stage_of(kp), yb);  // Q^T dS
+        second_product(kp, stage_prev_slice(k), yb);  // Q^T dS
       }
-      if constexpr (decltype(has_cur)::value) dpk = first_product(k, stage_of(k) + TILE);  // dP = dO V^T
+      if constexpr (decltype(has_cur)::value) dpk = first_product(k, stage_cur() + TILE);  // dP = dO V^T
       phase_end(k);
     };
     using T = std::integral_constant<bool, true>;
