@@ -62,6 +62,8 @@ def parse():
     p.add_argument("--no-gemm-calibration", action="store_true",
                    help="skip the vendor-GEMM rate measured after the timed region")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle time budget per leg")
+    p.add_argument("--prefill-kernel", type=int, default=0,
+                   help="forward kernel for the bf16 prefill (EA_FWD_KERNEL_*; 0 = library default)")
     p.add_argument("--prefill-dims", choices=["128,128", "192,128"], default="128,128",
                    help="head dims (d_qk, d_v) of the bf16 prefill forward")
     p.add_argument("--fp8-format", choices=["e4m3", "e5m2"], default="e4m3",
@@ -231,7 +233,7 @@ def main():
         o = torch.empty_like(q) if d_v == d_qk else torch.empty(q.shape[:3] + (d_v,), dtype=q.dtype, device=dev)
         B, N, H, d = inp.q.shape
         lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-        tun = ea.tuning(exp_mode=args.exp_mode)
+        tun = ea.tuning(exp_mode=args.exp_mode, kernel=args.prefill_kernel)
     if run_decode:
         pg = W.paged_decode_device(dev)
         if args.decode_page_size != 16:
@@ -317,7 +319,7 @@ def main():
     pf_dims = "d=128" if args.prefill_dims == "128,128" else f"(d_qk,d_v)=({args.prefill_dims})"
     cfg = {"workload": f"prefill fwd B=4 H=16 N=8192 {pf_dims} causal bf16 + paged decode B=64 Hq=32 Hkv=8 "
                        f"d=128 ctx U[512,32768] page {args.decode_page_size} bf16 (split-KV + LSE combine)",
-           "exp_mode": args.exp_mode, "input_gen_s": round(t_gen, 1)}
+           "exp_mode": args.exp_mode, "prefill_kernel": args.prefill_kernel, "input_gen_s": round(t_gen, 1)}
     if run_prefill:
         t_pf = np.array([e[0].elapsed_time(e[1]) for e in evs])      # ms
         flops = prefill_flops(B, H, N, d, d_v)
@@ -329,8 +331,9 @@ def main():
         out["roofline"] = {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                            "frac": tf / PEAK_BF16_TFLOPS,
                            "traffic": TRAFFIC_PREFILL if d_v == d == 128 else None,
-                           "kernel": "ea::fwd_pp_kernel<128, 128, causal>" if d_v == d else
-                                     f"ea::fwd_pp_kernel<{d}, {d_v}, causal>"}
+                           "kernel": ("ea::fwd_pp_persistent_kernel" if args.prefill_kernel in (0, 4) else
+                                      "ea::fwd_pp_kernel" if args.prefill_kernel == 2 else
+                                      f"forward kernel {args.prefill_kernel}") + f"<{d}, {d_v}, causal>"}
     if run_decode:
         t_dc = np.array([e[2].elapsed_time(e[3]) for e in evs])
         nbytes = decode_bytes(pg.seq_lens, Hq, Hkv, dd, pg.page_size)

@@ -43,9 +43,11 @@
 
 namespace ea {
 
+// One work tile (256 query rows of one (sequence, head)): the whole forward of
+// those rows. xcd and j locate the tile in the XCD-grouped, heaviest-first order.
 // D: head dim of Q and K; DV: head dim of V and O (equal, or 192 / 128).
 template <int D, int DV, bool CAUSAL, bool VARLEN, int EXPMODE>
-__global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
+__device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) {
   constexpr int BM = kPpBlockM, BN = kFwdBlockN;
   constexpr int TILE = BN * D;               // bf16 elements per K stage
   constexpr int VTILE = BN * DV;             // ... per V stage
@@ -62,8 +64,6 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t vs0[VTILE], vs1[VTILE], vs2[VTILE];
 
   // ---------------- tile assignment (XCD-grouped, heaviest first)
-  const int xcd = blockIdx.x & 7;
-  int j = blockIdx.x >> 3;
   int seq, h, mb;
   const int ngroups = a.nseq * a.Hq;
   if constexpr (!VARLEN) {
@@ -396,8 +396,41 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
 }
 
 template <int D, int DV, bool CAUSAL, bool VARLEN, int EXPMODE>
+__global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
+  pp_tile<D, DV, CAUSAL, VARLEN, EXPMODE>(a, blockIdx.x & 7, blockIdx.x >> 3);
+}
+
+// Persistent form: one workgroup per CU walks its XCD's tile list. Launching a
+// new workgroup on a CU that just retired one takes ~11 us on this GPU (about
+// 8% of a prefill forward that runs eight workgroups per CU); a persistent
+// workgroup goes straight to its next tile. The hardware's dynamic dispatch
+// balanced the heaviest-first list by itself; a static assignment must keep
+// that balance, so workgroup i of an XCD with W workgroups takes, in round r,
+// list entry r W + i for even r and r W + W - 1 - i for odd r (snake order):
+// the heaviest row block of one (sequence, head) pairs with the lightest of
+// the next.
+template <int D, int DV, bool CAUSAL, bool VARLEN, int EXPMODE>
+__global__ __launch_bounds__(512, 1) void fwd_pp_persistent_kernel(FwdArgs a) {
+  const int xcd = blockIdx.x & 7, i = blockIdx.x >> 3, W = gridDim.x >> 3;
+  const int per_xcd = uniform(a.tiles_per_xcd);
+  for (int r = 0; r * W < per_xcd; ++r) {
+    const int jj = r * W + ((r & 1) ? W - 1 - i : i);
+    if (jj < per_xcd) pp_tile<D, DV, CAUSAL, VARLEN, EXPMODE>(a, xcd, jj);
+  }
+}
+
+template <int D, int DV, bool CAUSAL, bool VARLEN, int EXPMODE>
 static hipError_t launch_pp_t(const FwdArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((fwd_pp_kernel<D, DV, CAUSAL, VARLEN, EXPMODE>), dim3(fwd_grid(a, VARLEN)), dim3(512), 0, s, a);
+  const int grid = fwd_grid(a, VARLEN);
+  if (a.persist_wgs > 0) {
+    FwdArgs b = a;
+    b.tiles_per_xcd = grid / 8;
+    const int w = min(a.persist_wgs / 8, b.tiles_per_xcd);  // workgroups per XCD
+    hipLaunchKernelGGL((fwd_pp_persistent_kernel<D, DV, CAUSAL, VARLEN, EXPMODE>), dim3(8 * max(w, 1)), dim3(512), 0,
+                       s, b);
+  } else {
+    hipLaunchKernelGGL((fwd_pp_kernel<D, DV, CAUSAL, VARLEN, EXPMODE>), dim3(grid), dim3(512), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -23,6 +23,9 @@ struct FwdArgs {
   float tau;           // lazy-rescale threshold in log2 units
   int natural;         // 1: ascending row-block order
   const int* seq_order;  // packed only: virtual -> actual sequence, or null (input order)
+  int persist_wgs;     // ping-pong kernel: > 0 runs the persistent form with this many
+                       // workgroups (a multiple of 8, one per CU); 0: one workgroup per tile
+  int tiles_per_xcd;   // set by the launcher for the persistent form
 };
 
 constexpr int kFwdBlockM = 128;  // query rows per workgroup (4 waves x 32)

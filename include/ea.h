@@ -74,18 +74,25 @@ typedef struct {
 } ea_fwd_tuning;
 
 /* Forward kernels (same results up to rounding order):
- *   EA_FWD_KERNEL_AUTO      the ping-pong kernel for d = 128, else the 4-wave one
+ *   EA_FWD_KERNEL_AUTO      for d = 128 the ping-pong kernel, in persistent form
+ *                           for dense inputs; else the 4-wave one
  *   EA_FWD_KERNEL_4WAVE     4 waves x 32 query rows, two workgroups per CU
  *   EA_FWD_KERNEL_PINGPONG  8 waves x 32 rows in two groups that alternate
  *                           matrix products and softmax on each SIMD
  *   EA_FWD_KERNEL_PIPELINED 8 waves x 32 rows, each wave overlapping the
  *                           softmax of one tile with its own matrix products
- *                           of the next and previous tiles */
+ *                           of the next and previous tiles
+ *   EA_FWD_KERNEL_PERSISTENT the ping-pong kernel in persistent form: one
+ *                           workgroup per CU walks a static, load-balanced
+ *                           list of row blocks instead of one workgroup per
+ *                           row block (the pages' persistent tile scheduler,
+ *                           "FlashAttention4 close reading", section 3.3) */
 enum {
   EA_FWD_KERNEL_AUTO = 0,
   EA_FWD_KERNEL_4WAVE = 1,
   EA_FWD_KERNEL_PINGPONG = 2,
-  EA_FWD_KERNEL_PIPELINED = 3
+  EA_FWD_KERNEL_PIPELINED = 3,
+  EA_FWD_KERNEL_PERSISTENT = 4
 };
 
 /* Default tuning values. */
@@ -117,8 +124,8 @@ ea_status ea_attn_fwd_tuned(const void* q, const void* k, const void* v, void* o
  * the last being the non-standard pair "FlashAttention-4: algorithm-pipeline
  * co-design for Blackwell" (kernel-level performance section) benchmarks for
  * the DeepSeek V3 architecture; other pairs return EA_ERR_UNSUPPORTED.
- * (192, 128) runs on the ping-pong kernel only (tuning->kernel AUTO or
- * PINGPONG). The usual scale is 1/sqrt(d_qk).
+ * (192, 128) runs on the ping-pong kernel only (tuning->kernel AUTO,
+ * PINGPONG or PERSISTENT). The usual scale is 1/sqrt(d_qk).
  */
 ea_status ea_attn_fwd_hd(const void* q, const void* k, const void* v, void* o, float* lse,
                          int B, int Nq, int Nk, int Hq, int Hkv, int d_qk, int d_v, int causal,
@@ -198,8 +205,8 @@ ea_status ea_attn_fwd_mx8(const void* q8, const void* k8, const void* v8,
  * ea_attn_fwd_mx8_tuned -- ea_attn_fwd_mx8 with forward tuning (NULL = the
  * defaults). tuning->kernel selects EA_FWD_KERNEL_4WAVE or
  * EA_FWD_KERNEL_PIPELINED (AUTO: the pipelined one); EA_FWD_KERNEL_PINGPONG,
- * exp_mode other than EA_EXP_HW and natural_order = 1 return
- * EA_ERR_UNSUPPORTED. rescale_log2 is the lazy-rescale threshold, which also
+ * EA_FWD_KERNEL_PERSISTENT, exp_mode other than EA_EXP_HW and
+ * natural_order = 1 return EA_ERR_UNSUPPORTED. rescale_log2 is the lazy-rescale threshold, which also
  * bounds P before its e4m3 rounding (P <= 2^rescale_log2, so values above 8
  * can overflow e4m3's 448).
  */

@@ -66,7 +66,7 @@ def test_fwd_head_dim_pair_errors(lib):
     assert g(P, P, P, P, None, 1, 8, 8, 2, 2, 128, 64, 0, 0.1, None, None) == -2
     assert g(P, P, P, P, None, 1, 8, 8, 2, 2, 192, 0, 0, 0.1, None, None) == -1
     assert g(None, P, P, P, None, 1, 8, 8, 2, 2, 192, 128, 0, 0.1, None, None) == -1
-    for kern in (1, 3):                                   # (192, 128): ping-pong kernel only
+    for kern in (1, 3):                                   # (192, 128): ping-pong kernel (or its persistent form) only
         t = ea.tuning(kernel=kern)
         assert g(P, P, P, P, None, 1, 8, 8, 2, 2, 192, 128, 0, 0.1, ctypes.byref(t), None) == -2
     assert lib.ea_attn_fwd(P, P, P, P, None, 1, 8, 8, 2, 2, 192, 0, 0.1, None) == -2   # needs the _hd entry
@@ -78,7 +78,7 @@ def test_tuning_errors(lib):
     assert lib.ea_attn_fwd_tuned(P, P, P, P, None, 1, 8, 8, 2, 2, 128, 0, 0.1, ctypes.byref(t), None) == -1
     t = ea.tuning(rescale_log2=-1.0)
     assert lib.ea_attn_fwd_tuned(P, P, P, P, None, 1, 8, 8, 2, 2, 128, 0, 0.1, ctypes.byref(t), None) == -1
-    t = ea.tuning(kernel=4)
+    t = ea.tuning(kernel=5)
     assert lib.ea_attn_fwd_tuned(P, P, P, P, None, 1, 8, 8, 2, 2, 128, 0, 0.1, ctypes.byref(t), None) == -1
     d = ea.default_tuning()
     assert d.exp_mode == 0 and d.rescale_log2 == 8.0 and d.natural_order == 0 and d.kernel == 0
@@ -112,7 +112,8 @@ def test_mx8_tuning_errors(lib):
     assert call(ea.tuning(kernel=2)) == -2      # no ping-pong fp8 kernel
     assert call(ea.tuning(exp_mode=1)) == -2    # hardware exponential only
     assert call(ea.tuning(natural_order=1)) == -2
-    assert call(ea.tuning(kernel=4)) == -1
+    assert call(ea.tuning(kernel=4)) == -2      # no persistent fp8 kernel
+    assert call(ea.tuning(kernel=5)) == -1
 
 
 def test_decode_argument_errors(lib):

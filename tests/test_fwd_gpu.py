@@ -54,8 +54,9 @@ SHAPES = [
 ]
 
 
-# 1: the 4-wave kernel, 2: the 8-wave ping-pong kernel (each against the oracle)
-KERNELS = [1, 2, 3]
+# 1: the 4-wave kernel, 2: the 8-wave ping-pong kernel, 3: the pipelined
+# kernel, 4: the ping-pong kernel in persistent form (each against the oracle)
+KERNELS = [1, 2, 3, 4]
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
@@ -251,3 +252,33 @@ def test_head_dims_192_128_prefill_sampled():
     assert np.isfinite(o).all() and np.isfinite(lse).all()
     o2, l2 = run_dense(inp, tuning=ea.tuning(natural_order=1))
     assert np.array_equal(o, o2) and np.array_equal(lse, l2)
+
+
+def test_persistent_bitwise_equals_per_tile_launch():
+    """The persistent form runs the same per-tile arithmetic as the ping-pong
+    kernel launched once per tile, so the outputs match bit for bit; shapes with
+    fewer tiles than workgroups, more tiles than one round, causal and not,
+    GQA, and (192, 128)."""
+    import exact_attention_amd as ea
+    cases = [((1, 300, 300, 2, 2, 128, True), None), ((2, 4096, 4096, 8, 4, 128, True), None),
+             ((1, 2000, 2000, 16, 16, 128, False), None), ((2, 1000, 1000, 4, 4, 192, True), 128)]
+    for (B, Nq, Nk, Hq, Hkv, d, causal), dv in cases:
+        inp = W.dense(B, Nq, Nk, Hq, Hkv, d, causal, seed=600 + Nq + Hq, dv=dv)
+        o2, l2 = run_dense(inp, tuning=ea.tuning(kernel=2))
+        o4, l4 = run_dense(inp, tuning=ea.tuning(kernel=4))
+        log(f"persistent vs per-tile {B, Nq, Nk, Hq, Hkv, d, dv, causal}: equal={np.array_equal(o2, o4)}")
+        assert np.array_equal(o2, o4) and np.array_equal(l2, l4)
+
+
+def test_persistent_prefill_workload_sampled():
+    import exact_attention_amd as ea
+    inp = W.prefill(True)
+    o, lse = run_dense(inp, tuning=ea.tuning(kernel=4))
+    B, N, H, d = inp.q.shape
+    rng = np.random.default_rng(25)
+    rows = _sample_rows(N, rng)
+    for (b, h) in [(0, 0), (B - 1, H - 1), (2, 9)]:
+        ro, rl = _rows(inp, b, h, rows)
+        assert_o_close(o[b, rows, h, :], ro, what=f"o[b={b},h={h}]")
+        assert_lse_close(lse[b, h, rows], rl, what=f"lse[b={b},h={h}]")
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
