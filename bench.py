@@ -25,6 +25,7 @@ against beside the published peak.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -41,11 +42,20 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 # HBM bytes per launch measured by rocprofv3 (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0,
-# the factors a plain 1 GiB copy reads); None until measured for the current
-# kernels. Sources: profiles/*_counters.md.
-TRAFFIC_PREFILL = 618_255_360    # fwd_pp_kernel<128, 128, causal>: 234,836 KiB fetched, 134,093 KiB written
-TRAFFIC_DECODE = 4_866_191_360   # decode_split_kernel<true> + combine: 2,373,166 KiB fetched, 5,807 KiB written
-TRAFFIC_FP8 = 492_166_827        # fwd_mx8_sp_kernel<causal, e4m3>: 173,648 KiB fetched, 133,336 KiB written
+# the factors a plain 1 GiB copy reads), keyed by the kernel they were taken
+# on; a kernel not listed reports traffic null. Sources: profiles/*_counters.md.
+TRAFFIC = {
+    # fwd_pp_persistent_kernel<128, 128, causal>: 215,978 KiB fetched, 134,439 KiB written
+    "ea::fwd_pp_persistent_kernel<128, 128, causal>": 579_988_480,
+    # fwd_pp_kernel<128, 128, causal>: 234,836 KiB fetched, 134,093 KiB written
+    "ea::fwd_pp_kernel<128, 128, causal>": 618_255_360,
+    # fwd_mx8_sp_persistent_kernel<causal, e4m3>: 165,417 KiB fetched, 137,416 KiB written
+    "ea::fwd_mx8_sp_persistent_kernel<causal, e4m3>": 479_488_000,
+    # decode_split_kernel<true> + combine: 2,373,166 KiB fetched, 5,807 KiB written
+    "ea::decode_split_kernel<page16> + ea::decode_combine_kernel": 4_866_191_360,
+    # fwd_mx8_sp_kernel<causal, e4m3>: 173,648 KiB fetched, 133,336 KiB written
+    "ea::fwd_mx8_sp_kernel<causal, e4m3>": 492_166_827,
+}
 
 
 def parse():
@@ -66,6 +76,8 @@ def parse():
                    help="forward kernel for the bf16 prefill (EA_FWD_KERNEL_*; 0 = library default)")
     p.add_argument("--prefill-dims", choices=["128,128", "192,128"], default="128,128",
                    help="head dims (d_qk, d_v) of the bf16 prefill forward")
+    p.add_argument("--fp8-kernel", type=int, default=0, help="fp8 forward kernel (EA_FWD_KERNEL_*; 0 = default)")
+    p.add_argument("--bwd-schedule", type=int, default=0, help="backward schedule (EA_BWD_SCHEDULE_*; 0 = default)")
     p.add_argument("--fp8-format", choices=["e4m3", "e5m2"], default="e4m3",
                    help="element format of the fp8 forward's MX inputs")
     p.add_argument("--decode-page-size", type=int, choices=[1, 2, 4, 8, 16], default=16,
@@ -270,6 +282,7 @@ def main():
               for x in (m8.q8, m8.k8, m8.v8, m8.q_scale, m8.k_scale, m8.v_scale)]
         B8, N8, H8, d8 = m8.q8.shape
         o8 = torch.empty((B8, N8, H8, d8), dtype=torch.bfloat16, device=dev)
+        tun8 = ea.tuning(kernel=args.fp8_kernel)
         lse8 = torch.empty((B8, H8, N8), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     t_gen = time.perf_counter() - t_gen
@@ -277,10 +290,11 @@ def main():
     def step(i, ev):
         if run_bwd:
             ev[6].record(stream)
-            r = ea.lib().ea_attn_bwd(ea._ptr(bq), ea._ptr(bk), ea._ptr(bv), ea._ptr(bo), ea._ptr(bdo), ea._ptr(blse),
-                                     ea._ptr(bdq), ea._ptr(bdk), ea._ptr(bdv), bB, bN, bN, bH, bH, bd, 1, bin_.scale,
-                                     ea._ptr(bws), bws.numel(), stream.cuda_stream)
-            ea._check(r, "ea_attn_bwd")
+            r = ea.lib().ea_attn_bwd_ex(ea._ptr(bq), ea._ptr(bk), ea._ptr(bv), ea._ptr(bo), ea._ptr(bdo),
+                                        ea._ptr(blse), ea._ptr(bdq), ea._ptr(bdk), ea._ptr(bdv), bB, bN, bN, bH, bH, bd,
+                                        1, bin_.scale, args.bwd_schedule, ea._ptr(bws), bws.numel(),
+                                        stream.cuda_stream)
+            ea._check(r, "ea_attn_bwd_ex")
             ev[7].record(stream)
         if run_prefill:
             ev[0].record(stream)
@@ -298,7 +312,8 @@ def main():
         if run_fp8:
             ev[4].record(stream)
             r = ea.lib().ea_attn_fwd_mx8_fmt(*[ea._ptr(x) for x in t8], ea._ptr(o8), ea._ptr(lse8), B8, N8, H8, H8,
-                                            d8, 1, m8.scale, ea.FP8_FORMATS[m8.fmt], None, stream.cuda_stream)
+                                            d8, 1, m8.scale, ea.FP8_FORMATS[m8.fmt], ctypes.byref(tun8),
+                                            stream.cuda_stream)
             ea._check(r, "ea_attn_fwd_mx8_fmt")
             ev[5].record(stream)
 
@@ -330,10 +345,12 @@ def main():
                           "tflops_best": flops / (t_pf.min() * 1e-3) / 1e12, "flop_per_launch": flops}
         out["roofline"] = {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                            "frac": tf / PEAK_BF16_TFLOPS,
-                           "traffic": TRAFFIC_PREFILL if d_v == d == 128 else None,
-                           "kernel": ("ea::fwd_pp_persistent_kernel" if args.prefill_kernel in (0, 4) else
-                                      "ea::fwd_pp_kernel" if args.prefill_kernel == 2 else
+                           "kernel": ("ea::fwd_pp_unrollkv_kernel" if args.prefill_kernel == 5 else
+                                      "ea::fwd_pp_persistent_kernel"
+                                      if args.prefill_kernel == 4 or (args.prefill_kernel == 0 and d == d_v == 128) else
+                                      "ea::fwd_pp_kernel" if args.prefill_kernel == 2 or d != d_v else
                                       f"forward kernel {args.prefill_kernel}") + f"<{d}, {d_v}, causal>"}
+        out["roofline"]["traffic"] = TRAFFIC.get(out["roofline"]["kernel"])
     if run_decode:
         t_dc = np.array([e[2].elapsed_time(e[3]) for e in evs])
         nbytes = decode_bytes(pg.seq_lens, Hq, Hkv, dd, pg.page_size)
@@ -342,9 +359,11 @@ def main():
                          "bytes_per_launch": nbytes, "gbs_best": nbytes / (t_dc.min() * 1e-3) / 1e9}
         out["roofline_decode"] = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                   "frac": gbs / PEAK_HBM_GBS,
-                                  "traffic": TRAFFIC_DECODE if pg.page_size == 16 else None,
-                                  "kernel": f"ea::decode_split_kernel<{'true' if pg.page_size % 16 == 0 else 'false'}>"
-                                            " + decode_combine_kernel"}
+                                  "kernel": f"ea::decode_split_kernel<{'page16' if pg.page_size % 16 == 0 else 'any'}>"
+                                            " + ea::decode_combine_kernel"}
+        # the counters were taken at page size 16
+        out["roofline_decode"]["traffic"] = (TRAFFIC.get(out["roofline_decode"]["kernel"])
+                                             if pg.page_size == 16 else None)
         if not run_prefill:
             out["value"], out["unit"] = gbs, "GB/s"
     if run_fp8:
@@ -356,8 +375,12 @@ def main():
         if run_prefill:
             out["fp8"]["ratio_to_bf16"] = tf8 / out["value"]
         out["roofline_fp8"] = {"bound": "mfma", "achieved": tf8, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                               "frac": tf8 / PEAK_FP8_TFLOPS, "traffic": TRAFFIC_FP8 if m8.fmt == "e4m3" else None,
-                               "kernel": f"ea::fwd_mx8_sp_kernel<causal, {m8.fmt}>"}
+                               "frac": tf8 / PEAK_FP8_TFLOPS,
+                               "kernel": {0: "ea::fwd_mx8_sp_persistent_kernel", 4: "ea::fwd_mx8_sp_persistent_kernel",
+                                          3: "ea::fwd_mx8_sp_kernel", 1: "ea::fwd_mx8_kernel"}.get(
+                                              args.fp8_kernel, f"fp8 kernel {args.fp8_kernel}")
+                                         + f"<causal, {m8.fmt}>"}
+        out["roofline_fp8"]["traffic"] = TRAFFIC.get(out["roofline_fp8"]["kernel"])
         if not (run_prefill or run_decode):
             out["value"], out["unit"], out["dtype"] = tf8, "TFLOP/s", f"fp8_{m8.fmt}"
     if run_bwd:
@@ -369,7 +392,9 @@ def main():
         out["bwd"] = {"value": tfb, "unit": "TFLOP/s", "ms_mean": float(t_bw.mean()), "ms_min": float(t_bw.min()),
                       "flop_per_launch": flops_b, "workload": "B=4 H=16 N=8192 d=128 causal bf16 (dQ, dK, dV)",
                       "flop_convention": "5 products x 2 N^2 d, causal half; the kernels compute 7 (S and dP twice)",
-                      "kernels": "ea::bwd_prep_kernel + ea::bwd_dq_kernel + ea::bwd_dkdv_kernel",
+                      "kernels": ("ea::bwd_prep_kernel + ea::bwd_dq_persistent_kernel + ea::bwd_dkdv_persistent_kernel"
+                                  if args.bwd_schedule == 2 else
+                                  "ea::bwd_prep_kernel + ea::bwd_dq_kernel + ea::bwd_dkdv_kernel"),
                       "frac_of_peak": tfb / PEAK_BF16_TFLOPS}
         if not (run_prefill or run_decode or run_fp8):
             out["value"], out["unit"] = tfb, "TFLOP/s"

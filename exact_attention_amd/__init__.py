@@ -54,6 +54,7 @@ _SIGNATURES = {
                             _c_int),
     "ea_attn_bwd_workspace_size": ([_c_int] * 3, _c_size_t),
     "ea_attn_bwd": ([_c_void_p] * 9 + [_c_int] * 7 + [_c_float, _c_void_p, _c_size_t, _c_void_p], _c_int),
+    "ea_attn_bwd_ex": ([_c_void_p] * 9 + [_c_int] * 7 + [_c_float, _c_int, _c_void_p, _c_size_t, _c_void_p], _c_int),
     "ea_decode_workspace_size": ([_c_int] * 7, _c_size_t),
     "ea_attn_decode_paged": ([_c_void_p] * 7 + [_c_int] * 7 + [_c_float, _c_int, _c_void_p, _c_size_t, _c_void_p], _c_int),
     "ea_test_exp2": ([_c_void_p, _c_void_p, _c_int, _c_int, _c_void_p], _c_int),
@@ -114,7 +115,8 @@ def default_tuning() -> FwdTuning:
 def tuning(exp_mode: int = EA_EXP_HW, rescale_log2: float = 8.0, natural_order: int = 0,
            kernel: int = 0) -> FwdTuning:
     """Forward tuning; kernel: 0 auto, 1 the 4-wave kernel, 2 the 8-wave ping-pong kernel,
-    3 the 8-wave software-pipelined kernel."""
+    3 the 8-wave software-pipelined kernel, 4 the ping-pong kernel in persistent form,
+    5 that persistent form with the K/V pipeline running on across row blocks (unroll-KV)."""
     return FwdTuning(exp_mode, rescale_log2, natural_order, kernel)
 
 
@@ -219,9 +221,10 @@ def attn_fwd_mx8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = True, sca
 
 
 def attn_bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None, *,
-             workspace: torch.Tensor | None = None):
+             workspace: torch.Tensor | None = None, schedule: int = 0):
     """Backward of attn_fwd. q, o, dout [B,Nq,Hq,d], k, v [B,Nk,Hkv,d] bf16;
-    lse [B,Hq,Nq] fp32 from the forward. Returns (dq, dk, dv) bf16."""
+    lse [B,Hq,Nq] fp32 from the forward. schedule: 0 library default, 1 one
+    workgroup per tile, 2 persistent. Returns (dq, dk, dv) bf16."""
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
         _need(t, n, torch.bfloat16, 4)
     _need(lse, "lse", torch.float32, 3)
@@ -237,9 +240,9 @@ def attn_bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = 
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    st = lib().ea_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
-                           B, Nq, Nk, Hq, Hkv, d, int(bool(causal)), float(scale), _ptr(workspace),
-                           workspace.numel() * workspace.element_size(), _stream(q))
+    st = lib().ea_attn_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                              _ptr(dv), B, Nq, Nk, Hq, Hkv, d, int(bool(causal)), float(scale), int(schedule),
+                              _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q))
     _check(st, "ea_attn_bwd")
     return dq, dk, dv
 

@@ -116,15 +116,13 @@ struct TileDma {
 // tiles of 64 in two LDS stages.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
+__device__ __forceinline__ void dq_tile(const BwdArgs& a, const int xcd, const int j) {
   constexpr int BM = 128, BN = kBwdTileK, NDT = D / 32;
   constexpr int TILE = BN * D;
   __shared__ __attribute__((aligned(1024))) uint16_t smem_raw[2 * 2 * TILE];
   EA_LDS uint16_t* sm = (EA_LDS uint16_t*)smem_raw;
 
   // XCD-grouped, heaviest first: all row blocks of one (sequence, head) on one XCD
-  const int xcd = blockIdx.x & 7;
-  const int j = blockIdx.x >> 3;
   const int kg = j / a.n_mb;
   const int r = j - kg * a.n_mb;
   const int g = xcd + 8 * kg;
@@ -271,6 +269,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   }
 }
 
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
+  dq_tile<D, CAUSAL>(a, blockIdx.x & 7, blockIdx.x >> 3);
+}
+// persistent form (persistent_snake in ea_fwd_common.h)
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void bwd_dq_persistent_kernel(BwdArgs a) {
+  persistent_snake(uniform(a.tiles_per_xcd), [&](int xcd, int j) { dq_tile<D, CAUSAL>(a, xcd, j); });
+}
+
+
 // ---------------------------------------------------------------------------
 // dK, dV: one workgroup = 8 waves for 128 keys of one (sequence, KV head); it
 // walks every query tile (64 rows, two 32-row slices) of every query head of
@@ -287,7 +296,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 // and each one's DMA is issued three phases before its first use.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
+__device__ __forceinline__ void dkdv_tile(const BwdArgs& a, const int xcd, const int j) {
   constexpr int BK = 128, BQ = kBwdTileQ, NDT = D / 32;
   constexpr int TILE = BQ * D;
   constexpr int NSTAGE = 3;
@@ -297,8 +306,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   EA_LDS uint16_t* sm = (EA_LDS uint16_t*)smem_raw;
 
   // XCD-grouped; causal: the key blocks with the most query rows (lowest) first
-  const int xcd = blockIdx.x & 7;
-  const int j = blockIdx.x >> 3;
   const int kg = j / a.n_kb;
   const int r = j - kg * a.n_kb;
   const int g = xcd + 8 * kg;
@@ -568,16 +575,41 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
 }
 
 template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
+  dkdv_tile<D, CAUSAL>(a, blockIdx.x & 7, blockIdx.x >> 3);
+}
+// persistent form (persistent_snake in ea_fwd_common.h)
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_persistent_kernel(BwdArgs a) {
+  persistent_snake(uniform(a.tiles_per_xcd), [&](int xcd, int j) { dkdv_tile<D, CAUSAL>(a, xcd, j); });
+}
+
+
+template <int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   const int rows = a.B * a.Nq * a.Hq;
   hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((rows + 15) / 16), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int gq = 8 * ((a.B * a.Hq + 7) / 8) * a.n_mb;
+  const int gk = 8 * ((a.B * a.Hkv + 7) / 8) * a.n_kb;
+  if (a.persist_wgs > 0) {
+    // persistent forms: the dQ kernel fits two workgroups per CU, the dK/dV
+    // kernel one
+    BwdArgs b = a;
+    b.tiles_per_xcd = gq / 8;
+    const int wq = max(1, min(2 * a.persist_wgs / 8, b.tiles_per_xcd));
+    hipLaunchKernelGGL((bwd_dq_persistent_kernel<D, CAUSAL>), dim3(8 * wq), dim3(256), 0, s, b);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    b.tiles_per_xcd = gk / 8;
+    const int wk = max(1, min(a.persist_wgs / 8, b.tiles_per_xcd));
+    hipLaunchKernelGGL((bwd_dkdv_persistent_kernel<D, CAUSAL>), dim3(8 * wk), dim3(512), 0, s, b);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(gq), dim3(256), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int gk = 8 * ((a.B * a.Hkv + 7) / 8) * a.n_kb;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(gk), dim3(512), 0, s, a);
   return hipGetLastError();
 }

@@ -53,6 +53,21 @@ __device__ __forceinline__ int launder(int x) {
   return x;
 }
 
+// the same for a wave-uniform value held in a scalar register
+__device__ __forceinline__ int launder_s(int x) {
+  asm volatile("" : "+s"(x));
+  return x;
+}
+
+__device__ __forceinline__ const uint16_t* launder_s(const uint16_t* p) {
+  asm volatile("" : "+s"(p));
+  return p;
+}
+__device__ __forceinline__ uint32_t launder_s(uint32_t x) {
+  asm volatile("" : "+s"(x));
+  return x;
+}
+
 // elements B .. B+7 of a score accumulator, rounded to bf16 and packed as an
 // MFMA operand
 template <int B>
@@ -60,6 +75,24 @@ __device__ __forceinline__ bf16x8 pack_p8(const f32x16 v) {
   const i32x4 t = {(int)pack_bf16x2(v[B + 0], v[B + 1]), (int)pack_bf16x2(v[B + 2], v[B + 3]),
                    (int)pack_bf16x2(v[B + 4], v[B + 5]), (int)pack_bf16x2(v[B + 6], v[B + 7])};
   return __builtin_bit_cast(bf16x8, t);
+}
+
+// Persistent workgroups: one per CU walks its share of an XCD-grouped work
+// list (entry j of XCD x is global tile 8 j + x, as in the one-tile-per-
+// workgroup launch). A new workgroup launch on a CU that just retired one
+// costs ~11 us on this GPU; a persistent workgroup goes straight to its next
+// tile. The dynamic dispatch of one workgroup per tile balanced a
+// heaviest-first list by itself; the static split keeps that balance with a
+// snake order: workgroup i of the W on an XCD takes entry r W + i in even
+// rounds r and r W + W - 1 - i in odd ones, so a heavy entry pairs with a
+// light one.
+template <typename F>
+__device__ __forceinline__ void persistent_snake(int per_xcd, F&& tile) {
+  const int xcd = blockIdx.x & 7, i = blockIdx.x >> 3, W = gridDim.x >> 3;
+  for (int r = 0; r * W < per_xcd; ++r) {
+    const int jj = r * W + ((r & 1) ? W - 1 - i : i);
+    if (jj < per_xcd) tile(xcd, jj);
+  }
 }
 
 template <int EXPMODE>

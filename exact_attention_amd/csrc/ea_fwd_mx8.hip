@@ -348,7 +348,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mx8_kernel(Mx8Args a) {
 // Masking runs before the block under a branch (diagonal and ragged tiles,
 // and tiles past a wave's causal limit), the lazy O rescale after it.
 template <bool CAUSAL, int FMT>
-__global__ __launch_bounds__(512, 1) void fwd_mx8_sp_kernel(Mx8Args a) {
+__device__ __forceinline__ void mx8_sp_tile(const Mx8Args& a, const int xcd, const int j) {
   constexpr int D = 128, BM = kPpBlockM, BN = kFwdBlockN;
   constexpr int TILE = BN * D;  // bytes per K or V tile
   constexpr int NDT = D / 32;
@@ -357,8 +357,6 @@ __global__ __launch_bounds__(512, 1) void fwd_mx8_sp_kernel(Mx8Args a) {
   __shared__ __attribute__((aligned(1024))) uint8_t vs0[TILE], vs1[TILE], vs2[TILE];
 
   // ---------------- tile assignment: XCD-grouped, heaviest causal row blocks first
-  const int xcd = blockIdx.x & 7;
-  const int j = blockIdx.x >> 3;
   const int kg = j / a.n_mb;
   const int r0 = j - kg * a.n_mb;
   const int g = xcd + 8 * kg;
@@ -708,10 +706,30 @@ __global__ __launch_bounds__(512, 1) void fwd_mx8_sp_kernel(Mx8Args a) {
   }
 }
 
+template <bool CAUSAL, int FMT>
+__global__ __launch_bounds__(512, 1) void fwd_mx8_sp_kernel(Mx8Args a) {
+  mx8_sp_tile<CAUSAL, FMT>(a, blockIdx.x & 7, blockIdx.x >> 3);
+}
+
+// persistent form: one workgroup per CU (persistent_snake in ea_fwd_common.h)
+template <bool CAUSAL, int FMT>
+__global__ __launch_bounds__(512, 1) void fwd_mx8_sp_persistent_kernel(Mx8Args a) {
+  persistent_snake(uniform(a.tiles_per_xcd), [&](int xcd, int j) { mx8_sp_tile<CAUSAL, FMT>(a, xcd, j); });
+}
+
 template <int FMT>
 static hipError_t launch_mx8_f(const Mx8Args& a, bool causal, bool pipelined, hipStream_t s) {
   const int grid = 8 * ((a.B * a.Hq + 7) / 8) * a.n_mb;
-  if (pipelined) {
+  if (pipelined && a.persist_wgs > 0) {
+    Mx8Args b = a;
+    b.tiles_per_xcd = grid / 8;
+    const int w = max(1, min(a.persist_wgs / 8, b.tiles_per_xcd));  // workgroups per XCD
+    if (causal) {
+      hipLaunchKernelGGL((fwd_mx8_sp_persistent_kernel<true, FMT>), dim3(8 * w), dim3(512), 0, s, b);
+    } else {
+      hipLaunchKernelGGL((fwd_mx8_sp_persistent_kernel<false, FMT>), dim3(8 * w), dim3(512), 0, s, b);
+    }
+  } else if (pipelined) {
     if (causal) {
       hipLaunchKernelGGL((fwd_mx8_sp_kernel<true, FMT>), dim3(grid), dim3(512), 0, s, a);
     } else {

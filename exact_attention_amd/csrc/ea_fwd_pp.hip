@@ -43,34 +43,28 @@
 
 namespace ea {
 
-// One work tile (256 query rows of one (sequence, head)): the whole forward of
-// those rows. xcd and j locate the tile in the XCD-grouped, heaviest-first order.
-// D: head dim of Q and K; DV: head dim of V and O (equal, or 192 / 128).
-template <int D, int DV, bool CAUSAL, bool VARLEN, int EXPMODE>
-__device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) {
-  constexpr int BM = kPpBlockM, BN = kFwdBlockN;
-  constexpr int TILE = BN * D;               // bf16 elements per K stage
-  constexpr int VTILE = BN * DV;             // ... per V stage
-  constexpr int NDT = DV / 32;               // 32-wide d tiles of O^T
-  constexpr int ROWB = D * 2;                // bytes per K row
-  constexpr int VROWB = DV * 2;              // bytes per V row
-  constexpr int NI = TILE * 2 / 1024;        // 1 KB DMA instructions per K tile
-  constexpr int IPW = NI / 4;                // ... per wave of group A
-  constexpr int NIV = VTILE * 2 / 1024;      // ... per V tile
-  constexpr int IPWV = NIV / 4;
-  static_assert(IPW >= 1 && NI % 4 == 0 && IPWV >= 1 && NIV % 4 == 0,
-                "tiles must split into 4 waves of 1 KB DMA");
-  __shared__ __attribute__((aligned(1024))) uint16_t ks0[TILE], ks1[TILE], ks2[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t vs0[VTILE], vs1[VTILE], vs2[VTILE];
+// One work tile: 256 query rows of one (sequence, head), located in the
+// XCD-grouped, heaviest-first order.
+struct PpTile {
+  int seq, h, row_lo, q0, lq, k0, lk, hk, nkb;
+};
 
-  // ---------------- tile assignment (XCD-grouped, heaviest first)
+// Tile j of XCD xcd; false when that entry holds no rows (padding of the grid
+// to whole XCDs, or past the packed sequences).
+template <bool CAUSAL, bool VARLEN>
+__device__ __forceinline__ bool pp_locate(const FwdArgs& a, int xcd, int j, PpTile& t) {
+  constexpr int BM = kPpBlockM, BN = kFwdBlockN;
+  // scalar from here on: the branches below are then uniform, and the fields
+  // they produce stay in scalar registers
+  xcd = uniform(xcd);
+  j = uniform(j);
   int seq, h, mb;
   const int ngroups = a.nseq * a.Hq;
   if constexpr (!VARLEN) {
     const int kg = j / a.n_mb;
     const int r = j - kg * a.n_mb;
     const int g = xcd + 8 * kg;
-    if (g >= ngroups) return;
+    if (g >= ngroups) return false;
     seq = g / a.Hq;
     h = g - seq * a.Hq;
     mb = a.natural ? r : a.n_mb - 1 - r;
@@ -88,7 +82,7 @@ __device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) 
       if (j < nm) break;
       j -= nm;
     }
-    if (g >= ngroups) return;
+    if (g >= ngroups) return false;
     seq = s;
     h = g - (g / a.Hq) * a.Hq;
     mb = a.natural ? j : nm - 1 - j;
@@ -105,116 +99,86 @@ __device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) 
     k0 = seq * a.Nk;
     lk = a.Nk;
   }
-  seq = uniform(seq);
-  h = uniform(h);
-  mb = uniform(mb);
-  q0 = uniform(q0);
-  lq = uniform(lq);
-  k0 = uniform(k0);
-  lk = uniform(lk);
-  const int hk = uniform(h / a.group);
-  const int off = lk - lq;  // bottom-right causal alignment
-  const int row_lo = mb * BM;
-  int nkeys = lk;
-  if constexpr (CAUSAL) nkeys = min(lk, row_lo + BM + off);
+  t.seq = uniform(seq);
+  t.h = uniform(h);
+  t.row_lo = uniform(mb) * BM;
+  t.q0 = uniform(q0);
+  t.lq = uniform(lq);
+  t.k0 = uniform(k0);
+  t.lk = uniform(lk);
+  t.hk = uniform(t.h / a.group);
+  int nkeys = t.lk;
+  if constexpr (CAUSAL) nkeys = min(t.lk, t.row_lo + BM + (t.lk - t.lq));  // bottom-right causal alignment
   if (nkeys < 0) nkeys = 0;
-  const int nkb = uniform((nkeys + BN - 1) / BN);
+  t.nkb = uniform((nkeys + BN - 1) / BN);
+  return true;
+}
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, w = uniform(tid >> 6), hh = lane >> 5, c = lane & 31;
-  const int grp = w >> 2;                               // 0: group A, 1: group B
-  const int wrow = row_lo + 64 * (w & 3) + 32 * grp;    // wave's first query row
-  const int qi = wrow + c;                              // this lane's query row
-  const size_t qstride = (size_t)a.Hq * D, kstride = (size_t)a.Hkv * D;
-  const size_t ostride = (size_t)a.Hq * DV, vstride = (size_t)a.Hkv * DV;
+// The per-wave state of the ping-pong forward and its two phase bodies,
+// shared by the one-tile kernel and the persistent walk.
+// D: head dim of Q and K; DV: head dim of V and O (equal, or 192 / 128).
+template <int D, int DV, bool CAUSAL, int EXPMODE>
+struct PpCore {
+  static constexpr int BN = kFwdBlockN;
+  static constexpr int NDT = DV / 32;  // 32-wide d tiles of O^T
 
-  // ---------------- Q^T operand (B of S^T = K Q^T), kept in VGPRs
-  bf16x8 qf[D / 16];
-  {
-    const uint16_t* qp = a.q + (size_t)(q0 + qi) * qstride + (size_t)h * D + 8 * hh;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) qf[kk] = (qi < lq) ? *(const bf16x8*)(qp + 16 * kk) : bf16x8{};
-  }
-
-  // ---------------- K/V DMA: wave w of group A fills 1 KB pieces w*IPW ..
-  // w*IPW+IPW-1 of a tile. Lane s of piece p lands at stage byte 1024 p + 16 s = row r, slot sl;
-  // it fetches the global 16-byte chunk sl ^ swz(r) of row r.
-  const uint16_t* kg_base = a.k + (size_t)k0 * kstride + (size_t)hk * D;
-  const uint16_t* vg_base = a.v + (size_t)k0 * vstride + (size_t)hk * DV;
-  uint32_t dma_off[IPW], dma_voff[IPWV];
-#pragma unroll
-  for (int i = 0; i < IPW; ++i) {
-    const int p = 1024 * ((w & 3) * IPW + i) + 16 * lane;
-    const int r = p / ROWB, sl = (p % ROWB) / 16;
-    dma_off[i] = (uint32_t)(r * (int)kstride * 2 + ((sl ^ swz<D>(r)) << 4));
-  }
-#pragma unroll
-  for (int i = 0; i < IPWV; ++i) {
-    const int p = 1024 * ((w & 3) * IPWV + i) + 16 * lane;
-    const int r = p / VROWB, sl = (p % VROWB) / 16;
-    dma_voff[i] = (uint32_t)(r * (int)vstride * 2 + ((sl ^ swz<DV>(r)) << 4));
-  }
-  // one K (V_TILE = false) or V tile into a stage; rows past the sequence land as zeros
-  auto dma_tile = [&](EA_LDS uint16_t* stage, const uint16_t* gbase, int t, auto v_tile) __attribute__((always_inline)) {
-    constexpr bool V = decltype(v_tile)::value;
-    constexpr int DD = V ? DV : D, NP = V ? IPWV : IPW;
-    const size_t stride = V ? vstride : kstride;
-    const int rows = t < nkb ? min(lk - t * BN, BN) : 0;  // tiles past the causal bound are not fetched
-    const uint32_t nrec = rows > 0 ? (uint32_t)((rows - 1) * (int)stride * 2 + DD * 2) : 0u;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(gbase + (size_t)(rows > 0 ? t : 0) * BN * stride, nrec);
-#pragma unroll
-    for (int i = 0; i < NP; ++i)
-      buffer_load16_lds(rs, (EA_LDS void*)(stage + 512 * ((w & 3) * NP + i)), V ? dma_voff[i] : dma_off[i]);
-  };
-  using KTILE = std::integral_constant<bool, false>;
-  using VTILE_ = std::integral_constant<bool, true>;
-  // stage r is a constant wherever these are inlined, so every access names
-  // one LDS object
-  auto kstage = [&](int r) __attribute__((always_inline)) -> EA_LDS uint16_t* {
-    return r == 0 ? (EA_LDS uint16_t*)ks0 : r == 1 ? (EA_LDS uint16_t*)ks1 : (EA_LDS uint16_t*)ks2;
-  };
-  auto vstage = [&](int r) __attribute__((always_inline)) -> EA_LDS uint16_t* {
-    return r == 0 ? (EA_LDS uint16_t*)vs0 : r == 1 ? (EA_LDS uint16_t*)vs1 : (EA_LDS uint16_t*)vs2;
-  };
-
+  int lane, hh, c, w, grp;
   // loop-invariant LDS element offsets of this lane's operand reads (see the
   // 4-wave kernel): K rows c and c + 32, V^T transposed reads
   int k_off[D / 16];
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) k_off[kk] = tile_off<D>(c, 16 * kk + 8 * hh);
-  const int tr_row = 4 * hh + ((lane & 15) >> 2);
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   int v_off[NDT][2];
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) {
-    v_off[dt][0] = tile_off<DV>(tr_row, 32 * dt + tr_col);
-    v_off[dt][1] = tile_off<DV>(tr_row + 8, 32 * dt + tr_col);
-  }
-  const int wave_last_q = wrow + 31;
-  const int wave_first_q = wrow;
-  // a tile is fully masked for this wave (wave-uniform) if its first key lies
-  // beyond the wave's last row's causal limit
-  auto tile_dead = [&](int t) __attribute__((always_inline)) { return CAUSAL && t * BN > wave_last_q + off; };
-
-  float m_run = kNegInf, l_run = 0.f;
+  bf16x8 qf[D / 16];  // Q^T operand (B of S^T = K Q^T)
   f32x16 oacc[NDT];
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16{};
-  f32x16 s0 = f32x16{}, s1 = f32x16{};
+  f32x16 s0, s1;
   bf16x8 pb[4];
-#pragma unroll
-  for (int st = 0; st < 4; ++st) pb[st] = bf16x8{};
-  const float sl = a.scale_log2;
+  float m_run, l_run;
 
-  // ---- MFMA part of step s: S_s = K_s Q^T, then O += V_{s-1} P_{s-1}, as one
-  // straight-line block so the V^T reads overlap the S products. Both run for
-  // every step: for a tile this wave skips (past its causal limit, or s = nkb)
-  // the VALU part leaves P = 0, stages past the end hold zeros from the DMA,
-  // and the V stage read at step 0 is zeroed before the loop, so the extra
-  // products add exact zeros.
-  auto mfma_part = [&](int r) __attribute__((always_inline)) {
-    const EA_LDS uint16_t* ks = kstage(r);
-    const EA_LDS uint16_t* vs = vstage((r + 2) % 3);
+  __device__ __forceinline__ void init() {
+    const int tid = threadIdx.x;
+    lane = tid & 63;
+    w = uniform(tid >> 6);
+    hh = lane >> 5;
+    c = lane & 31;
+    grp = w >> 2;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) k_off[kk] = tile_off<D>(c, 16 * kk + 8 * hh);
+    const int tr_row = 4 * hh + ((lane & 15) >> 2);
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      v_off[dt][0] = tile_off<DV>(tr_row, 32 * dt + tr_col);
+      v_off[dt][1] = tile_off<DV>(tr_row + 8, 32 * dt + tr_col);
+    }
+    s0 = f32x16{};
+    s1 = f32x16{};
+#pragma unroll
+    for (int st = 0; st < 4; ++st) pb[st] = bf16x8{};
+    reset();
+  }
+  __device__ __forceinline__ void reset() {
+    m_run = kNegInf;
+    l_run = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16{};
+  }
+  // first query row of this wave in a tile starting at row_lo
+  __device__ __forceinline__ int wave_row(int row_lo) const { return row_lo + 64 * (w & 3) + 32 * grp; }
+
+  // Q^T rows of this lane from global memory (zeros past the sequence end)
+  __device__ __forceinline__ void load_q(const FwdArgs& a, const PpTile& t) {
+    const int qi = wave_row(t.row_lo) + c;
+    const uint16_t* qp = a.q + (size_t)(t.q0 + qi) * ((size_t)a.Hq * D) + (size_t)t.h * D + 8 * hh;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) qf[kk] = (qi < t.lq) ? *(const bf16x8*)(qp + 16 * kk) : bf16x8{};
+  }
+
+  // ---- MFMA part of a step: S = K_s Q^T into s0, s1, then O += V_{s-1} P_{s-1}
+  // (pb), as one straight-line block so the V^T reads overlap the S products.
+  // Both run for every step: for a tile this wave skips (past its causal
+  // limit, or the pipeline tail) the VALU part leaves P = 0, stages past the
+  // end hold zeros from the DMA, and the V stage read at the first step is
+  // zeroed, so the extra products add exact zeros.
+  __device__ __forceinline__ void mfma_part(const EA_LDS uint16_t* ks, const EA_LDS uint16_t* vs) {
     // The lane offsets pass through an empty asm here so that the stage base
     // is added inside this block, where it folds into the ds_read offset
     // field, instead of a hoisted register copy per stage and offset.
@@ -264,11 +228,14 @@ __device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) 
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
     __builtin_amdgcn_s_setprio(0);
-  };
+  }
 
-  // ---- VALU part of step s: softmax of S_s into P_s (bf16, computed in place
-  // over S), m, l, rescale
-  auto valu_part = [&](int s, bool act) __attribute__((always_inline)) {
+  // ---- VALU part of step s of a tile: softmax of S_s into P_s (bf16,
+  // computed in place over S), m, l, rescale. act: the tile holds keys this
+  // wave sees. qi: this lane's query row; wave_first_q: the wave's first row;
+  // lk: keys of the sequence; off = lk - lq (bottom-right causal alignment).
+  __device__ __forceinline__ void valu_part(int s, bool act, int qi, int wave_first_q, int lk, int off, float sl,
+                                            float tau) {
     if (!act) {
 #pragma unroll
       for (int st = 0; st < 4; ++st) pb[st] = bf16x8{};
@@ -293,7 +260,7 @@ __device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) 
     for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, __builtin_fmaxf(s0[i], s1[i]));
     mx = max_with_partner32(mx);
     const float m_new = __builtin_fmaxf(m_run, mx * sl);
-    if (__ballot(m_new > m_run + a.tau)) {
+    if (__ballot(m_new > m_run + tau)) {
       const float alpha = (m_run == kNegInf) ? 0.f : exp2_hw(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
@@ -317,7 +284,118 @@ __device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) 
     pb[1] = pack_p8<8>(s0);
     pb[2] = pack_p8<0>(s1);
     pb[3] = pack_p8<8>(s1);
+  }
+
+  // ---- end of a tile: O = acc / l (bf16), lse = ln2 * (m + log2 l)
+  template <bool VARLEN>
+  __device__ __forceinline__ void store(const FwdArgs& a, int seq, int h, int row_lo, int q0, int lq) {
+    const float l_tot = sum_with_partner32(l_run);
+    const float inv = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
+    const int qi = wave_row(row_lo) + c;
+    if (qi < lq) {
+      uint16_t* op = a.o + (size_t)(q0 + qi) * ((size_t)a.Hq * DV) + (size_t)h * DV;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d0 = 32 * dt + 8 * g4 + 4 * hh;
+          uint2 val;
+          val.x = pack_bf16x2(oacc[dt][4 * g4] * inv, oacc[dt][4 * g4 + 1] * inv);
+          val.y = pack_bf16x2(oacc[dt][4 * g4 + 2] * inv, oacc[dt][4 * g4 + 3] * inv);
+          *(uint2*)(op + d0) = val;
+        }
+      }
+      if (a.lse != nullptr && hh == 0) {
+        const float v = (l_tot > 0.f && m_run != kNegInf) ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
+        size_t idx;
+        if constexpr (VARLEN) {
+          idx = (size_t)h * a.total_q + q0 + qi;
+        } else {
+          idx = ((size_t)seq * a.Hq + h) * a.Nq + qi;
+        }
+        a.lse[idx] = v;
+      }
+    }
+  }
+};
+
+// Per-lane global byte offsets of LDS DMA: wave slot ws (0..3) fills 1 KB
+// pieces ws*NP .. ws*NP+NP-1 of a tile of rows of DD bf16. Lane s of piece p
+// lands at tile byte 1024 p + 16 s = row r, slot sl; it fetches the global
+// 16-byte chunk sl ^ swz(r) of row r (rows `stride` elements apart).
+template <int DD>
+__device__ __forceinline__ uint32_t dma_lane_off(int piece, int lane, size_t stride) {
+  constexpr int ROWB = DD * 2;
+  const int p = 1024 * piece + 16 * lane;
+  const int r = p / ROWB, sl = (p % ROWB) / 16;
+  return (uint32_t)(r * (int)stride * 2 + ((sl ^ swz<DD>(r)) << 4));
+}
+
+// One work tile: the whole forward of its 256 rows.
+template <int D, int DV, bool CAUSAL, bool VARLEN, int EXPMODE>
+__device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) {
+  constexpr int BN = kFwdBlockN;
+  constexpr int TILE = BN * D;               // bf16 elements per K stage
+  constexpr int VTILE = BN * DV;             // ... per V stage
+  constexpr int NI = TILE * 2 / 1024;        // 1 KB DMA instructions per K tile
+  constexpr int IPW = NI / 4;                // ... per wave of group A
+  constexpr int NIV = VTILE * 2 / 1024;      // ... per V tile
+  constexpr int IPWV = NIV / 4;
+  static_assert(IPW >= 1 && NI % 4 == 0 && IPWV >= 1 && NIV % 4 == 0,
+                "tiles must split into 4 waves of 1 KB DMA");
+  __shared__ __attribute__((aligned(1024))) uint16_t ks0[TILE], ks1[TILE], ks2[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t vs0[VTILE], vs1[VTILE], vs2[VTILE];
+
+  PpTile t;
+  if (!pp_locate<CAUSAL, VARLEN>(a, xcd, j, t)) return;
+  const int off = t.lk - t.lq;  // bottom-right causal alignment
+  const int nkb = t.nkb;
+
+  PpCore<D, DV, CAUSAL, EXPMODE> cr;
+  cr.init();
+  const int tid = threadIdx.x;
+  const int lane = cr.lane, w = cr.w, grp = cr.grp;
+  const int wrow = cr.wave_row(t.row_lo);  // wave's first query row
+  const int qi = wrow + cr.c;              // this lane's query row
+  const size_t kstride = (size_t)a.Hkv * D, vstride = (size_t)a.Hkv * DV;
+  cr.load_q(a, t);
+
+  // ---------------- K/V DMA: wave w of group A fills 1 KB pieces w*IPW ..
+  // w*IPW+IPW-1 of a tile
+  const uint16_t* kg_base = a.k + (size_t)t.k0 * kstride + (size_t)t.hk * D;
+  const uint16_t* vg_base = a.v + (size_t)t.k0 * vstride + (size_t)t.hk * DV;
+  uint32_t dma_off[IPW], dma_voff[IPWV];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) dma_off[i] = dma_lane_off<D>((w & 3) * IPW + i, lane, kstride);
+#pragma unroll
+  for (int i = 0; i < IPWV; ++i) dma_voff[i] = dma_lane_off<DV>((w & 3) * IPWV + i, lane, vstride);
+  // one K (V_TILE = false) or V tile into a stage; rows past the sequence land as zeros
+  auto dma_tile = [&](EA_LDS uint16_t* stage, const uint16_t* gbase, int tt, auto v_tile) __attribute__((always_inline)) {
+    constexpr bool V = decltype(v_tile)::value;
+    constexpr int DD = V ? DV : D, NP = V ? IPWV : IPW;
+    const size_t stride = V ? vstride : kstride;
+    const int rows = tt < nkb ? min(t.lk - tt * BN, BN) : 0;  // tiles past the causal bound are not fetched
+    const uint32_t nrec = rows > 0 ? (uint32_t)((rows - 1) * (int)stride * 2 + DD * 2) : 0u;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(gbase + (size_t)(rows > 0 ? tt : 0) * BN * stride, nrec);
+#pragma unroll
+    for (int i = 0; i < NP; ++i)
+      buffer_load16_lds(rs, (EA_LDS void*)(stage + 512 * ((w & 3) * NP + i)), V ? dma_voff[i] : dma_off[i]);
   };
+  using KTILE = std::integral_constant<bool, false>;
+  using VTILE_ = std::integral_constant<bool, true>;
+  // stage r is a constant wherever these are inlined, so every access names
+  // one LDS object
+  auto kstage = [&](int r) __attribute__((always_inline)) -> EA_LDS uint16_t* {
+    return r == 0 ? (EA_LDS uint16_t*)ks0 : r == 1 ? (EA_LDS uint16_t*)ks1 : (EA_LDS uint16_t*)ks2;
+  };
+  auto vstage = [&](int r) __attribute__((always_inline)) -> EA_LDS uint16_t* {
+    return r == 0 ? (EA_LDS uint16_t*)vs0 : r == 1 ? (EA_LDS uint16_t*)vs1 : (EA_LDS uint16_t*)vs2;
+  };
+  const int wave_last_q = wrow + 31;
+  // a tile is fully masked for this wave (wave-uniform) if its first key lies
+  // beyond the wave's last row's causal limit
+  auto tile_dead = [&](int s) __attribute__((always_inline)) { return CAUSAL && s * BN > wave_last_q + off; };
+  const float sl = a.scale_log2;
 
   // ---- one step: MFMA part, barrier, VALU part, barrier. Group B starts one
   // barrier late, so in phase 2s group A runs the MFMA part of step s while B
@@ -329,13 +407,13 @@ __device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) 
   // pieces in flight -- before the barrier after which both groups read them.
   auto step = [&](int r, int s) __attribute__((always_inline)) {
     const bool act = s < nkb && !tile_dead(s);
-    mfma_part(r);
+    cr.mfma_part(kstage(r), vstage((r + 2) % 3));
     pp_barrier();
     if (grp == 0) {
       dma_tile(kstage((r + 2) % 3), kg_base, s + 2, KTILE{});
       dma_tile(vstage((r + 1) % 3), vg_base, s + 1, VTILE_{});
     }
-    valu_part(s, act);
+    cr.valu_part(s, act, qi, wrow, t.lk, off, sl, a.tau);
     if (grp == 0) wait_vmcnt<IPW + IPWV>();
     pp_barrier();
   };
@@ -365,34 +443,244 @@ __device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) 
   if (grp == 0) pp_barrier();
   // no DMA may still be writing this workgroup's LDS when it exits
   __builtin_amdgcn_s_waitcnt(0);
+  cr.template store<VARLEN>(a, t.seq, t.h, t.row_lo, t.q0, t.lq);
+}
 
-  // ---------------- epilogue: O = acc / l (bf16), lse = ln2 * (m + log2 l)
-  const float l_tot = sum_with_partner32(l_run);
-  const float inv = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
-  if (qi < lq) {
-    uint16_t* op = a.o + (size_t)(q0 + qi) * ostride + (size_t)h * DV;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = 32 * dt + 8 * g4 + 4 * hh;
-        uint2 val;
-        val.x = pack_bf16x2(oacc[dt][4 * g4] * inv, oacc[dt][4 * g4 + 1] * inv);
-        val.y = pack_bf16x2(oacc[dt][4 * g4 + 2] * inv, oacc[dt][4 * g4 + 3] * inv);
-        *(uint2*)(op + d0) = val;
-      }
+// Persistent walk with the K/V pipeline running on across tiles (the
+// unroll-KV schedule of "Low-precision FlashAttention-4: end-to-end
+// block-scaled attention for Blackwell", section 2.1.2, in this kernel's
+// terms): one workgroup per CU runs one continuous sequence of steps over its
+// tiles (persistent_snake's order). Step 0 of tile n+1 computes S_0 of tile
+// n+1 in the same MFMA block as the last O += V P of tile n, and its VALU part
+// first stores tile n's O and LSE, then starts tile n+1's softmax. The DMA
+// issued two steps ahead simply continues into the next tile's K/V tiles, and
+// the next tile's Q rows arrive by LDS DMA into a fourth LDS region while the
+// current tile runs, so no tile waits on HBM at its start, and the pipeline
+// fills and drains once per workgroup instead of once per tile.
+//  * Every tile runs at least kMinSteps steps (steps past its keys multiply
+//    P = 0 by zero stages, adding exact zeros): the next tile's Q pieces are
+//    issued at step 1 and read at the last step, which needs two steps of
+//    DMA waits in between.
+//  * Results are bitwise those of the one-tile kernel: each row sees the same
+//    products in the same order.
+//  * Measured on MI355X it is not faster than the one-tile body in a
+//    persistent loop: this kernel's tile boundaries already cost little (the
+//    other wave group keeps the matrix core busy through them), while the
+//    boundary bookkeeping adds scalar instructions to every step's softmax
+//    phase, the longer of the two.
+template <int D, int DV, bool CAUSAL, bool VARLEN, int EXPMODE>
+__device__ __forceinline__ void pp_walk(const FwdArgs& a) {
+  static_assert(D == DV, "the next tile's Q is staged in LDS: equal head dims only");
+  constexpr int BN = kFwdBlockN;
+  constexpr int TILE = BN * D;               // bf16 elements per K or V stage
+  constexpr int IPW = TILE * 2 / 1024 / 4;   // 1 KB DMA pieces per wave of group A per tile
+  constexpr int QTILE = kPpBlockM * D;       // the next tile's Q rows
+  constexpr int NQ = QTILE * 2 / 1024 / 4;   // ... pieces per wave of group A (one 64-row block)
+  constexpr int kMinSteps = 4;
+  static_assert(NQ * 1024 == TILE * 2, "a wave's Q block is one stage-sized tile");
+  static_assert(2 * IPW + NQ < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) uint16_t ks0[TILE], ks1[TILE], ks2[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t vs0[TILE], vs1[TILE], vs2[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t qs[QTILE];
+
+  // ---------------- this workgroup's tiles, in persistent_snake's order
+  const int per_xcd = uniform(a.tiles_per_xcd);
+  const int xcd = uniform(blockIdx.x & 7), wi = uniform(blockIdx.x >> 3), W = uniform(gridDim.x >> 3);
+  int it = 0;
+  auto next_tile = [&](PpTile& t) __attribute__((always_inline)) -> bool {
+    while (it * W < per_xcd) {
+      const int r = it++;
+      const int jj = r * W + ((r & 1) ? W - 1 - wi : wi);
+      if (jj < per_xcd && pp_locate<CAUSAL, VARLEN>(a, xcd, jj, t)) return true;
     }
-    if (a.lse != nullptr && hh == 0) {
-      const float v = (l_tot > 0.f && m_run != kNegInf) ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
-      size_t idx;
-      if constexpr (VARLEN) {
-        idx = (size_t)h * a.total_q + q0 + qi;
+    return false;
+  };
+  PpTile cur, nxt;
+  if (!next_tile(cur)) return;
+  bool has_nxt = next_tile(nxt);
+  int steps = max(cur.nkb, kMinSteps);
+  int s = 0;          // step of cur
+  bool live = true;   // false: the drain step after the last tile
+  bool has_prv = false;
+  int p_seq = 0, p_h = 0, p_row_lo = 0, p_q0 = 0, p_lq = 0;  // the tile whose O is in the accumulators
+
+  PpCore<D, D, CAUSAL, EXPMODE> cr;
+  cr.init();
+  const int tid = threadIdx.x;
+  const int lane = cr.lane, w = cr.w, grp = cr.grp;
+  const size_t kstride = (size_t)a.Hkv * D, qstride = (size_t)a.Hq * D;
+  const float sl = a.scale_log2;
+  cr.load_q(a, cur);
+
+  // K and V rows of each tile's KV head; nxt_nkb = 0 when there is no next tile
+  auto kv_base = [&](const uint16_t* tensor, const PpTile& t) __attribute__((always_inline)) {
+    return tensor + (size_t)t.k0 * kstride + (size_t)t.hk * D;
+  };
+  const uint16_t* cur_kb = kv_base(a.k, cur);
+  const uint16_t* cur_vb = kv_base(a.v, cur);
+  const uint16_t* nxt_kb = has_nxt ? kv_base(a.k, nxt) : a.k;
+  const uint16_t* nxt_vb = has_nxt ? kv_base(a.v, nxt) : a.v;
+  int nxt_nkb = has_nxt ? nxt.nkb : 0;
+
+  uint32_t dma_off[IPW];  // K and V rows have the same stride
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) dma_off[i] = dma_lane_off<D>((w & 3) * IPW + i, lane, kstride);
+  // Source of key tile t of a tile in K or V: base and byte range (0 for
+  // tiles at or past nkb, so those stages fill with zeros). kb: the tile's
+  // first key row of its KV head in that tensor. Branch-free scalar work,
+  // done at the start of a step, where it issues between the MFMAs; the empty
+  // asm keeps the compiler from sinking it into the DMA issue after the
+  // barrier, whose length the other group waits for.
+  struct KvSrc {
+    const uint16_t* base;
+    uint32_t nrec;
+  };
+  const size_t tile_elems = (size_t)BN * kstride;
+  const uint32_t row_bytes = (uint32_t)(kstride * 2);
+  auto kv_src = [&](const uint16_t* kb, int lk, int nkb, int t) __attribute__((always_inline)) {
+    const int rows = t < nkb ? min(lk - t * BN, BN) : 0;
+    KvSrc r;
+    r.nrec = launder_s(rows > 0 ? (uint32_t)(rows - 1) * row_bytes + (uint32_t)(D * 2) : 0u);
+    r.base = launder_s(kb + (size_t)(uint32_t)t * tile_elems);
+    return r;
+  };
+  // one K or V tile into a stage. The wave's slot passes through an empty asm
+  // at every use, so the LDS destinations are formed here (one scalar add
+  // each) rather than hoisted out of the loop as one scalar register per
+  // stage and piece.
+  auto dma_kv = [&](EA_LDS uint16_t* stage, const KvSrc& src) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src.base, src.nrec);
+    EA_LDS uint16_t* dst = stage + 512 * IPW * launder_s(w & 3);
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) buffer_load16_lds(rs, (EA_LDS void*)(dst + 512 * i), dma_off[i]);
+  };
+  // the next tile's Q rows: wave w of group A fills 64-row block w of the Q
+  // region in the K-stage layout (rows past the sequence land as zeros)
+  auto dma_q = [&]() __attribute__((always_inline)) {
+    const int rb = nxt.row_lo + 64 * (w & 3);
+    const int rows = min(nxt.lq - rb, 64);
+    const uint32_t nrec = rows > 0 ? (uint32_t)((rows - 1) * (int)qstride * 2 + D * 2) : 0u;
+    const uint16_t* base = a.q + (rows > 0 ? (size_t)(nxt.q0 + rb) * qstride + (size_t)nxt.h * D : (size_t)0);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, nrec);
+    // per-lane offsets formed here from a laundered lane id, not hoisted out
+    // of the loop as NQ live registers
+    const int ln = launder(lane);
+    EA_LDS uint16_t* dst = (EA_LDS uint16_t*)qs + TILE * launder_s(w & 3);
+#pragma unroll
+    for (int p = 0; p < NQ; ++p)
+      buffer_load16_lds(rs, (EA_LDS void*)(dst + 512 * p), dma_lane_off<D>(p, ln, qstride));
+  };
+  // this wave's Q^T operand of the next tile, from the Q region
+  auto read_q = [&]() __attribute__((always_inline)) {
+    const EA_LDS uint16_t* qb = (const EA_LDS uint16_t*)qs + (w & 3) * TILE + 32 * grp * D;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) cr.qf[kk] = lds_load<bf16x8>(qb + cr.k_off[kk]);
+    wait_lgkm0();  // the region is refilled two steps later
+  };
+  auto kstage = [&](int r) __attribute__((always_inline)) -> EA_LDS uint16_t* {
+    return r == 0 ? (EA_LDS uint16_t*)ks0 : r == 1 ? (EA_LDS uint16_t*)ks1 : (EA_LDS uint16_t*)ks2;
+  };
+  auto vstage = [&](int r) __attribute__((always_inline)) -> EA_LDS uint16_t* {
+    return r == 0 ? (EA_LDS uint16_t*)vs0 : r == 1 ? (EA_LDS uint16_t*)vs1 : (EA_LDS uint16_t*)vs2;
+  };
+
+  // ---- one step (global step g, stage r = g mod 3): as in the one-tile
+  // kernel, plus the tile boundary work in the VALU part. Group A's DMA at
+  // step g fetches what step g + 2 reads: its K tile and the V tile of step
+  // g + 1's scores, from cur or, near cur's end, from nxt.
+  auto wstep = [&](auto rc) __attribute__((always_inline)) -> bool {
+    constexpr int r = decltype(rc)::value;
+    KvSrc ksrc, vsrc;
+    {
+      const bool kin = s + 2 < steps, vin = s + 1 < steps;
+      ksrc = kv_src(kin ? cur_kb : nxt_kb, kin ? cur.lk : nxt.lk, kin ? cur.nkb : nxt_nkb, kin ? s + 2 : s + 2 - steps);
+      vsrc = kv_src(vin ? cur_vb : nxt_vb, vin ? cur.lk : nxt.lk, vin ? cur.nkb : nxt_nkb, vin ? s + 1 : 0);
+    }
+    cr.mfma_part(kstage(r), vstage((r + 2) % 3));
+    pp_barrier();
+    if (!live) {  // drain: the last tile's final O += V P is in
+      cr.template store<VARLEN>(a, p_seq, p_h, p_row_lo, p_q0, p_lq);
+      pp_barrier();
+      return false;
+    }
+    if (grp == 0) {
+      dma_kv(kstage((r + 2) % 3), ksrc);
+      dma_kv(vstage((r + 1) % 3), vsrc);
+      if (s == 1 && has_nxt) dma_q();
+    }
+    if (s == 0 && has_prv) {  // tile boundary: the previous tile's final O += V P just ran
+      cr.template store<VARLEN>(a, p_seq, p_h, p_row_lo, p_q0, p_lq);
+      cr.reset();
+    }
+    {
+      const int wrow = cr.wave_row(cur.row_lo);
+      const int off = cur.lk - cur.lq;
+      const bool act = s < cur.nkb && !(CAUSAL && s * BN > wrow + 31 + off);
+      cr.valu_part(s, act, wrow + cr.c, wrow, cur.lk, off, sl, a.tau);
+    }
+    if (s == steps - 1 && has_nxt) read_q();
+    if (grp == 0) {
+      if (s == 1 && has_nxt) {
+        wait_vmcnt<2 * IPW + NQ>();  // the Q pieces may stay in flight one more step
       } else {
-        idx = ((size_t)seq * a.Hq + h) * a.Nq + qi;
+        wait_vmcnt<2 * IPW>();
       }
-      a.lse[idx] = v;
     }
+    pp_barrier();
+    if (++s == steps) {
+      s = 0;
+      has_prv = true;
+      p_seq = cur.seq;
+      p_h = cur.h;
+      p_row_lo = cur.row_lo;
+      p_q0 = cur.q0;
+      p_lq = cur.lq;
+      if (has_nxt) {
+        cur = nxt;
+        cur_kb = nxt_kb;
+        cur_vb = nxt_vb;
+        steps = max(cur.nkb, kMinSteps);
+        has_nxt = next_tile(nxt);
+        nxt_nkb = has_nxt ? nxt.nkb : 0;
+        if (has_nxt) {
+          nxt_kb = kv_base(a.k, nxt);
+          nxt_vb = kv_base(a.v, nxt);
+        }
+      } else {
+        live = false;
+      }
+    }
+    return true;
+  };
+
+  // prologue: K_0, K_1 and V_0 of the first tile; the V stage that the first
+  // step multiplies by P = 0 is zeroed so it holds no stale NaN
+  {
+    static_assert(TILE % (8 * 512) == 0, "stage zeroing covers the tile");
+#pragma unroll
+    for (int i = 0; i < TILE / (8 * 512); ++i)
+      lds_store<i32x4>((EA_LDS uint16_t*)vs2 + 8 * (tid + 512 * i), i32x4{});
   }
+  if (grp == 0) {
+    dma_kv(kstage(0), kv_src(cur_kb, cur.lk, cur.nkb, 0));
+    dma_kv(kstage(1), kv_src(cur_kb, cur.lk, cur.nkb, 1));
+    dma_kv(vstage(0), kv_src(cur_vb, cur.lk, cur.nkb, 0));
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  using R0 = std::integral_constant<int, 0>;
+  using R1 = std::integral_constant<int, 1>;
+  using R2 = std::integral_constant<int, 2>;
+  if (grp == 1) pp_barrier();  // group B runs one phase behind
+  for (;;) {
+    if (!wstep(R0{})) break;
+    if (!wstep(R1{})) break;
+    if (!wstep(R2{})) break;
+  }
+  if (grp == 0) pp_barrier();
+  // no DMA may still be writing this workgroup's LDS when it exits
+  __builtin_amdgcn_s_waitcnt(0);
 }
 
 template <int D, int DV, bool CAUSAL, bool VARLEN, int EXPMODE>
@@ -400,23 +688,20 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   pp_tile<D, DV, CAUSAL, VARLEN, EXPMODE>(a, blockIdx.x & 7, blockIdx.x >> 3);
 }
 
-// Persistent form: one workgroup per CU walks its XCD's tile list. Launching a
-// new workgroup on a CU that just retired one takes ~11 us on this GPU (about
-// 8% of a prefill forward that runs eight workgroups per CU); a persistent
-// workgroup goes straight to its next tile. The hardware's dynamic dispatch
-// balanced the heaviest-first list by itself; a static assignment must keep
-// that balance, so workgroup i of an XCD with W workgroups takes, in round r,
-// list entry r W + i for even r and r W + W - 1 - i for odd r (snake order):
-// the heaviest row block of one (sequence, head) pairs with the lightest of
-// the next.
+// Persistent form (persistent_snake in ea_fwd_common.h): one workgroup per
+// CU runs the one-tile body for each tile of its list.
 template <int D, int DV, bool CAUSAL, bool VARLEN, int EXPMODE>
 __global__ __launch_bounds__(512, 1) void fwd_pp_persistent_kernel(FwdArgs a) {
-  const int xcd = blockIdx.x & 7, i = blockIdx.x >> 3, W = gridDim.x >> 3;
-  const int per_xcd = uniform(a.tiles_per_xcd);
-  for (int r = 0; r * W < per_xcd; ++r) {
-    const int jj = r * W + ((r & 1) ? W - 1 - i : i);
-    if (jj < per_xcd) pp_tile<D, DV, CAUSAL, VARLEN, EXPMODE>(a, xcd, jj);
-  }
+  persistent_snake(uniform(a.tiles_per_xcd),
+                   [&](int xcd, int j) { pp_tile<D, DV, CAUSAL, VARLEN, EXPMODE>(a, xcd, j); });
+}
+
+// Persistent form with the K/V pipeline running on across tiles (pp_walk);
+// equal head dims only: the next tile's Q of (192, 128) does not fit beside
+// its stages in LDS.
+template <int D, bool CAUSAL, bool VARLEN, int EXPMODE>
+__global__ __launch_bounds__(512, 1) void fwd_pp_unrollkv_kernel(FwdArgs a) {
+  pp_walk<D, D, CAUSAL, VARLEN, EXPMODE>(a);
 }
 
 template <int D, int DV, bool CAUSAL, bool VARLEN, int EXPMODE>
@@ -426,8 +711,17 @@ static hipError_t launch_pp_t(const FwdArgs& a, hipStream_t s) {
     FwdArgs b = a;
     b.tiles_per_xcd = grid / 8;
     const int w = min(a.persist_wgs / 8, b.tiles_per_xcd);  // workgroups per XCD
-    hipLaunchKernelGGL((fwd_pp_persistent_kernel<D, DV, CAUSAL, VARLEN, EXPMODE>), dim3(8 * max(w, 1)), dim3(512), 0,
-                       s, b);
+    if (a.unroll_kv) {
+      if constexpr (D == DV) {
+        hipLaunchKernelGGL((fwd_pp_unrollkv_kernel<D, CAUSAL, VARLEN, EXPMODE>), dim3(8 * max(w, 1)), dim3(512), 0,
+                           s, b);
+      } else {
+        return hipErrorInvalidValue;
+      }
+    } else {
+      hipLaunchKernelGGL((fwd_pp_persistent_kernel<D, DV, CAUSAL, VARLEN, EXPMODE>), dim3(8 * max(w, 1)), dim3(512),
+                         0, s, b);
+    }
   } else {
     hipLaunchKernelGGL((fwd_pp_kernel<D, DV, CAUSAL, VARLEN, EXPMODE>), dim3(grid), dim3(512), 0, s, a);
   }

@@ -26,6 +26,8 @@ struct FwdArgs {
   int persist_wgs;     // ping-pong kernel: > 0 runs the persistent form with this many
                        // workgroups (a multiple of 8, one per CU); 0: one workgroup per tile
   int tiles_per_xcd;   // set by the launcher for the persistent form
+  int unroll_kv;       // with persist_wgs > 0 and equal head dims: 1 runs the walk whose
+                       // K/V pipeline continues across tiles (unroll-KV schedule)
 };
 
 constexpr int kFwdBlockM = 128;  // query rows per workgroup (4 waves x 32)
@@ -63,6 +65,8 @@ struct Mx8Args {
   float scale_log2;
   float tau;
   int fmt;  // Q/K/V codes: 0 = OCP e4m3, 1 = OCP e5m2
+  int persist_wgs;    // pipelined kernel: > 0 runs the persistent form (workgroups, multiple of 8)
+  int tiles_per_xcd;  // set by the launcher for the persistent form
 };
 hipError_t launch_fwd_mx8(const Mx8Args& a, bool causal, hipStream_t s);
 // 8-wave software-pipelined MX fp8 forward; a.n_mb counts kPpBlockM-row blocks
@@ -87,6 +91,8 @@ struct BwdArgs {
   int n_kb;            // 128-key blocks (dK/dV kernel)
   float scale, scale_log2;
   int natural;         // 1: ascending block order (results do not depend on it)
+  int persist_wgs;     // > 0: persistent dQ and dK/dV kernels with this many workgroups (multiple of 8)
+  int tiles_per_xcd;   // set by the launcher for each persistent kernel
 };
 hipError_t launch_bwd(const BwdArgs& a, int d, bool causal, hipStream_t s);
 size_t bwd_workspace_bytes(int B, int Hq, int Nq);

@@ -86,13 +86,22 @@ typedef struct {
  *                           workgroup per CU walks a static, load-balanced
  *                           list of row blocks instead of one workgroup per
  *                           row block (the pages' persistent tile scheduler,
- *                           "FlashAttention4 close reading", section 3.3) */
+ *                           "FlashAttention4 close reading", section 3.3)
+ *   EA_FWD_KERNEL_UNROLL_KV the persistent form with the K/V pipeline running
+ *                           on across row blocks: the first S of the next
+ *                           block is computed with the last O += V P of the
+ *                           current one (the unroll-KV schedule of
+ *                           "Low-precision FlashAttention-4: end-to-end
+ *                           block-scaled attention for Blackwell", section
+ *                           2.1.2); bitwise the results of the ping-pong
+ *                           kernel; (d_qk, d_v) = (64, 64) and (128, 128) only */
 enum {
   EA_FWD_KERNEL_AUTO = 0,
   EA_FWD_KERNEL_4WAVE = 1,
   EA_FWD_KERNEL_PINGPONG = 2,
   EA_FWD_KERNEL_PIPELINED = 3,
-  EA_FWD_KERNEL_PERSISTENT = 4
+  EA_FWD_KERNEL_PERSISTENT = 4,
+  EA_FWD_KERNEL_UNROLL_KV = 5
 };
 
 /* Default tuning values. */
@@ -203,10 +212,12 @@ ea_status ea_attn_fwd_mx8(const void* q8, const void* k8, const void* v8,
 
 /*
  * ea_attn_fwd_mx8_tuned -- ea_attn_fwd_mx8 with forward tuning (NULL = the
- * defaults). tuning->kernel selects EA_FWD_KERNEL_4WAVE or
- * EA_FWD_KERNEL_PIPELINED (AUTO: the pipelined one); EA_FWD_KERNEL_PINGPONG,
- * EA_FWD_KERNEL_PERSISTENT, exp_mode other than EA_EXP_HW and
- * natural_order = 1 return EA_ERR_UNSUPPORTED. rescale_log2 is the lazy-rescale threshold, which also
+ * defaults). tuning->kernel selects EA_FWD_KERNEL_4WAVE,
+ * EA_FWD_KERNEL_PIPELINED or EA_FWD_KERNEL_PERSISTENT (the pipelined kernel
+ * with one workgroup per CU; AUTO: that persistent form); EA_FWD_KERNEL_PINGPONG,
+ * EA_FWD_KERNEL_UNROLL_KV,
+ * exp_mode other than EA_EXP_HW and natural_order = 1 return
+ * EA_ERR_UNSUPPORTED. rescale_log2 is the lazy-rescale threshold, which also
  * bounds P before its e4m3 rounding (P <= 2^rescale_log2, so values above 8
  * can overflow e4m3's 448).
  */
@@ -236,6 +247,17 @@ ea_status ea_attn_fwd_mx8_tuned(const void* q8, const void* k8, const void* v8,
  *     bytes (per-row statistics), owned by the caller, contents ignored.
  */
 size_t ea_attn_bwd_workspace_size(int B, int Hq, int Nq);
+/* Work schedule of the backward kernels (results bitwise identical):
+ *   EA_BWD_SCHEDULE_AUTO       the library's choice (one workgroup per tile);
+ *   EA_BWD_SCHEDULE_PER_TILE   one workgroup per work tile;
+ *   EA_BWD_SCHEDULE_PERSISTENT one workgroup per CU (two for the dQ kernel)
+ *                              walking a load-balanced static tile list. */
+enum { EA_BWD_SCHEDULE_AUTO = 0, EA_BWD_SCHEDULE_PER_TILE = 1, EA_BWD_SCHEDULE_PERSISTENT = 2 };
+/* ea_attn_bwd with an explicit schedule (anything else is EA_ERR_INVALID). */
+ea_status ea_attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                         const float* lse, void* dq, void* dk, void* dv, int B, int Nq, int Nk, int Hq, int Hkv,
+                         int d, int causal, float scale, int schedule, void* workspace, size_t workspace_bytes,
+                         void* stream);
 ea_status ea_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                       const float* lse, void* dq, void* dk, void* dv, int B, int Nq, int Nk, int Hq, int Hkv,
                       int d, int causal, float scale, void* workspace, size_t workspace_bytes, void* stream);

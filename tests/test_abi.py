@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("ea_attn_fwd", "ea_attn_fwd_hd", "ea_attn_bwd", "ea_attn_bwd_workspace_size", "ea_attn_fwd_varlen", "ea_attn_fwd_varlen_ordered", "ea_varlen_lpt_order",
+    for n in ("ea_attn_fwd", "ea_attn_fwd_hd", "ea_attn_bwd", "ea_attn_bwd_ex", "ea_attn_bwd_workspace_size", "ea_attn_fwd_varlen", "ea_attn_fwd_varlen_ordered", "ea_varlen_lpt_order",
               "ea_attn_fwd_mx8", "ea_attn_fwd_mx8_tuned", "ea_attn_fwd_mx8_fmt", "ea_attn_decode_paged",
               "ea_decode_workspace_size", "ea_last_error"):
         assert n in names
@@ -66,7 +66,7 @@ def test_fwd_head_dim_pair_errors(lib):
     assert g(P, P, P, P, None, 1, 8, 8, 2, 2, 128, 64, 0, 0.1, None, None) == -2
     assert g(P, P, P, P, None, 1, 8, 8, 2, 2, 192, 0, 0, 0.1, None, None) == -1
     assert g(None, P, P, P, None, 1, 8, 8, 2, 2, 192, 128, 0, 0.1, None, None) == -1
-    for kern in (1, 3):                                   # (192, 128): ping-pong kernel (or its persistent form) only
+    for kern in (1, 3, 5):                                # (192, 128): ping-pong kernel (or its persistent form) only
         t = ea.tuning(kernel=kern)
         assert g(P, P, P, P, None, 1, 8, 8, 2, 2, 192, 128, 0, 0.1, ctypes.byref(t), None) == -2
     assert lib.ea_attn_fwd(P, P, P, P, None, 1, 8, 8, 2, 2, 192, 0, 0.1, None) == -2   # needs the _hd entry
@@ -78,7 +78,7 @@ def test_tuning_errors(lib):
     assert lib.ea_attn_fwd_tuned(P, P, P, P, None, 1, 8, 8, 2, 2, 128, 0, 0.1, ctypes.byref(t), None) == -1
     t = ea.tuning(rescale_log2=-1.0)
     assert lib.ea_attn_fwd_tuned(P, P, P, P, None, 1, 8, 8, 2, 2, 128, 0, 0.1, ctypes.byref(t), None) == -1
-    t = ea.tuning(kernel=5)
+    t = ea.tuning(kernel=6)
     assert lib.ea_attn_fwd_tuned(P, P, P, P, None, 1, 8, 8, 2, 2, 128, 0, 0.1, ctypes.byref(t), None) == -1
     d = ea.default_tuning()
     assert d.exp_mode == 0 and d.rescale_log2 == 8.0 and d.natural_order == 0 and d.kernel == 0
@@ -112,8 +112,8 @@ def test_mx8_tuning_errors(lib):
     assert call(ea.tuning(kernel=2)) == -2      # no ping-pong fp8 kernel
     assert call(ea.tuning(exp_mode=1)) == -2    # hardware exponential only
     assert call(ea.tuning(natural_order=1)) == -2
-    assert call(ea.tuning(kernel=4)) == -2      # no persistent fp8 kernel
-    assert call(ea.tuning(kernel=5)) == -1
+    assert call(ea.tuning(kernel=5)) == -2      # no unroll-KV fp8 kernel
+    assert call(ea.tuning(kernel=6)) == -1
 
 
 def test_decode_argument_errors(lib):
@@ -165,6 +165,8 @@ def test_bwd_argument_errors(lib):
     assert call(causal=3) == -1
     assert call(wsb=ws - 1) == -4 and "workspace" in _err(lib)
     assert call(wsp=None) == -4
+    g = lib.ea_attn_bwd_ex
+    assert g(P, P, P, P, P, P, P, P, P, 1, 8, 8, 2, 2, 128, 0, 0.1, 3, P, ws, None) == -1 and "schedule" in _err(lib)
 
 
 def test_binding_refuses_cpu_tensors():

@@ -25,11 +25,11 @@ NORM_TOL = 1e-2
 ELEM_TOL = 1e-2
 
 
-def run_bwd(inp, do_bits):
+def run_bwd(inp, do_bits, schedule=0):
     import exact_attention_amd as ea
     q, k, v = dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v)
     o, lse = ea.attn_fwd(q, k, v, inp.causal, inp.scale)
-    dq, dk, dv = ea.attn_bwd(q, k, v, o, dev_bf16(do_bits), lse, inp.causal, inp.scale)
+    dq, dk, dv = ea.attn_bwd(q, k, v, o, dev_bf16(do_bits), lse, inp.causal, inp.scale, schedule=schedule)
     torch.cuda.synchronize()
     return tuple(f64(host_bits(x)) for x in (dq, dk, dv))
 
@@ -116,3 +116,15 @@ def test_bwd_prefill_size_heads():
         check(dk[sl], rk, f"dk[b={b},h={h}]")
         check(dv[sl], rv, f"dv[b={b},h={h}]")
     assert all(np.isfinite(x).all() for x in (dq, dk, dv))
+
+
+def test_bwd_schedules_bitwise_equal():
+    """One workgroup per tile and the persistent schedule run the same per-tile
+    arithmetic: bitwise equal gradients (causal and not, GQA, d = 64)."""
+    for (B, N, Hq, Hkv, d, causal) in [(2, 700, 4, 2, 128, True), (1, 1500, 8, 8, 128, False), (2, 333, 2, 1, 64, True)]:
+        inp = W.dense(B, N, N, Hq, Hkv, d, causal, seed=560 + N)
+        do_bits = W.normal_bf16_bits(560 + N, W.STREAM_DO, (B, N, Hq, d))
+        a = run_bwd(inp, do_bits, schedule=1)
+        b = run_bwd(inp, do_bits, schedule=2)
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y)

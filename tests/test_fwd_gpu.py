@@ -55,8 +55,9 @@ SHAPES = [
 
 
 # 1: the 4-wave kernel, 2: the 8-wave ping-pong kernel, 3: the pipelined
-# kernel, 4: the ping-pong kernel in persistent form (each against the oracle)
-KERNELS = [1, 2, 3, 4]
+# kernel, 4: the ping-pong kernel in persistent form, 5: its unroll-KV form
+# (each against the oracle)
+KERNELS = [1, 2, 3, 4, 5]
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
@@ -261,12 +262,33 @@ def test_persistent_bitwise_equals_per_tile_launch():
     GQA, and (192, 128)."""
     import exact_attention_amd as ea
     cases = [((1, 300, 300, 2, 2, 128, True), None), ((2, 4096, 4096, 8, 4, 128, True), None),
-             ((1, 2000, 2000, 16, 16, 128, False), None), ((2, 1000, 1000, 4, 4, 192, True), 128)]
+             ((1, 2000, 2000, 16, 16, 128, False), None), ((2, 1000, 1000, 4, 4, 192, True), 128),
+             # tiles with fewer key tiles than the walk's minimum step count
+             ((3, 100, 100, 16, 8, 128, True), None), ((2, 130, 70, 24, 24, 128, False), None),
+             # d = 64; rows with no key; more tiles than workgroups, mixed lengths
+             ((2, 3000, 3000, 12, 4, 64, True), None), ((1, 1200, 300, 40, 8, 128, True), None),
+             ((1, 1, 1, 600, 600, 128, False), None)]
     for (B, Nq, Nk, Hq, Hkv, d, causal), dv in cases:
         inp = W.dense(B, Nq, Nk, Hq, Hkv, d, causal, seed=600 + Nq + Hq, dv=dv)
         o2, l2 = run_dense(inp, tuning=ea.tuning(kernel=2))
-        o4, l4 = run_dense(inp, tuning=ea.tuning(kernel=4))
-        log(f"persistent vs per-tile {B, Nq, Nk, Hq, Hkv, d, dv, causal}: equal={np.array_equal(o2, o4)}")
+        for kern in ((4,) if dv not in (None, d) else (4, 5)):
+            o4, l4 = run_dense(inp, tuning=ea.tuning(kernel=kern))
+            log(f"kernel {kern} vs per-tile {B, Nq, Nk, Hq, Hkv, d, dv, causal}: equal={np.array_equal(o2, o4)}")
+            assert np.array_equal(o2, o4) and np.array_equal(l2, l4)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_persistent_varlen_bitwise_equals_per_tile_launch(causal):
+    """Packed sequences through the persistent walk: lengths from 1 row to
+    several blocks (tiles of every step count, empty-looking tails), bitwise
+    equal to one workgroup per tile."""
+    import exact_attention_amd as ea
+    L = [1, 700, 64, 2000, 3, 255, 256, 257, 1500, 90]
+    inp = W.varlen(L, L, 6, 2, 128, causal, seed=95)
+    o2, l2 = run_varlen(inp, tuning=ea.tuning(kernel=2))
+    for kern in (4, 5):
+        o4, l4 = run_varlen(inp, tuning=ea.tuning(kernel=kern))
+        log(f"kernel {kern} varlen causal={causal}: equal={np.array_equal(o2, o4)}")
         assert np.array_equal(o2, o4) and np.array_equal(l2, l4)
 
 

@@ -21,8 +21,8 @@ NORM_TOL = 5e-2
 LSE_TOL = 5e-2
 
 
-# the 4-wave kernel and the 8-wave software-pipelined one
-KERNELS = [1, 3]
+# the 4-wave kernel, the 8-wave software-pipelined one and its persistent form
+KERNELS = [1, 3, 4]
 
 
 def run_mx8(m, kernel=0):
