@@ -152,6 +152,30 @@ def mfma_loop_rate(torch, ea, dev, reps=5):
     return flops / (float(np.median(ts)) * 1e-3) / 1e12
 
 
+def stream_read_rate(torch, ea, dev, reps=5):
+    """GB/s of the library's streaming-read calibration (ea_test_stream_read:
+    4 GiB read once by 8192 workgroups of 256 threads, 16 loads of 16 B in
+    flight per thread), best of reps launches, or None."""
+    nbytes, blocks = 4 << 30, 8192
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    out = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+    s = torch.cuda.current_stream(dev)
+    best = None
+    for i in range(reps + 1):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        if ea.lib().ea_test_stream_read(ea._ptr(buf), nbytes, ea._ptr(out), blocks, s.cuda_stream) != 0:
+            return None
+        e1.record(s)
+        torch.cuda.synchronize()
+        if i:
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+    del buf
+    return nbytes / (best * 1e-3) / 1e9
+
+
 def prefill_flops(B, H, N, d, dv=None):
     """Causal forward FLOPs, counted as half of the full N x N work:
     2 N^2 d (scores) + 2 N^2 dv (P V) per (batch, head), halved."""
@@ -405,6 +429,11 @@ def main():
                 out[key]["sustained"] = {
                     "what": f"vendor BLAS {dt_name} GEMM {n}^3 on this GPU", "unit": "TFLOP/s",
                     "value": r, "frac": (out[key]["achieved"] / r) if r else None}
+        if "roofline_decode" in out:
+            r = stream_read_rate(torch, ea, dev)
+            out["roofline_decode"]["sustained"] = {
+                "what": "streaming 16-B read of 4 GiB on all CUs (ea_test_stream_read), this GPU",
+                "unit": "GB/s", "value": r, "frac": (out["roofline_decode"]["achieved"] / r) if r else None}
         if "roofline" in out:
             r = mfma_loop_rate(torch, ea, dev)
             out["roofline"]["mfma_loop"] = {

@@ -59,6 +59,7 @@ _SIGNATURES = {
     "ea_attn_decode_paged": ([_c_void_p] * 7 + [_c_int] * 7 + [_c_float, _c_int, _c_void_p, _c_size_t, _c_void_p], _c_int),
     "ea_test_exp2": ([_c_void_p, _c_void_p, _c_int, _c_int, _c_void_p], _c_int),
     "ea_test_mfma_loop": ([_c_void_p, _c_int, _c_int, _c_void_p], _c_int),
+    "ea_test_stream_read": ([_c_void_p, _c_size_t, _c_void_p, _c_int, _c_void_p], _c_int),
 }
 
 _lib = None

@@ -39,7 +39,34 @@ __global__ __launch_bounds__(512) void mfma_loop_kernel(float* out, int iters) {
   out[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// A streaming read: each thread reads kStreamUnroll 16-byte chunks per pass
+// (grid-stride, non-temporal) and folds them into one value, so the launch
+// measures the HBM read rate a plain kernel sustains on this device.
+constexpr int kStreamUnroll = 16;
+__global__ __launch_bounds__(256) void stream_read_kernel(const ea::i32x4* __restrict__ p, size_t n16, int* out) {
+  const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t nt = (size_t)gridDim.x * blockDim.x;
+  ea::i32x4 acc = {0, 0, 0, 0};
+  for (size_t base = tid; base + (kStreamUnroll - 1) * nt < n16; base += kStreamUnroll * nt) {
+    ea::i32x4 v[kStreamUnroll];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) v[u] = __builtin_nontemporal_load(p + base + u * nt);
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) acc ^= v[u];
+  }
+  out[tid] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
 }  // namespace
+
+extern "C" ea_status ea_test_stream_read(const void* buf, size_t bytes, int* out, int blocks, void* stream) {
+  if (buf == nullptr || out == nullptr || blocks <= 0 || blocks > 65536) return EA_ERR_INVALID;
+  const size_t pass = (size_t)16 * kStreamUnroll * 256 * (size_t)blocks;  // bytes per grid pass
+  if (bytes == 0 || bytes % pass != 0) return EA_ERR_INVALID;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                     (const ea::i32x4*)buf, bytes / 16, out);
+  return hipGetLastError() == hipSuccess ? EA_OK : EA_ERR_HIP;
+}
 
 extern "C" ea_status ea_test_mfma_loop(float* out, int blocks, int iters, void* stream) {
   if (out == nullptr || blocks <= 0 || iters <= 0 || blocks > 65536) return EA_ERR_INVALID;

@@ -34,6 +34,17 @@ ea_status ea_test_exp2(const float* x, float* y, int n, int mode, void* stream);
  */
 ea_status ea_test_mfma_loop(float* out, int blocks, int iters, void* stream);
 
+/*
+ * ea_test_stream_read -- calibration of the HBM read rate: blocks workgroups
+ * of 256 threads read the device buffer buf once, 16 bytes per load, 16 loads
+ * in flight per thread (grid-stride, non-temporal), and fold it into one value
+ * per thread. Bytes read per launch = bytes.
+ *   out: device int array of blocks * 256 elements (written, meaningless
+ *   beyond keeping the reads alive). 0 < blocks <= 65536 and bytes a positive
+ *   multiple of 65536 * blocks (one grid pass); otherwise EA_ERR_INVALID.
+ */
+ea_status ea_test_stream_read(const void* buf, size_t bytes, int* out, int blocks, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -185,3 +185,13 @@ def test_varlen_lpt_order_argument_errors(lib):
     assert f(P, P, 4, 2, 256, P, P, None) == -1
     assert f(P, P, 4, 1, 100, P, P, None) == -1        # not a forward row block
     assert f(P, P, 1 << 17, 1, 256, P, P, None) == -2  # quadratic ranking: capped
+
+
+def test_stream_read_errors(lib):
+    f = lib.ea_test_stream_read
+    out = ctypes.c_void_p(1)
+    assert f(None, 1 << 20, out, 16, None) == -1
+    assert f(P, 1 << 20, None, 16, None) == -1
+    assert f(P, 1 << 20, out, 0, None) == -1
+    assert f(P, 1000, out, 1, None) == -1          # not a whole grid pass
+    assert f(P, 0, out, 1, None) == -1

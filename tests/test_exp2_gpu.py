@@ -55,3 +55,21 @@ def test_mfma_loop_calibration_runs():
     assert ea.lib().ea_test_mfma_loop(ea._ptr(out), 8, 10, None) == 0
     torch.cuda.synchronize()
     assert torch.isfinite(out).all()
+
+
+def test_stream_read_calibration_reads_every_byte():
+    """The streaming-read calibration used by bench.py visits every 16-byte
+    chunk once: with all chunks zero but one, exactly one thread's folded
+    value is nonzero, and it equals that chunk's words folded by XOR."""
+    import exact_attention_amd as ea
+    blocks = 16
+    nbytes = 65536 * blocks * 2                       # two grid passes
+    buf = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda")
+    buf[4 * 12345: 4 * 12345 + 4] = torch.tensor([1, 2, 4, 8], dtype=torch.int32)
+    out = torch.full((blocks * 256,), -1, dtype=torch.int32, device="cuda")
+    assert ea.lib().ea_test_stream_read(ea._ptr(buf), nbytes, ea._ptr(out), blocks, None) == 0
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    nz = np.nonzero(o)[0]
+    assert len(nz) == 1 and o[nz[0]] == (1 ^ 2 ^ 4 ^ 8)
+    assert nz[0] == 12345 % (blocks * 256)             # chunk c is read by thread c mod (threads)
