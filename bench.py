@@ -74,7 +74,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle time budget per leg")
     p.add_argument("--prefill-kernel", type=int, default=0,
                    help="forward kernel for the bf16 prefill (EA_FWD_KERNEL_*; 0 = library default)")
-    p.add_argument("--prefill-dims", choices=["128,128", "192,128"], default="128,128",
+    p.add_argument("--prefill-dims", choices=["128,128", "192,128", "64,64"], default="128,128",
                    help="head dims (d_qk, d_v) of the bf16 prefill forward")
     p.add_argument("--fp8-kernel", type=int, default=0, help="fp8 forward kernel (EA_FWD_KERNEL_*; 0 = default)")
     p.add_argument("--bwd-schedule", type=int, default=0, help="backward schedule (EA_BWD_SCHEDULE_*; 0 = default)")
@@ -371,9 +371,10 @@ def main():
                            "frac": tf / PEAK_BF16_TFLOPS,
                            "kernel": ("ea::fwd_pp_unrollkv_kernel" if args.prefill_kernel == 5 else
                                       "ea::fwd_pp_persistent_kernel"
-                                      if args.prefill_kernel == 4 or (args.prefill_kernel == 0 and d == d_v == 128) else
-                                      "ea::fwd_pp_kernel" if args.prefill_kernel == 2 or d != d_v else
-                                      f"forward kernel {args.prefill_kernel}") + f"<{d}, {d_v}, causal>"}
+                                      if args.prefill_kernel == 4 or (args.prefill_kernel == 0 and d >= 128) else
+                                      "ea::fwd_pp_kernel" if args.prefill_kernel == 2 else
+                                      "ea::fwd_bf16_kernel" if args.prefill_kernel in (0, 1) else
+                                      "ea::fwd_sp_kernel") + f"<{d}, {d_v}, causal>"}
         out["roofline"]["traffic"] = TRAFFIC.get(out["roofline"]["kernel"])
     if run_decode:
         t_dc = np.array([e[2].elapsed_time(e[3]) for e in evs])

@@ -68,7 +68,9 @@ hipError_t dispatch_fwd(ea::FwdArgs a, int d, int dv, bool causal, bool varlen, 
                         hipStream_t s) {
   if (d != dv) {
     a.n_mb = (a.n_mb + 1) / 2;
-    if (tt.kernel == EA_FWD_KERNEL_PERSISTENT) {
+    // AUTO: the persistent form for dense inputs here too (1.36 against
+    // 1.39 ms at B=4 H=16 N=8192 causal)
+    if (tt.kernel == EA_FWD_KERNEL_PERSISTENT || (tt.kernel == EA_FWD_KERNEL_AUTO && !varlen)) {
       a.persist_wgs = persistent_workgroups();
       if (a.persist_wgs <= 0) return hipErrorInvalidDevice;
     }

@@ -74,8 +74,9 @@ typedef struct {
 } ea_fwd_tuning;
 
 /* Forward kernels (same results up to rounding order):
- *   EA_FWD_KERNEL_AUTO      for d = 128 the ping-pong kernel, in persistent form
- *                           for dense inputs; else the 4-wave one
+ *   EA_FWD_KERNEL_AUTO      for d_qk = 128 or 192 the ping-pong kernel, in
+ *                           persistent form for dense inputs; for d = 64 the
+ *                           4-wave one
  *   EA_FWD_KERNEL_4WAVE     4 waves x 32 query rows, two workgroups per CU
  *   EA_FWD_KERNEL_PINGPONG  8 waves x 32 rows in two groups that alternate
  *                           matrix products and softmax on each SIMD
