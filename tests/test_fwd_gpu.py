@@ -304,3 +304,25 @@ def test_persistent_prefill_workload_sampled():
         assert_o_close(o[b, rows, h, :], ro, what=f"o[b={b},h={h}]")
         assert_lse_close(lse[b, h, rows], rl, what=f"lse[b={b},h={h}]")
     assert np.isfinite(o).all() and np.isfinite(lse).all()
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_varlen_empty_sequences_all_kernels(causal):
+    """Packed sequences with no query rows, with no keys (their rows get O = 0,
+    lse = -inf), or both, between ordinary ones: every kernel against the
+    oracle, and the persistent and unroll-KV forms bit for bit against the
+    ping-pong kernel."""
+    import exact_attention_amd as ea
+    Lq = [5, 0, 300, 64, 0, 200, 1, 257]
+    Lk = [0, 10, 300, 0, 0, 260, 700, 257]
+    inp = W.varlen(Lq, Lk, 4, 2, 128, causal, seed=97)
+    ro, rl = oracle.attention_varlen(f64(inp.q), f64(inp.k), f64(inp.v), inp.cu_q, inp.cu_k, causal, inp.scale)
+    res = {}
+    for kern in KERNELS:
+        o, lse = run_varlen(inp, poison_rows=33, tuning=ea.tuning(kernel=kern))
+        log(f"varlen empty sequences causal={causal} kernel={kern}")
+        assert_o_close(o, ro, what=f"o[kernel {kern}]")
+        assert_lse_close(lse, rl, what=f"lse[kernel {kern}]")
+        res[kern] = (o, lse)
+    for kern in (4, 5):
+        assert np.array_equal(res[kern][0], res[2][0]) and np.array_equal(res[kern][1], res[2][1])
