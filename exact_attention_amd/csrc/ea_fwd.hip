@@ -240,7 +240,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
     // ---- row max (raw scores; scale > 0 commutes with max)
     float mx = kNegInf;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, __builtin_fmaxf(s0[i], s1[i]));
+    // max(max(acc, a), b) per pair of scores folds into one three-input max
+    for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s0[i]), s1[i]);
     mx = max_with_partner32(mx);
     const float m_new = __builtin_fmaxf(m_run, mx * sl);
     // ---- lazy rescale, wave-uniform

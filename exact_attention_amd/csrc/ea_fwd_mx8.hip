@@ -256,7 +256,8 @@ __global__ __launch_bounds__(256, 2) void fwd_mx8_kernel(Mx8Args a) {
     // ---- online softmax (fp32), lazy rescale with threshold tau (log2)
     float mx = kNegInf;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, __builtin_fmaxf(s0[i], s1[i]));
+    // max(max(acc, a), b) per pair of scores folds into one three-input max
+    for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s0[i]), s1[i]);
     mx = max_with_partner32(mx);
     const float m_new = __builtin_fmaxf(m_run, mx * sl);
     if (__ballot(m_new > m_run + a.tau)) {

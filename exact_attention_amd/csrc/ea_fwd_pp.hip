@@ -123,8 +123,8 @@ struct PpCore {
   static constexpr int NDT = DV / 32;  // 32-wide d tiles of O^T
 
   int lane, hh, c, w, grp;
-  // loop-invariant LDS element offsets of this lane's operand reads (see the
-  // 4-wave kernel): K rows c and c + 32, V^T transposed reads
+  // LDS byte offsets of this lane's operand reads (see the 4-wave kernel):
+  // K rows c and c + 32, V^T transposed reads
   int k_off[D / 16];
   int v_off[NDT][2];
   bf16x8 qf[D / 16];  // Q^T operand (B of S^T = K Q^T)
@@ -141,13 +141,13 @@ struct PpCore {
     c = lane & 31;
     grp = w >> 2;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) k_off[kk] = tile_off<D>(c, 16 * kk + 8 * hh);
+    for (int kk = 0; kk < D / 16; ++kk) k_off[kk] = 2 * tile_off<D>(c, 16 * kk + 8 * hh);
     const int tr_row = 4 * hh + ((lane & 15) >> 2);
     const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      v_off[dt][0] = tile_off<DV>(tr_row, 32 * dt + tr_col);
-      v_off[dt][1] = tile_off<DV>(tr_row + 8, 32 * dt + tr_col);
+      v_off[dt][0] = 2 * tile_off<DV>(tr_row, 32 * dt + tr_col);
+      v_off[dt][1] = 2 * tile_off<DV>(tr_row + 8, 32 * dt + tr_col);
     }
     s0 = f32x16{};
     s1 = f32x16{};
@@ -179,24 +179,24 @@ struct PpCore {
   // end hold zeros from the DMA, and the V stage read at the first step is
   // zeroed, so the extra products add exact zeros.
   __device__ __forceinline__ void mfma_part(const EA_LDS uint16_t* ks, const EA_LDS uint16_t* vs) {
-    // The lane offsets pass through an empty asm here so that the stage base
-    // is added inside this block, where it folds into the ds_read offset
-    // field, instead of a hoisted register copy per stage and offset.
-    int ko[D / 16], vo[NDT][2];
+    // The lane offsets pass through an empty asm in place, so to the compiler
+    // they change every step: the stage base is then added here, where it
+    // folds into the ds_read offset field, instead of a hoisted register per
+    // stage and offset, and no copy or shift is made per step.
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      ko[kk] = launder(k_off[kk]);
-    }
+    for (int kk = 0; kk < D / 16; ++kk) k_off[kk] = launder(k_off[kk]);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      vo[dt][0] = launder(v_off[dt][0]);
-      vo[dt][1] = launder(v_off[dt][1]);
+      v_off[dt][0] = launder(v_off[dt][0]);
+      v_off[dt][1] = launder(v_off[dt][1]);
     }
+    const EA_LDS char* kb = (const EA_LDS char*)ks;
+    const EA_LDS char* vb = (const EA_LDS char*)vs;
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      const bf16x8 ka0 = lds_load<bf16x8>(ks + ko[kk]);
-      const bf16x8 ka1 = lds_load<bf16x8>(ks + ko[kk] + 32 * D);
+      const bf16x8 ka0 = lds_load<bf16x8>(kb + k_off[kk]);
+      const bf16x8 ka1 = lds_load<bf16x8>(kb + k_off[kk] + 64 * D);
       s0 = mfma32x32x16(ka0, qf[kk], kk == 0 ? f32x16{} : s0);
       s1 = mfma32x32x16(ka1, qf[kk], kk == 0 ? f32x16{} : s1);
     }
@@ -204,8 +204,8 @@ struct PpCore {
     for (int st = 0; st < 4; ++st) {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const i16x4 lo = ds_read_tr16(vs + vo[dt][0] + 16 * st * DV);
-        const i16x4 hi = ds_read_tr16(vs + vo[dt][1] + 16 * st * DV);
+        const i16x4 lo = ds_read_tr16((const EA_LDS uint16_t*)(vb + v_off[dt][0] + 32 * st * DV));
+        const i16x4 hi = ds_read_tr16((const EA_LDS uint16_t*)(vb + v_off[dt][1] + 32 * st * DV));
         const i32x4 t = {__builtin_bit_cast(i32x2, lo)[0], __builtin_bit_cast(i32x2, lo)[1],
                          __builtin_bit_cast(i32x2, hi)[0], __builtin_bit_cast(i32x2, hi)[1]};
         oacc[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, t), pb[st], oacc[dt]);
@@ -257,7 +257,8 @@ struct PpCore {
     }
     float mx = kNegInf;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, __builtin_fmaxf(s0[i], s1[i]));
+    // max(max(acc, a), b) per pair of scores folds into one three-input max
+    for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s0[i]), s1[i]);
     mx = max_with_partner32(mx);
     const float m_new = __builtin_fmaxf(m_run, mx * sl);
     if (__ballot(m_new > m_run + tau)) {
@@ -574,7 +575,7 @@ __device__ __forceinline__ void pp_walk(const FwdArgs& a) {
   auto read_q = [&]() __attribute__((always_inline)) {
     const EA_LDS uint16_t* qb = (const EA_LDS uint16_t*)qs + (w & 3) * TILE + 32 * grp * D;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) cr.qf[kk] = lds_load<bf16x8>(qb + cr.k_off[kk]);
+    for (int kk = 0; kk < D / 16; ++kk) cr.qf[kk] = lds_load<bf16x8>((const EA_LDS char*)qb + cr.k_off[kk]);
     wait_lgkm0();  // the region is refilled two steps later
   };
   auto kstage = [&](int r) __attribute__((always_inline)) -> EA_LDS uint16_t* {
