@@ -45,10 +45,10 @@ PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 # the factors a plain 1 GiB copy reads), keyed by the kernel they were taken
 # on; a kernel not listed reports traffic null. Sources: profiles/*_counters.md.
 TRAFFIC = {
-    # fwd_pp_persistent_kernel<128, 128, causal>: 215,727 KiB fetched, 134,287 KiB written
-    "ea::fwd_pp_persistent_kernel<128, 128, causal>": 579_318_784,
-    # fwd_pp_kernel<128, 128, causal>: 234,836 KiB fetched, 134,093 KiB written
-    "ea::fwd_pp_kernel<128, 128, causal>": 618_255_360,
+    # fwd_pp_persistent_kernel<128, 128, causal>: 216,150 KiB fetched, 134,314 KiB written
+    "ea::fwd_pp_persistent_kernel<128, 128, causal>": 580_212_736,
+    # fwd_pp_kernel<128, 128, causal>: 239,567 KiB fetched, 133,467 KiB written
+    "ea::fwd_pp_kernel<128, 128, causal>": 627_302_400,
     # fwd_mx8_sp_persistent_kernel<causal, e4m3>: 165,478 KiB fetched, 137,988 KiB written
     "ea::fwd_mx8_sp_persistent_kernel<causal, e4m3>": 480_198_656,
     # decode_split_kernel<true> + combine: 2,373,166 KiB fetched, 5,807 KiB written
