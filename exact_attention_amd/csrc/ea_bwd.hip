@@ -491,19 +491,27 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, const int xcd, const
         EA_LDS f32x4* xp = (EA_LDS f32x4*)pxch[k & 1][pr];
         float p[16];
         // element i = row rbase + 8 (i / 4) + 4 hh + i % 4 of key kj
+        auto probs = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const f32x4 l4 = lds_load<f32x4>(lst + 32 * rs + 8 * i4 + 4 * hh);
-          f32x4 p4;
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const f32x4 l4 = lds_load<f32x4>(lst + 32 * rs + 8 * i4 + 4 * hh);
+            f32x4 p4;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            bool ok = true;
-            if constexpr (CAUSAL) ok = kj <= rbase + 8 * i4 + 4 * hh + e + off;
-            p4[e] = ok ? exp2_hw(__builtin_fmaf(x[4 * i4 + e], sl, -l4[e])) : 0.f;
-            p[4 * i4 + e] = p4[e];
+            for (int e = 0; e < 4; ++e) {
+              bool ok = true;
+              if constexpr (decltype(masked)::value) ok = kj <= rbase + 8 * i4 + 4 * hh + e + off;
+              p4[e] = ok ? exp2_hw(__builtin_fmaf(x[4 * i4 + e], sl, -l4[e])) : 0.f;
+              p[4 * i4 + e] = p4[e];
+            }
+            lds_store<f32x4>(xp + 64 * i4 + lane, p4);
           }
-          lds_store<f32x4>(xp + 64 * i4 + lane, p4);
-        }
+        };
+        // wave-uniform: the wave's last key is at or before the causal limit
+        // of the slice's first row, so no element of the slice is masked
+        if (!CAUSAL || k_lo + pr * 32 + 31 <= rbase + off)
+          probs(std::integral_constant<bool, false>{});
+        else
+          probs(std::integral_constant<bool, true>{});
         pack16(p, pk);
         if (rs == 1 && ++qt == qt0 + nqt) {
           qt = qt0;
