@@ -168,14 +168,14 @@ __global__ __launch_bounds__(512, 1) void fwd_sp_kernel(FwdArgs a) {
   // 4-wave kernel): K rows c and c + 32, V^T transposed reads
   int k_off[D / 16];
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) k_off[kk] = tile_off<D>(c, 16 * kk + 8 * hh);
+  for (int kk = 0; kk < D / 16; ++kk) k_off[kk] = 2 * tile_off<D>(c, 16 * kk + 8 * hh);  // bytes
   const int tr_row = 4 * hh + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   int v_off[NDT][2];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {
-    v_off[dt][0] = tile_off<D>(tr_row, 32 * dt + tr_col);
-    v_off[dt][1] = tile_off<D>(tr_row + 8, 32 * dt + tr_col);
+    v_off[dt][0] = 2 * tile_off<D>(tr_row, 32 * dt + tr_col);  // bytes
+    v_off[dt][1] = 2 * tile_off<D>(tr_row + 8, 32 * dt + tr_col);
   }
   const int wave_first_q = wrow;
 
@@ -235,27 +235,27 @@ __global__ __launch_bounds__(512, 1) void fwd_sp_kernel(FwdArgs a) {
                    __attribute__((always_inline)) -> bool {
     const EA_LDS uint16_t* ks = kstage((r + 1) % 3);
     const EA_LDS uint16_t* vs = vstage((r + 2) % 3);
-    // The lane offsets pass through an empty asm here so that the stage base
-    // is added inside this block, where it folds into the ds_read offset
-    // field, instead of a hoisted register copy per stage and offset.
-    int ko[D / 16], vo[NDT][2];
+    // The lane offsets (bytes) pass through an empty asm in place, so to the
+    // compiler they change every step: the stage base is added inside this
+    // block, where it folds into the ds_read offset field, instead of a
+    // hoisted register per stage and offset, and no copy is made per step.
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) ko[kk] = launder(k_off[kk]);
+    for (int kk = 0; kk < D / 16; ++kk) k_off[kk] = launder(k_off[kk]);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      vo[dt][0] = launder(v_off[dt][0]);
-      vo[dt][1] = launder(v_off[dt][1]);
+      v_off[dt][0] = launder(v_off[dt][0]);
+      v_off[dt][1] = launder(v_off[dt][1]);
     }
     // operand of MFMA j: j < NS reads K row block (j mod 2) at d slice j / 2;
     // j >= NS reads V^T for P slice st and d tile dt
     bf16x8 opnd[NMF];
     auto read_operand = [&](int j) __attribute__((always_inline)) {
       if (j < NS) {
-        opnd[j] = lds_load<bf16x8>(ks + ko[j >> 1] + 32 * D * (j & 1));
+        opnd[j] = lds_load<bf16x8>((const EA_LDS char*)ks + k_off[j >> 1] + 64 * D * (j & 1));
       } else {
         const int st = (j - NS) / NDT, dt = (j - NS) % NDT;
-        const i16x4 lo = ds_read_tr16(vs + vo[dt][0] + 16 * st * D);
-        const i16x4 hi = ds_read_tr16(vs + vo[dt][1] + 16 * st * D);
+        const i16x4 lo = ds_read_tr16((const EA_LDS uint16_t*)((const EA_LDS char*)vs + v_off[dt][0] + 32 * st * D));
+        const i16x4 hi = ds_read_tr16((const EA_LDS uint16_t*)((const EA_LDS char*)vs + v_off[dt][1] + 32 * st * D));
         const i32x4 t = {__builtin_bit_cast(i32x2, lo)[0], __builtin_bit_cast(i32x2, lo)[1],
                          __builtin_bit_cast(i32x2, hi)[0], __builtin_bit_cast(i32x2, hi)[1]};
         opnd[j] = __builtin_bit_cast(bf16x8, t);
@@ -382,8 +382,8 @@ __global__ __launch_bounds__(512, 1) void fwd_sp_kernel(FwdArgs a) {
   __syncthreads();
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
-    const bf16x8 ka0 = lds_load<bf16x8>((EA_LDS uint16_t*)ks0 + k_off[kk]);
-    const bf16x8 ka1 = lds_load<bf16x8>((EA_LDS uint16_t*)ks0 + k_off[kk] + 32 * D);
+    const bf16x8 ka0 = lds_load<bf16x8>((const EA_LDS char*)ks0 + k_off[kk]);
+    const bf16x8 ka1 = lds_load<bf16x8>((const EA_LDS char*)ks0 + k_off[kk] + 64 * D);
     sc0 = mfma32x32x16(ka0, qf[kk], kk == 0 ? f32x16{} : sc0);
     sc1 = mfma32x32x16(ka1, qf[kk], kk == 0 ? f32x16{} : sc1);
   }
