@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libexactatt
 
 EA_EXP_HW, EA_EXP_POLY, EA_EXP_HYBRID = 0, 1, 2
 EA_FWD_KERNEL_AUTO, EA_FWD_KERNEL_4WAVE, EA_FWD_KERNEL_PINGPONG, EA_FWD_KERNEL_PIPELINED = 0, 1, 2, 3
+EA_FWD_KERNEL_PERSISTENT, EA_FWD_KERNEL_UNROLL_KV = 4, 5
 
 _c_int, _c_float, _c_void_p, _c_size_t = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
@@ -60,6 +61,10 @@ _SIGNATURES = {
     "ea_test_exp2": ([_c_void_p, _c_void_p, _c_int, _c_int, _c_void_p], _c_int),
     "ea_test_mfma_loop": ([_c_void_p, _c_int, _c_int, _c_void_p], _c_int),
     "ea_test_stream_read": ([_c_void_p, _c_size_t, _c_void_p, _c_int, _c_void_p], _c_int),
+    "ea_test_pair_probe": ([_c_void_p, _c_int, _c_int, _c_int, ctypes.c_longlong, _c_void_p], _c_int),
+    "ea_test_fwd_rescale_stats_len": ([_c_int] * 3, _c_size_t),
+    "ea_test_fwd_rescale_stats": ([_c_void_p] * 5 + [_c_int] * 6 + [_c_float, _c_float, _c_void_p, _c_size_t,
+                                                                   _c_void_p], _c_int),
 }
 
 _lib = None
@@ -94,17 +99,37 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _need(t: torch.Tensor, name: str, dtype, dim: int):
+def _need(t, name: str, dtype, dim: int):
+    """Type, dtype, rank and layout of one tensor argument (device checked
+    separately, after the shapes, by _on_gpu)."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if t.dim() != dim:
         raise ValueError(f"{name} must have {dim} dims, got shape {tuple(t.shape)}")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be on a GPU")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _shape(t, name: str, shape) -> None:
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _on_gpu(*named) -> None:
+    """Every tensor on the same GPU (the kernels dereference all pointers on
+    the device of the first)."""
+    dev = None
+    for name, t in named:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be on a GPU")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
 
 
 def default_tuning() -> FwdTuning:
@@ -116,8 +141,9 @@ def default_tuning() -> FwdTuning:
 def tuning(exp_mode: int = EA_EXP_HW, rescale_log2: float = 8.0, natural_order: int = 0,
            kernel: int = 0) -> FwdTuning:
     """Forward tuning; kernel: 0 auto, 1 the 4-wave kernel, 2 the 8-wave ping-pong kernel,
-    3 the 8-wave software-pipelined kernel, 4 the ping-pong kernel in persistent form,
-    5 that persistent form with the K/V pipeline running on across row blocks (unroll-KV)."""
+    3 the 8-wave software-pipelined kernel (MX fp8 only), 4 the ping-pong kernel in persistent
+    form (the fp8 pipelined kernel in persistent form for attn_fwd_mx8), 5 that persistent form
+    with the K/V pipeline running on across row blocks (unroll-KV; bf16 only)."""
     return FwdTuning(exp_mode, rescale_log2, natural_order, kernel)
 
 
@@ -134,6 +160,13 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, *, tunin
     dv = v.shape[3]
     if tuple(v.shape[:3]) != tuple(k.shape[:3]) or k.shape[0] != B or k.shape[3] != d:
         raise ValueError("k must be [B, Nk, Hkv, d] matching q and v [B, Nk, Hkv, dv]")
+    if out is not None:
+        _need(out, "out", torch.bfloat16, 4)
+        _shape(out, "out", (B, Nq, Hq, dv))
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 3)
+        _shape(lse, "lse", (B, Hq, Nq))
+    _on_gpu(("q", q), ("k", k), ("v", v), ("out", out), ("lse", lse))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     o = out if out is not None else torch.empty((B, Nq, Hq, dv), dtype=q.dtype, device=q.device)
@@ -154,6 +187,7 @@ def varlen_lpt_order(cu_seqlens_q, cu_seqlens_k, causal: bool, block_m: int = 25
     S = cu_seqlens_q.shape[0] - 1
     if cu_seqlens_k.shape[0] != S + 1:
         raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    _on_gpu(("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k))
     order = torch.empty(S, dtype=torch.int32, device=cu_seqlens_q.device)
     weights = torch.empty(S, dtype=torch.int32, device=cu_seqlens_q.device)
     st = lib().ea_varlen_lpt_order(_ptr(cu_seqlens_q), _ptr(cu_seqlens_k), S, int(bool(causal)), int(block_m),
@@ -178,15 +212,22 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, caus
     _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1)
     Tq, Hq, d = q.shape
     Tk, Hkv, _ = k.shape
+    if k.shape[2] != d:
+        raise ValueError(f"k must be [Tk, Hkv, {d}] (q's head dim), got {tuple(k.shape)}")
+    _shape(v, "v", k.shape)
     S = cu_seqlens_q.shape[0] - 1
+    if S < 1:
+        raise ValueError("cu_seqlens_q must hold at least two entries")
     if cu_seqlens_k.shape[0] != S + 1:
         raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    if seq_order is not None and seq_order.shape[0] != S:
+        raise ValueError("seq_order must have one entry per sequence")
+    _on_gpu(("q", q), ("k", k), ("v", v), ("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k),
+            ("seq_order", seq_order))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     o = torch.empty_like(q)
     lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device) if want_lse else None
-    if seq_order is not None and seq_order.shape[0] != S:
-        raise ValueError("seq_order must have one entry per sequence")
     st = lib().ea_attn_fwd_varlen_ordered(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens_q),
                                           _ptr(cu_seqlens_k), S, Tq, Tk, int(max_seqlen_q), Hq, Hkv, d,
                                           int(bool(causal)), float(scale), _ptr(seq_order),
@@ -205,10 +246,19 @@ def attn_fwd_mx8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = True, sca
     e8m0. Returns (o bf16, lse)."""
     if fmt not in FP8_FORMATS:
         raise ValueError(f"fmt must be one of {sorted(FP8_FORMATS)}")
-    for t, n in ((q8, "q8"), (k8, "k8"), (v8, "v8"), (q_scale, "q_scale"), (k_scale, "k_scale"), (v_scale, "v_scale")):
+    named = (("q8", q8), ("k8", k8), ("v8", v8), ("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale))
+    for n, t in named:
         _need(t, n, torch.uint8, 4)
     B, N, Hq, d = q8.shape
     Hkv = k8.shape[2]
+    _shape(k8, "k8", (B, N, Hkv, d))
+    _shape(v8, "v8", (B, N, Hkv, d))
+    if d % 32 or N % 32:
+        raise ValueError(f"N ({N}) and d ({d}) must be multiples of 32 (the MX block)")
+    _shape(q_scale, "q_scale", (B, N, Hq, d // 32))
+    _shape(k_scale, "k_scale", (B, N, Hkv, d // 32))
+    _shape(v_scale, "v_scale", (B, N // 32, Hkv, d))
+    _on_gpu(*named)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     o = torch.empty((B, N, Hq, d), dtype=torch.bfloat16, device=q8.device)
@@ -233,8 +283,13 @@ def attn_bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = 
     _, Nk, Hkv, _ = k.shape
     if tuple(v.shape) != tuple(k.shape) or tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape):
         raise ValueError("shapes: q, o, dout [B,Nq,Hq,d]; k, v [B,Nk,Hkv,d]")
+    if k.shape[0] != B or k.shape[3] != d:
+        raise ValueError(f"k must be [{B}, Nk, Hkv, {d}] to match q, got {tuple(k.shape)}")
     if tuple(lse.shape) != (B, Hq, Nq):
         raise ValueError("lse must be [B, Hq, Nq]")
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, 1)
+    _on_gpu(("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("lse", lse), ("workspace", workspace))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     need = int(lib().ea_attn_bwd_workspace_size(B, Hq, Nq))
@@ -264,9 +319,19 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, page_size: int
     _need(block_table, "block_table", torch.int32, 2)
     _need(seq_lens, "seq_lens", torch.int32, 1)
     B, Hq, d = q.shape
-    P, ps, Hkv, _ = k_cache.shape
+    P, ps, Hkv, dk = k_cache.shape
+    _shape(v_cache, "v_cache", k_cache.shape)
+    if dk != d:
+        raise ValueError(f"k_cache head dim {dk} differs from q's {d}")
+    if block_table.shape[0] != B:
+        raise ValueError(f"block_table must have {B} rows (one per sequence), got {block_table.shape[0]}")
+    _shape(seq_lens, "seq_lens", (B,))
     if page_size is not None and page_size != ps:
         raise ValueError("page_size does not match k_cache.shape[1]")
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, 1)
+    _on_gpu(("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("block_table", block_table),
+            ("seq_lens", seq_lens), ("workspace", workspace))
     max_pages = block_table.shape[1]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -282,9 +347,34 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, page_size: int
     return o, lse
 
 
+def test_fwd_rescale_stats(q, k, v, causal: bool, scale: float | None = None, rescale_log2: float = 8.0):
+    """Test-only: the default dense forward (d = 128) plus its per-wave
+    lazy-rescale statistics. Returns (o, lse, stats int32 [tiles, 8, 2]:
+    steps with live keys, steps that rescaled)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, torch.bfloat16, 4)
+    B, Nq, Hq, d = q.shape
+    _, Nk, Hkv, _ = k.shape
+    if d != 128 or tuple(v.shape) != tuple(k.shape) or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("q [B,Nq,Hq,128], k/v [B,Nk,Hkv,128]")
+    _on_gpu(("q", q), ("k", k), ("v", v))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    n = int(lib().ea_test_fwd_rescale_stats_len(B, Nq, Hq))
+    stats = torch.zeros(n, dtype=torch.int32, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    st = lib().ea_test_fwd_rescale_stats(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Nq, Nk, Hq, Hkv,
+                                         int(bool(causal)), float(scale), float(rescale_log2), _ptr(stats), n,
+                                         _stream(q))
+    _check(st, "ea_test_fwd_rescale_stats")
+    return o, lse, stats.view(-1, 8, 2)
+
+
 def test_exp2(x: torch.Tensor, mode: int) -> torch.Tensor:
     """Test-only: 2^x with the kernels' exponential (EA_EXP_HW or EA_EXP_POLY)."""
     _need(x, "x", torch.float32, 1)
+    _on_gpu(("x", x))
     y = torch.empty_like(x)
     _check(lib().ea_test_exp2(_ptr(x), _ptr(y), x.numel(), int(mode), _stream(x)), "ea_test_exp2")
     return y

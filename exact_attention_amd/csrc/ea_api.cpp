@@ -2,6 +2,7 @@
 // call), tuning defaults, work decomposition parameters and kernel dispatch.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -33,6 +34,9 @@ ea_status hip_status(hipError_t e, const char* what) {
 
 bool finite_pos(float x) { return std::isfinite(x) && x > 0.f; }
 
+// largest lazy-rescale threshold of the MX fp8 forward: floor(log2(448) * 1000) / 1000
+constexpr float kMx8MaxRescaleLog2 = 8.807f;
+
 ea_status check_tuning(const ea_fwd_tuning* t) {
   if (t == nullptr) return EA_OK;
   if (t->exp_mode < 0 || t->exp_mode > 2) return fail(EA_ERR_INVALID, "tuning.exp_mode must be 0, 1 or 2");
@@ -41,23 +45,26 @@ ea_status check_tuning(const ea_fwd_tuning* t) {
   if (t->natural_order != 0 && t->natural_order != 1)
     return fail(EA_ERR_INVALID, "tuning.natural_order must be 0 or 1");
   if (t->kernel < EA_FWD_KERNEL_AUTO || t->kernel > EA_FWD_KERNEL_UNROLL_KV)
-    return fail(EA_ERR_INVALID, "tuning.kernel must be 0, 1, 2, 3 or 4");
+    return fail(EA_ERR_INVALID, "tuning.kernel must be 0, 1, 2, 3, 4 or 5");
   return EA_OK;
 }
 
 // Workgroups of the persistent ping-pong form: one per CU of the current
 // device, rounded down to a multiple of 8 (the tile order deals work to the 8
 // XCDs by workgroup id). Cached per device; 0 if the count is unavailable.
+// Threads may race to fill an entry: each stores the same value, atomically.
 int persistent_workgroups() {
-  static int cache[64];
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cache[dev] == 0) {
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cache[dev] = (cus / 8) * 8;
+    n = (cus / 8) * 8;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
 // The 8-wave kernels cover 256-row blocks, the 4-wave kernel 128-row blocks;
@@ -75,10 +82,6 @@ hipError_t dispatch_fwd(ea::FwdArgs a, int d, int dv, bool causal, bool varlen, 
       if (a.persist_wgs <= 0) return hipErrorInvalidDevice;
     }
     return ea::launch_fwd_pp(a, d, dv, causal, varlen, tt.exp_mode, s);
-  }
-  if (tt.kernel == EA_FWD_KERNEL_PIPELINED) {
-    a.n_mb = (a.n_mb + 1) / 2;
-    return ea::launch_fwd_sp(a, d, causal, varlen, tt.exp_mode, s);
   }
   const bool pp = tt.kernel == EA_FWD_KERNEL_PINGPONG || tt.kernel == EA_FWD_KERNEL_PERSISTENT ||
                   tt.kernel == EA_FWD_KERNEL_UNROLL_KV || (tt.kernel == EA_FWD_KERNEL_AUTO && d == 128);
@@ -128,6 +131,8 @@ ea_status ea_attn_fwd_hd(const void* q, const void* k, const void* v, void* o, f
   if (!finite_pos(scale)) return fail(EA_ERR_INVALID, "scale must be finite and positive");
   if (causal != 0 && causal != 1) return fail(EA_ERR_INVALID, "causal must be 0 or 1");
   if (ea_status st = check_tuning(tuning); st != EA_OK) return st;
+  if (tuning != nullptr && tuning->kernel == EA_FWD_KERNEL_PIPELINED)
+    return fail(EA_ERR_UNSUPPORTED, "the bf16 forward has no pipelined kernel (kernel 3 is MX fp8 only)");
   if (d != d_v && tuning != nullptr && tuning->kernel != EA_FWD_KERNEL_AUTO &&
       tuning->kernel != EA_FWD_KERNEL_PINGPONG && tuning->kernel != EA_FWD_KERNEL_PERSISTENT)
     return fail(EA_ERR_UNSUPPORTED, "head dims (%d, %d) run on the ping-pong kernel only", d, d_v);
@@ -161,6 +166,48 @@ ea_status ea_attn_fwd_hd(const void* q, const void* k, const void* v, void* o, f
                     "attention forward launch");
 }
 
+size_t ea_test_fwd_rescale_stats_len(int B, int Nq, int Hq) {
+  if (B <= 0 || Nq <= 0 || Hq <= 0) return 0;
+  const long long tiles = ((B * (long long)Hq + 7) / 8) * 8 * ((Nq + ea::kPpBlockM - 1) / ea::kPpBlockM);
+  return (size_t)tiles * 16;
+}
+
+ea_status ea_test_fwd_rescale_stats(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                                    int Nq, int Nk, int Hq, int Hkv, int causal, float scale, float rescale_log2,
+                                    int* stats, size_t stats_len, void* stream) {
+  if (!q || !k || !v || !o || !stats) return fail(EA_ERR_INVALID, "q, k, v, o and stats must be non-null");
+  if (B <= 0 || Nq <= 0 || Nk <= 0 || Hq <= 0 || Hkv <= 0)
+    return fail(EA_ERR_INVALID, "B, Nq, Nk, Hq and Hkv must be positive");
+  if (Hq % Hkv) return fail(EA_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if (!finite_pos(scale)) return fail(EA_ERR_INVALID, "scale must be finite and positive");
+  if (causal != 0 && causal != 1) return fail(EA_ERR_INVALID, "causal must be 0 or 1");
+  if (!(rescale_log2 >= 0.f && rescale_log2 <= 16.f)) return fail(EA_ERR_INVALID, "rescale_log2 must be in [0, 16]");
+  if ((long long)B * Nq >= (1LL << 31) || (long long)B * Nk >= (1LL << 31))
+    return fail(EA_ERR_UNSUPPORTED, "B * N must be below 2^31");
+  const size_t need = ea_test_fwd_rescale_stats_len(B, Nq, Hq);
+  if (stats_len < need) return fail(EA_ERR_WORKSPACE, "stats needs %zu ints, %zu given", need, stats_len);
+  ea::FwdArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.o = (uint16_t*)o;
+  a.lse = lse;
+  a.nseq = B;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.group = Hq / Hkv;
+  a.total_q = B * Nq;
+  a.n_mb = (Nq + ea::kPpBlockM - 1) / ea::kPpBlockM;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.tau = rescale_log2;
+  a.stats = stats;
+  a.persist_wgs = persistent_workgroups();
+  if (a.persist_wgs <= 0) return fail(EA_ERR_HIP, "device CU count unavailable");
+  return hip_status(ea::launch_fwd_pp_stats(a, causal != 0, (hipStream_t)stream), "statistics forward launch");
+}
+
 ea_status ea_attn_fwd_tuned(const void* q, const void* k, const void* v, void* o, float* lse,
                             int B, int Nq, int Nk, int Hq, int Hkv, int d, int causal,
                             float scale, const ea_fwd_tuning* tuning, void* stream) {
@@ -189,6 +236,8 @@ ea_status ea_attn_fwd_varlen_ordered(const void* q, const void* k, const void* v
   if (!finite_pos(scale)) return fail(EA_ERR_INVALID, "scale must be finite and positive");
   if (causal != 0 && causal != 1) return fail(EA_ERR_INVALID, "causal must be 0 or 1");
   if (ea_status st = check_tuning(tuning); st != EA_OK) return st;
+  if (tuning != nullptr && tuning->kernel == EA_FWD_KERNEL_PIPELINED)
+    return fail(EA_ERR_UNSUPPORTED, "the bf16 forward has no pipelined kernel (kernel 3 is MX fp8 only)");
   if (max_seqlen_q > total_q) return fail(EA_ERR_INVALID, "max_seqlen_q exceeds total_q");
   const int n_mb = (max_seqlen_q + ea::kFwdBlockM - 1) / ea::kFwdBlockM;
   if ((long long)((num_seqs * (long long)Hq + 7) / 8) * 8 * n_mb >= (1LL << 31))
@@ -268,6 +317,11 @@ ea_status ea_attn_fwd_mx8_fmt(const void* q8, const void* k8, const void* v8, co
     return fail(EA_ERR_UNSUPPORTED, "MX fp8 forward: hardware exponential and heaviest-first order only");
   if (tt.kernel == EA_FWD_KERNEL_PINGPONG || tt.kernel == EA_FWD_KERNEL_UNROLL_KV)
     return fail(EA_ERR_UNSUPPORTED, "MX fp8 forward: kernel 0, 1, 3 or 4 (no ping-pong or unroll-KV kernel)");
+  // P is rounded to e4m3 with scale 1 and is at most 2^rescale_log2, so the
+  // threshold must keep it under e4m3's largest finite value 448 (2^8.807...)
+  if (tt.rescale_log2 > kMx8MaxRescaleLog2)
+    return fail(EA_ERR_UNSUPPORTED, "MX fp8 forward: rescale_log2 %g lets P exceed e4m3's 448 (at most %g)",
+                (double)tt.rescale_log2, (double)kMx8MaxRescaleLog2);
   // the pipelined kernel is the faster one on fp8 (its products are cheap
   // next to the softmax, which it overlaps with them)
   const bool pipelined = tt.kernel != EA_FWD_KERNEL_4WAVE;

@@ -51,7 +51,7 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 // FMA-pipe exp2 following the range-reduction + cubic scheme of
 // "FlashAttention-4: algorithm-pipeline co-design for Blackwell" (hybrid
 // exponent section) and "FlashAttention4 close reading" (section 3.1.3):
-// clamp x at -127, split x = n + f with n = floor(x), f in [0,1), evaluate a
+// clamp x at -127 (below it the result is 0), split x = n + f with n = floor(x), f in [0,1), evaluate a
 // cubic for 2^f by Horner (3 FMAs) and put n into the exponent field
 // (v_ldexp_f32). On gfx950 the round-down split is one v_floor_f32 and a
 // subtraction instead of the magic-bias add.
@@ -66,12 +66,14 @@ __device__ __forceinline__ float exp2_poly(float x) {
   // n = floor(x) is an exact integer; f = x - n lies in [0, 1] (it rounds up to
   // exactly 1.0 for x just below an integer, which the cubic still handles:
   // p(1) ~ 2). v_fract_f32 is not used: it clamps its result below 1.0, so
-  // x - fract(x) is then not an integer for tiny negative x.
-  x = __builtin_fmaxf(x, -127.0f);
-  const float n = __builtin_floorf(x);
-  const float f = x - n;
+  // x - fract(x) is then not an integer for tiny negative x. Inputs below
+  // -127 (masked scores are -inf) give exactly 0, as an underflow would.
+  const float xc = __builtin_fmaxf(x, -127.0f);
+  const float n = __builtin_floorf(xc);
+  const float f = xc - n;
   const float p = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(kExp2P3, f, kExp2P2), f, kExp2P1), f, 1.0f);
-  return __builtin_amdgcn_ldexpf(p, (int)n);
+  const float r = __builtin_amdgcn_ldexpf(p, (int)n);
+  return x < -127.0f ? 0.0f : r;
 }
 
 // ---------------------------------------------------------------------------

@@ -117,7 +117,9 @@ __device__ __forceinline__ bool pp_locate(const FwdArgs& a, int xcd, int j, PpTi
 // The per-wave state of the ping-pong forward and its two phase bodies,
 // shared by the one-tile kernel and the persistent walk.
 // D: head dim of Q and K; DV: head dim of V and O (equal, or 192 / 128).
-template <int D, int DV, bool CAUSAL, int EXPMODE>
+// STATS: count this wave's steps with live keys and its lazy-rescale
+// decisions (the test-only statistics launch).
+template <int D, int DV, bool CAUSAL, int EXPMODE, bool STATS = false>
 struct PpCore {
   static constexpr int BN = kFwdBlockN;
   static constexpr int NDT = DV / 32;  // 32-wide d tiles of O^T
@@ -132,6 +134,7 @@ struct PpCore {
   f32x16 s0, s1;
   bf16x8 pb[4];
   float m_run, l_run;
+  int n_live = 0, n_rescale = 0;  // STATS only
 
   __device__ __forceinline__ void init() {
     const int tid = threadIdx.x;
@@ -261,7 +264,9 @@ struct PpCore {
     for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s0[i]), s1[i]);
     mx = max_with_partner32(mx);
     const float m_new = __builtin_fmaxf(m_run, mx * sl);
+    if constexpr (STATS) ++n_live;
     if (__ballot(m_new > m_run + tau)) {
+      if constexpr (STATS) ++n_rescale;
       const float alpha = (m_run == kNegInf) ? 0.f : exp2_hw(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
@@ -332,8 +337,10 @@ __device__ __forceinline__ uint32_t dma_lane_off(int piece, int lane, size_t str
   return (uint32_t)(r * (int)stride * 2 + ((sl ^ swz<DD>(r)) << 4));
 }
 
-// One work tile: the whole forward of its 256 rows.
-template <int D, int DV, bool CAUSAL, bool VARLEN, int EXPMODE>
+// One work tile: the whole forward of its 256 rows. STATS: also write, per
+// wave, the number of steps with live keys and of lazy rescales to
+// a.stats[2 (8 (8 j + xcd) + wave) + {0, 1}] (plain vector stores).
+template <int D, int DV, bool CAUSAL, bool VARLEN, int EXPMODE, bool STATS = false>
 __device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) {
   constexpr int BN = kFwdBlockN;
   constexpr int TILE = BN * D;               // bf16 elements per K stage
@@ -352,7 +359,7 @@ __device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) 
   const int off = t.lk - t.lq;  // bottom-right causal alignment
   const int nkb = t.nkb;
 
-  PpCore<D, DV, CAUSAL, EXPMODE> cr;
+  PpCore<D, DV, CAUSAL, EXPMODE, STATS> cr;
   cr.init();
   const int tid = threadIdx.x;
   const int lane = cr.lane, w = cr.w, grp = cr.grp;
@@ -445,6 +452,13 @@ __device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) 
   // no DMA may still be writing this workgroup's LDS when it exits
   __builtin_amdgcn_s_waitcnt(0);
   cr.template store<VARLEN>(a, t.seq, t.h, t.row_lo, t.q0, t.lq);
+  if constexpr (STATS) {
+    if (lane == 0) {
+      int* st = a.stats + 2 * (8 * (8 * j + xcd) + w);
+      st[0] = cr.n_live;
+      st[1] = cr.n_rescale;
+    }
+  }
 }
 
 // Persistent walk with the K/V pipeline running on across tiles (the
@@ -690,11 +704,28 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
 }
 
 // Persistent form (persistent_snake in ea_fwd_common.h): one workgroup per
-// CU runs the one-tile body for each tile of its list.
-template <int D, int DV, bool CAUSAL, bool VARLEN, int EXPMODE>
+// CU runs the one-tile body for each tile of its list. STATS: the test-only
+// statistics launch (per-wave step and rescale counts in a.stats).
+template <int D, int DV, bool CAUSAL, bool VARLEN, int EXPMODE, bool STATS = false>
 __global__ __launch_bounds__(512, 1) void fwd_pp_persistent_kernel(FwdArgs a) {
   persistent_snake(uniform(a.tiles_per_xcd),
-                   [&](int xcd, int j) { pp_tile<D, DV, CAUSAL, VARLEN, EXPMODE>(a, xcd, j); });
+                   [&](int xcd, int j) { pp_tile<D, DV, CAUSAL, VARLEN, EXPMODE, STATS>(a, xcd, j); });
+}
+
+// Test-only: the default dense forward (persistent ping-pong, d = 128,
+// hardware exp) with per-wave lazy-rescale statistics in a.stats, which must
+// hold 16 ints per work tile.
+hipError_t launch_fwd_pp_stats(const FwdArgs& a, bool causal, hipStream_t s) {
+  FwdArgs b = a;
+  const int grid = fwd_grid(a, false);
+  b.tiles_per_xcd = grid / 8;
+  const int w = max(min(a.persist_wgs / 8, b.tiles_per_xcd), 1);
+  if (causal) {
+    hipLaunchKernelGGL((fwd_pp_persistent_kernel<128, 128, true, false, 0, true>), dim3(8 * w), dim3(512), 0, s, b);
+  } else {
+    hipLaunchKernelGGL((fwd_pp_persistent_kernel<128, 128, false, false, 0, true>), dim3(8 * w), dim3(512), 0, s, b);
+  }
+  return hipGetLastError();
 }
 
 // Persistent form with the K/V pipeline running on across tiles (pp_walk);

@@ -28,6 +28,7 @@ struct FwdArgs {
   int tiles_per_xcd;   // set by the launcher for the persistent form
   int unroll_kv;       // with persist_wgs > 0 and equal head dims: 1 runs the walk whose
                        // K/V pipeline continues across tiles (unroll-KV schedule)
+  int* stats;          // test-only statistics launch: per-wave counts (else unused)
 };
 
 constexpr int kFwdBlockM = 128;  // query rows per workgroup (4 waves x 32)
@@ -42,9 +43,10 @@ hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, bool varlen, int exp
 // d: head dim of Q and K, dv: of V and O ((64, 64), (128, 128) or (192, 128))
 hipError_t launch_fwd_pp(const FwdArgs& a, int d, int dv, bool causal, bool varlen, int exp_mode,
                          hipStream_t s);
-// 8-wave software-pipelined forward; a.n_mb counts kPpBlockM-row blocks
-hipError_t launch_fwd_sp(const FwdArgs& a, int d, bool causal, bool varlen, int exp_mode,
-                         hipStream_t s);
+// test-only: the persistent ping-pong forward (dense, d = 128, hardware exp)
+// writing per-wave live-step and lazy-rescale counts to a.stats (16 ints per
+// work tile); a.n_mb counts kPpBlockM-row blocks, a.persist_wgs is set
+hipError_t launch_fwd_pp_stats(const FwdArgs& a, bool causal, hipStream_t s);
 
 // varlen batch order (heaviest sequence first): weights[b] and order[virtual] = actual
 hipError_t launch_lpt_order(const int* cu_q, const int* cu_k, int n, int causal, int block_m, int* weights,

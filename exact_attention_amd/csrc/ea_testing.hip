@@ -81,3 +81,251 @@ extern "C" ea_status ea_test_exp2(const float* x, float* y, int n, int mode, voi
   hipLaunchKernelGGL(exp2_kernel, dim3((n + 255) / 256), dim3(256), 0, (hipStream_t)stream, x, y, n, mode);
   return hipGetLastError() == hipSuccess ? EA_OK : EA_ERR_HIP;
 }
+
+// ---------------------------------------------------------------------------
+// Two-role issue probe. The forward kernels pair two waves on each SIMD: one
+// feeds the matrix core while the other runs the softmax on the vector ALU.
+// This kernel measures what each role sustains alone and beside the other:
+// waves 0-3 run role_a, waves 4-7 (the same SIMDs) run role_b, each in a loop
+// of identical iterations until `budget` shader-clock cycles (s_memtime) have
+// passed, then record how many iterations they finished in how many cycles.
+// One workgroup per CU (the 96 KB of LDS it declares leave no room for a
+// second), so each SIMD holds exactly the two probed waves.
+//
+// Roles (one iteration each):
+//   IDLE       nothing (the wave exits at once)
+//   MFMA_REG   32 v_mfma_f32_32x32x16_bf16, operands in registers, four
+//              accumulators in VGPRs
+//   MFMA_LDS   the forward's product part: 16 MFMAs whose A operand comes
+//              from ds_read_b128 (a 64 x 128 K stage) and 16 whose A operand
+//              comes from two ds_read_b64_tr_b16 each (a V^T stage), three
+//              stages in turn, reads issued ahead of their MFMA
+//   SOFTMAX    the forward's softmax of one 64-key step on 32 scores per
+//              lane: three-input max chain, lane-swap max, wave vote on the
+//              lazy-rescale test, 32 FMA + 32 exp2, two sum chains, 16 bf16
+//              packs
+//   EXP        32 independent v_exp_f32
+//   FMA        32 independent v_fma_f32
+//   MFMA_AGPR  MFMA_REG with the accumulators in AGPRs
+//   MFMA_LDS_PRIO MFMA_LDS at raised wave priority (s_setprio 1), as the
+//              forward runs its product part
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kProbeStage = 64 * 128;  // bf16 elements per K or V stage
+
+__device__ __forceinline__ void probe_launder(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void probe_keep(float x) { asm volatile("" ::"v"(x)); }
+__device__ __forceinline__ void probe_keep16(const ea::f32x16& x) { asm volatile("" ::"v"(x)); }
+
+__device__ __forceinline__ ea::f32x16 mfma_agpr(ea::bf16x8 a, ea::bf16x8 b, ea::f32x16 c) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  return c;
+}
+
+struct ProbeCounts {
+  long long iters, cycles;
+};
+
+template <typename F>
+__device__ __forceinline__ ProbeCounts probe_run(long long budget, F&& body) {
+  const long long t0 = __builtin_amdgcn_s_memtime();
+  long long t = t0, n = 0;
+  while (t - t0 < budget) {
+#pragma unroll 1
+    for (int u = 0; u < 4; ++u) body((int)(n + u));
+    n += 4;
+    t = __builtin_amdgcn_s_memtime();
+  }
+  return {n, t - t0};
+}
+
+// AGPRS: the instantiation that holds the AGPR-accumulator role (a kernel
+// that uses AGPRs at all gets its register budget split evenly between VGPRs
+// and AGPRs, so the other roles run in the instantiation without it)
+template <bool AGPRS>
+__global__ __launch_bounds__(512, 1) void pair_probe_kernel(long long* out, int role_a, int role_b,
+                                                            long long budget) {
+  __shared__ __attribute__((aligned(1024))) uint16_t kst[3 * kProbeStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t vst[3 * kProbeStage];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int i = tid; i < 3 * kProbeStage; i += 512) {
+    kst[i] = (uint16_t)(0x3c00 + (i & 63));  // small positive bf16 values
+    vst[i] = (uint16_t)(0x3c00 + ((i >> 3) & 63));
+  }
+  __syncthreads();
+  const int role = __builtin_amdgcn_readfirstlane(w < 4 ? role_a : role_b);
+  const int hh = lane >> 5, c = lane & 31;
+  ea::bf16x8 qa, qb;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    qa[i] = (__bf16)(1e-3f * (float)(lane + i));
+    qb[i] = (__bf16)(1e-3f * (float)(lane - i));
+  }
+  ProbeCounts r{0, 0};
+  if (role == EA_PROBE_MFMA_REG || role == EA_PROBE_MFMA_AGPR) {
+    ea::f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    if (role == EA_PROBE_MFMA_REG) {
+      r = probe_run(budget, [&](int) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          c0 = ea::mfma32x32x16(qa, qb, c0);
+          c1 = ea::mfma32x32x16(qa, qb, c1);
+          c2 = ea::mfma32x32x16(qa, qb, c2);
+          c3 = ea::mfma32x32x16(qa, qb, c3);
+        }
+      });
+    } else if constexpr (AGPRS) {
+      r = probe_run(budget, [&](int) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          c0 = mfma_agpr(qa, qb, c0);
+          c1 = mfma_agpr(qa, qb, c1);
+          c2 = mfma_agpr(qa, qb, c2);
+          c3 = mfma_agpr(qa, qb, c3);
+        }
+      });
+      asm volatile("s_nop 15\n s_nop 15\n s_nop 15" ::: "memory");
+    }
+    probe_keep16(c0);
+    probe_keep16(c1);
+    probe_keep16(c2);
+    probe_keep16(c3);
+  } else if (role == EA_PROBE_MFMA_LDS || role == EA_PROBE_MFMA_LDS_PRIO) {
+    // operand offsets of the forward (bytes): K rows c and c + 32 at d chunk
+    // 16 kk + 8 hh; V^T transposed reads of 4 rows x 4 columns per 16 lanes
+    int k_off[8], v_off[4][2];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) k_off[kk] = 2 * ea::tile_off<128>(c, 16 * kk + 8 * hh);
+    const int tr_row = 4 * hh + ((lane & 15) >> 2);
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      v_off[dt][0] = 2 * ea::tile_off<128>(tr_row, 32 * dt + tr_col);
+      v_off[dt][1] = 2 * ea::tile_off<128>(tr_row + 8, 32 * dt + tr_col);
+    }
+    ea::f32x16 s0 = {}, s1 = {}, o[4] = {};
+    const bool prio = role == EA_PROBE_MFMA_LDS_PRIO;
+    r = probe_run(budget, [&](int it) {
+      const int st = it % 3;
+      const char EA_LDS* kb = (const char EA_LDS*)((EA_LDS uint16_t*)kst + st * kProbeStage);
+      const char EA_LDS* vb = (const char EA_LDS*)((EA_LDS uint16_t*)vst + st * kProbeStage);
+      if (prio) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const ea::bf16x8 k0 = ea::lds_load<ea::bf16x8>(kb + k_off[kk]);
+        const ea::bf16x8 k1 = ea::lds_load<ea::bf16x8>(kb + k_off[kk] + 64 * 128);
+        s0 = ea::mfma32x32x16(k0, qa, s0);
+        s1 = ea::mfma32x32x16(k1, qa, s1);
+      }
+#pragma unroll
+      for (int sj = 0; sj < 4; ++sj) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const ea::i16x4 lo = ea::ds_read_tr16((const EA_LDS uint16_t*)(vb + v_off[dt][0] + 32 * sj * 128));
+          const ea::i16x4 hi = ea::ds_read_tr16((const EA_LDS uint16_t*)(vb + v_off[dt][1] + 32 * sj * 128));
+          const ea::i32x4 t = {__builtin_bit_cast(ea::i32x2, lo)[0], __builtin_bit_cast(ea::i32x2, lo)[1],
+                               __builtin_bit_cast(ea::i32x2, hi)[0], __builtin_bit_cast(ea::i32x2, hi)[1]};
+          o[dt] = ea::mfma32x32x16(__builtin_bit_cast(ea::bf16x8, t), qb, o[dt]);
+        }
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 13; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+      if (prio) __builtin_amdgcn_s_setprio(0);
+    });
+    probe_keep16(s0);
+    probe_keep16(s1);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) probe_keep16(o[dt]);
+  } else if (role == EA_PROBE_SOFTMAX) {
+    float s[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) s[i] = 0.01f * (float)((lane * 7 + i * 13) & 127) - 0.5f;
+    float m_run = 1.0f, l_run = 0.f;
+    r = probe_run(budget, [&](int) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) probe_launder(s[i]);
+      float mx = ea::kNegInf;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[i]), s[i + 16]);
+      mx = ea::max_with_partner32(mx);
+      const float m_new = __builtin_fmaxf(m_run, mx * 0.127f);
+      if (__ballot(m_new > m_run + 8.0f)) {
+        l_run *= ea::exp2_hw(m_run - m_new);
+        m_run = m_new;
+      }
+      float p[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) p[i] = ea::exp2_hw(__builtin_fmaf(s[i], 0.127f, -m_run));
+      float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        l0 += p[i];
+        l1 += p[i + 16];
+      }
+      l_run += l0 + l1;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) probe_keep(__builtin_bit_cast(float, ea::pack_bf16x2(p[2 * i], p[2 * i + 1])));
+    });
+    probe_keep(l_run + m_run);
+  } else if (role == EA_PROBE_EXP || role == EA_PROBE_FMA) {
+    float x[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = -0.03f * (float)(lane + i);
+    // all inputs laundered first, all results kept last, so no result is
+    // consumed right after the instruction that makes it
+    if (role == EA_PROBE_EXP) {
+      r = probe_run(budget, [&](int) {
+        float y[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) probe_launder(x[i]);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) y[i] = ea::exp2_hw(x[i]);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) probe_keep(y[i]);
+      });
+    } else {
+      r = probe_run(budget, [&](int) {
+        float y[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) probe_launder(x[i]);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) y[i] = __builtin_fmaf(x[i], 1.0001f, 0.5f);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) probe_keep(y[i]);
+      });
+    }
+  }
+  if (lane == 0) {
+    out[2 * (blockIdx.x * 8 + w)] = r.iters;
+    out[2 * (blockIdx.x * 8 + w) + 1] = r.cycles;
+  }
+}
+
+}  // namespace
+
+extern "C" ea_status ea_test_pair_probe(long long* out, int blocks, int role_a, int role_b, long long budget,
+                                        void* stream) {
+  if (out == nullptr || blocks <= 0 || blocks > 4096) return EA_ERR_INVALID;
+  if (role_a < 0 || role_a > EA_PROBE_MFMA_LDS_PRIO || role_b < 0 || role_b > EA_PROBE_MFMA_LDS_PRIO)
+    return EA_ERR_INVALID;
+  if (budget <= 0 || budget > (1LL << 32)) return EA_ERR_INVALID;
+  if (role_a == EA_PROBE_MFMA_AGPR || role_b == EA_PROBE_MFMA_AGPR) {
+    hipLaunchKernelGGL(pair_probe_kernel<true>, dim3(blocks), dim3(512), 0, (hipStream_t)stream, out, role_a, role_b,
+                       budget);
+  } else {
+    hipLaunchKernelGGL(pair_probe_kernel<false>, dim3(blocks), dim3(512), 0, (hipStream_t)stream, out, role_a,
+                       role_b, budget);
+  }
+  return hipGetLastError() == hipSuccess ? EA_OK : EA_ERR_HIP;
+}

@@ -80,9 +80,11 @@ typedef struct {
  *   EA_FWD_KERNEL_4WAVE     4 waves x 32 query rows, two workgroups per CU
  *   EA_FWD_KERNEL_PINGPONG  8 waves x 32 rows in two groups that alternate
  *                           matrix products and softmax on each SIMD
- *   EA_FWD_KERNEL_PIPELINED 8 waves x 32 rows, each wave overlapping the
- *                           softmax of one tile with its own matrix products
- *                           of the next and previous tiles
+ *   EA_FWD_KERNEL_PIPELINED MX fp8 forward only (ea_attn_fwd_mx8_tuned): 8
+ *                           waves x 32 rows, each wave overlapping the softmax
+ *                           of one tile with its own matrix products of the
+ *                           next and previous tiles; the bf16 entry points
+ *                           return EA_ERR_UNSUPPORTED for it
  *   EA_FWD_KERNEL_PERSISTENT the ping-pong kernel in persistent form: one
  *                           workgroup per CU walks a static, load-balanced
  *                           list of row blocks instead of one workgroup per
@@ -219,8 +221,9 @@ ea_status ea_attn_fwd_mx8(const void* q8, const void* k8, const void* v8,
  * EA_FWD_KERNEL_UNROLL_KV,
  * exp_mode other than EA_EXP_HW and natural_order = 1 return
  * EA_ERR_UNSUPPORTED. rescale_log2 is the lazy-rescale threshold, which also
- * bounds P before its e4m3 rounding (P <= 2^rescale_log2, so values above 8
- * can overflow e4m3's 448).
+ * bounds P before its e4m3 rounding (P <= 2^rescale_log2): values above 8.807
+ * (log2 448, e4m3's largest finite value, rounded down) return
+ * EA_ERR_UNSUPPORTED.
  */
 ea_status ea_attn_fwd_mx8_tuned(const void* q8, const void* k8, const void* v8,
                                 const uint8_t* q_scale, const uint8_t* k_scale, const uint8_t* v_scale,
@@ -273,7 +276,8 @@ enum { EA_FP8_E4M3 = 0, EA_FP8_E5M2 = 1 };
  * q8 / k8 / v8 codes given by in_format (EA_FP8_E4M3 or EA_FP8_E5M2; anything
  * else is EA_ERR_INVALID). Scales, layouts, tuning and outputs are those of
  * ea_attn_fwd_mx8_tuned; P is re-quantised to e4m3 in both cases (P <=
- * 2^rescale_log2 fits e4m3's range).
+ * 2^rescale_log2, which the rescale_log2 <= 8.807 bound keeps within e4m3's
+ * 448).
  */
 ea_status ea_attn_fwd_mx8_fmt(const void* q8, const void* k8, const void* v8,
                               const uint8_t* q_scale, const uint8_t* k_scale, const uint8_t* v_scale,

@@ -45,6 +45,59 @@ ea_status ea_test_mfma_loop(float* out, int blocks, int iters, void* stream);
  */
 ea_status ea_test_stream_read(const void* buf, size_t bytes, int* out, int blocks, void* stream);
 
+/*
+ * ea_test_pair_probe -- calibration of two waves sharing one SIMD, the pairing
+ * the forward kernels are built on. blocks workgroups of 8 waves (one per CU:
+ * each declares 96 KB of LDS) run: waves 0-3 role_a, waves 4-7 role_b (wave
+ * w and w + 4 share a SIMD). Each wave repeats one iteration of its role until
+ * budget shader-clock cycles (s_memtime) have passed and writes
+ * out[2 (8 b + w)] = iterations done, out[2 (8 b + w) + 1] = cycles taken.
+ * Roles (one iteration): EA_PROBE_IDLE (the wave exits), EA_PROBE_MFMA_REG
+ * (32 v_mfma_f32_32x32x16_bf16 from registers), EA_PROBE_MFMA_LDS (the
+ * forward's product part: 16 MFMAs fed by ds_read_b128, 16 by two
+ * ds_read_b64_tr_b16 each), EA_PROBE_SOFTMAX (the forward's softmax of a
+ * 64-key step on 32 scores per lane), EA_PROBE_EXP (32 independent v_exp_f32),
+ * EA_PROBE_FMA (32 independent v_fma_f32), EA_PROBE_MFMA_AGPR (MFMA_REG with
+ * AGPR accumulators), EA_PROBE_MFMA_LDS_PRIO (MFMA_LDS at raised wave
+ * priority).
+ *   out: device int64 array of 16 * blocks elements. 0 < blocks <= 4096,
+ *   0 < budget <= 2^32, roles in range; otherwise EA_ERR_INVALID.
+ */
+/*
+ * ea_test_fwd_rescale_stats -- the library's default dense forward (the
+ * persistent ping-pong kernel, d = 128, hardware exponential, bf16 in the
+ * layouts of ea_attn_fwd) with lazy-rescale threshold rescale_log2 ("the
+ * conditional softmax rescaling" of "FlashAttention-4: algorithm-pipeline
+ * co-design for Blackwell": rescale the accumulator only when the running row
+ * max grows by more than that many powers of two), which also writes, for
+ * every work tile t (256 query rows of one (batch, head); tile index as the
+ * kernel numbers them) and wave w (0..7, 32 rows each):
+ *   stats[2 (8 t + w)]     = steps (64-key tiles) in which the wave saw keys,
+ *   stats[2 (8 t + w) + 1] = steps in which it rescaled (its running max grew
+ *                            by more than the threshold for some row, or
+ *                            it met its first keys).
+ * o and lse are written as by ea_attn_fwd, bit for bit. stats: device int32
+ * array of at least ea_test_fwd_rescale_stats_len(B, Nq, Hq) elements (padding
+ * tiles keep their contents). Errors as for ea_attn_fwd; EA_ERR_WORKSPACE
+ * when stats_len is short.
+ */
+size_t ea_test_fwd_rescale_stats_len(int B, int Nq, int Hq);
+ea_status ea_test_fwd_rescale_stats(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                                    int Nq, int Nk, int Hq, int Hkv, int causal, float scale, float rescale_log2,
+                                    int* stats, size_t stats_len, void* stream);
+
+enum {
+  EA_PROBE_IDLE = 0,
+  EA_PROBE_MFMA_REG = 1,
+  EA_PROBE_MFMA_LDS = 2,
+  EA_PROBE_SOFTMAX = 3,
+  EA_PROBE_EXP = 4,
+  EA_PROBE_FMA = 5,
+  EA_PROBE_MFMA_AGPR = 6,
+  EA_PROBE_MFMA_LDS_PRIO = 7
+};
+ea_status ea_test_pair_probe(long long* out, int blocks, int role_a, int role_b, long long budget, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -80,6 +80,13 @@ def test_tuning_errors(lib):
     assert lib.ea_attn_fwd_tuned(P, P, P, P, None, 1, 8, 8, 2, 2, 128, 0, 0.1, ctypes.byref(t), None) == -1
     t = ea.tuning(kernel=6)
     assert lib.ea_attn_fwd_tuned(P, P, P, P, None, 1, 8, 8, 2, 2, 128, 0, 0.1, ctypes.byref(t), None) == -1
+    assert "0, 1, 2, 3, 4 or 5" in _err(lib)
+    # kernel 3 (pipelined) exists for MX fp8 only
+    t = ea.tuning(kernel=3)
+    assert lib.ea_attn_fwd_tuned(P, P, P, P, None, 1, 8, 8, 2, 2, 128, 0, 0.1, ctypes.byref(t), None) == -2
+    assert "fp8 only" in _err(lib)
+    assert lib.ea_attn_fwd_varlen(P, P, P, P, None, P, P, 2, 10, 10, 5, 2, 2, 128, 1, 0.1, ctypes.byref(t),
+                                  None) == -2
     d = ea.default_tuning()
     assert d.exp_mode == 0 and d.rescale_log2 == 8.0 and d.natural_order == 0 and d.kernel == 0
 
@@ -114,6 +121,10 @@ def test_mx8_tuning_errors(lib):
     assert call(ea.tuning(natural_order=1)) == -2
     assert call(ea.tuning(kernel=5)) == -2      # no unroll-KV fp8 kernel
     assert call(ea.tuning(kernel=6)) == -1
+    # P <= 2^rescale_log2 is rounded to e4m3 with scale 1: the threshold must
+    # keep it under e4m3's 448 = 2^8.807...
+    assert call(ea.tuning(rescale_log2=8.9)) == -2 and "448" in _err(lib)
+    assert call(ea.tuning(rescale_log2=16.0)) == -2
 
 
 def test_decode_argument_errors(lib):

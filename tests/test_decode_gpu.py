@@ -225,3 +225,54 @@ def test_small_pages_many_sequences_odd_group():
         assert_o_close(o[nz], ro[nz])
         assert_lse_close(lse[nz], rl[nz])
         assert np.all(o[~nz] == 0) and np.all(np.isneginf(lse[~nz]))
+
+
+def _one_hot_keys(pg, targets):
+    """Queries that are unit vectors (query head h of every sequence points
+    along axis h) and keys that are zero except key targets[b, h] of
+    sequence b, which is 2^14 times that axis: every query then has one
+    dominant key whose score beats all others by 2^14 scale, so its softmax
+    weight is exactly 1 and every other weight underflows to exactly 0, and
+    the output row is that key's V row bit for bit (a gather through the page
+    table, made visible). Returns a new Paged with k_cache / q rewritten."""
+    B, Hq, d = pg.q.shape
+    Hkv = pg.k_cache.shape[2]
+    g = Hq // Hkv
+    one = W.f32_to_bf16_bits(np.ones(1, np.float32))[0]
+    big = W.f32_to_bf16_bits(np.full(1, 2.0 ** 14, np.float32))[0]
+    q = np.zeros_like(pg.q)
+    kc = np.where(pg.k_cache == W.BF16_NAN, W.BF16_NAN, np.uint16(0)).astype(np.uint16)
+    for b in range(B):
+        for h in range(Hq):
+            q[b, h, h] = one
+            t = int(targets[b, h])
+            page = pg.block_table[b, t // pg.page_size]
+            kc[page, t % pg.page_size, h // g, h] = big
+    return W.Paged(q, kc, pg.v_cache, pg.block_table, pg.seq_lens, pg.page_size, pg.scale)
+
+
+@pytest.mark.parametrize("page_size", [16, 1, 5])
+def test_gather_exact_dominant_key(page_size):
+    """Bit-exact page-table gathers, checked directly: for each (sequence,
+    query head) the output equals, bit for bit, the V row of the token the
+    host picks through the block table (random tokens, pages in a seeded
+    random order, NaN-poisoned tails, several range counts)."""
+    rng = np.random.default_rng(700 + page_size)
+    L = [1, 17, 300, 1024, 33, 4000, 2, 129]
+    Hq, Hkv = 32, 8
+    pg = W.paged(len(L), Hq, Hkv, 128, page_size, L, seed=700 + page_size)
+    for trial in range(3):
+        targets = np.stack([rng.integers(0, n, size=Hq) for n in L])
+        if trial == 0:
+            targets[:, 0] = 0
+            targets[:, 1] = np.asarray(L) - 1        # first and last token of every sequence
+        pq = _one_hot_keys(pg, targets)
+        for ns in (0, 3):
+            o, _ = run_decode(pq, num_splits=ns)
+            got = W.f32_to_bf16_bits(o.astype(np.float32))
+            g = Hq // Hkv
+            want = np.stack([np.stack([pg.v_cache[pg.block_table[b, targets[b, h] // page_size],
+                                                  targets[b, h] % page_size, h // g]
+                                       for h in range(Hq)]) for b in range(len(L))])
+            assert np.array_equal(got, want), f"page {page_size} trial {trial} splits {ns}"
+    log(f"  page {page_size}: {3 * 2 * len(L) * Hq} gathered rows bit-exact")

@@ -1,0 +1,96 @@
+"""Lazy (conditional) rescaling of the accumulator, "FlashAttention-4:
+algorithm-pipeline co-design for Blackwell", conditional softmax rescaling
+section: the running max is only moved (and O, l rescaled) when it grows by
+more than a threshold, here 2^8 (a factor of 256; the reading of the page's
+"gap exceeds 256"). The statistics launch counts, per wave, the 64-key steps
+that saw keys and the steps that rescaled; its outputs are those of the
+default forward bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from _helpers import assert_lse_close, assert_o_close, dev_bf16, f64, host_bits, log
+
+pytestmark = pytest.mark.gpu
+
+
+def live_steps(B, Nq, Nk, Hq, causal):
+    """Steps with keys per (tile, wave), from the kernel's work order: tile
+    8 j + x is entry j of XCD x; groups (b, h) go round-robin to the XCDs, a
+    group's 256-row blocks run heaviest (last) first; wave w owns rows
+    64 (w mod 4) + 32 (w div 4) .. +31 of its block."""
+    n_mb = -(-Nq // 256)
+    groups = B * Hq
+    per_xcd = -(-groups // 8) * n_mb
+    out = np.zeros((8 * per_xcd, 8), dtype=np.int64)
+    off = Nk - Nq
+    for x in range(8):
+        for j in range(per_xcd):
+            kg, r = divmod(j, n_mb)
+            g = x + 8 * kg
+            if g >= groups:
+                continue
+            mb = n_mb - 1 - r
+            row_lo = 256 * mb
+            nkeys = min(Nk, row_lo + 256 + off) if causal else Nk
+            nkb = -(-max(nkeys, 0) // 64)
+            for w in range(8):
+                wrow = row_lo + 64 * (w % 4) + 32 * (w // 4)
+                n = 0
+                for s in range(nkb):
+                    if not (causal and s * 64 > wrow + 31 + off):
+                        n += 1
+                out[8 * j + x, w] = n
+    return out
+
+
+@pytest.mark.parametrize("shape", [(1, 1000, 1000, 2, 2, True), (2, 600, 600, 3, 1, False), (1, 300, 700, 4, 2, True)])
+def test_stats_counts_and_bitwise_outputs(shape):
+    import exact_attention_amd as ea
+    B, Nq, Nk, Hq, Hkv, causal = shape
+    inp = W.dense(B, Nq, Nk, Hq, Hkv, 128, causal, seed=410 + Nq)
+    q, k, v = dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v)
+    o_ref, l_ref = ea.attn_fwd(q, k, v, causal, inp.scale)
+    res = {}
+    for tau in (0.0, 8.0):
+        o, lse, st = ea.test_fwd_rescale_stats(q, k, v, causal, inp.scale, tau)
+        torch.cuda.synchronize()
+        st = st.cpu().numpy()
+        res[tau] = st
+        if tau == 8.0:
+            assert torch.equal(o, o_ref) and torch.equal(lse, l_ref)
+        ro, rl = oracle.attention(f64(inp.q), f64(inp.k), f64(inp.v), causal, inp.scale)
+        assert_o_close(f64(host_bits(o)), ro)
+        assert_lse_close(lse.cpu().numpy(), rl)
+    want = live_steps(B, Nq, Nk, Hq, causal)
+    for tau, st in res.items():
+        assert np.array_equal(st[:, :, 0], want), f"live steps differ at tau={tau}"
+        live = st[:, :, 0] > 0
+        # a wave's first step with keys always moves the max off -inf
+        assert np.all(st[:, :, 1][live] >= 1) and np.all(st[:, :, 1] <= st[:, :, 0])
+    assert np.all(res[0.0][:, :, 1] >= res[8.0][:, :, 1])
+    frac = 1 - res[8.0][:, :, 1].sum() / res[8.0][:, :, 0].sum()
+    log(f"  {shape}: rescales tau=0 {res[0.0][:, :, 1].sum()}, tau=8 {res[8.0][:, :, 1].sum()} "
+        f"of {res[8.0][:, :, 0].sum()} live steps (skipped {frac:.3f})")
+
+
+def test_prefill_workload_skipped_fraction():
+    """The prefill workload (B=4, H=16, N=8192, causal): the fraction of steps
+    whose rescale the threshold skips, logged for the record (the pages report
+    about 90% on their workloads)."""
+    import exact_attention_amd as ea
+    inp = W.prefill(True)
+    q, k, v = dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v)
+    o, lse, st = ea.test_fwd_rescale_stats(q, k, v, True, inp.scale, 8.0)
+    o_ref, l_ref = ea.attn_fwd(q, k, v, True, inp.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(lse, l_ref)
+    st = st.cpu().numpy()
+    live, resc = st[:, :, 0].sum(), st[:, :, 1].sum()
+    waves = int((st[:, :, 0] > 0).sum())
+    log(f"prefill: {live} live wave-steps, {resc} rescales ({waves} first steps), skipped "
+        f"{1 - resc / live:.4f}, after the first step {1 - (resc - waves) / (live - waves):.4f}")
+    assert np.array_equal(st[:, :, 0], live_steps(4, 8192, 8192, 16, True))
+    assert resc < live
