@@ -58,6 +58,8 @@ _SIGNATURES = {
     "ea_attn_bwd_ex": ([_c_void_p] * 9 + [_c_int] * 7 + [_c_float, _c_int, _c_void_p, _c_size_t, _c_void_p], _c_int),
     "ea_decode_workspace_size": ([_c_int] * 7, _c_size_t),
     "ea_attn_decode_paged": ([_c_void_p] * 7 + [_c_int] * 7 + [_c_float, _c_int, _c_void_p, _c_size_t, _c_void_p], _c_int),
+    "ea_decode_noalloc_max_bytes": ([], _c_size_t),
+    "ea_attn_decode_paged_noalloc": ([_c_void_p] * 7 + [_c_int] * 7 + [_c_float, _c_int, _c_void_p], _c_int),
     "ea_test_exp2": ([_c_void_p, _c_void_p, _c_int, _c_int, _c_void_p], _c_int),
     "ea_test_mfma_loop": ([_c_void_p, _c_int, _c_int, _c_void_p], _c_int),
     "ea_test_stream_read": ([_c_void_p, _c_size_t, _c_void_p, _c_int, _c_void_p], _c_int),

@@ -475,11 +475,16 @@ size_t ea_decode_workspace_size(int B, int Hq, int Hkv, int d, int max_seqlen, i
   return ea::decode_workspace_bytes(B, Hq, d, choose_ranges(Hq, Hkv, num_splits));
 }
 
-ea_status ea_attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
-                               const int* block_table, const int* seq_lens, void* o, float* lse,
-                               int B, int Hq, int Hkv, int d, int page_size, int num_pages,
-                               int max_pages_per_seq, float scale, int num_splits, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks and argument block shared by the two decode entry points (host
+// only, before any HIP call).
+ea_status decode_args(const void* q, const void* k_cache, const void* v_cache, const int* block_table,
+                      const int* seq_lens, void* o, float* lse, int B, int Hq, int Hkv, int d, int page_size,
+                      int num_pages, int max_pages_per_seq, float scale, int num_splits, ea::DecodeArgs& a,
+                      size_t& need) {
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o)
     return fail(EA_ERR_INVALID, "tensor pointers must be non-null");
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || page_size <= 0 || num_pages <= 0 ||
@@ -498,11 +503,8 @@ ea_status ea_attn_decode_paged(const void* q, const void* k_cache, const void* v
   if ((long long)num_pages * page_size * Hkv * d >= (1LL << 40) || (long long)num_pages * page_size >= (1LL << 31))
     return fail(EA_ERR_UNSUPPORTED, "KV pool too large");
   const int max_seqlen = max_pages_per_seq * page_size;
-  const size_t need = ea_decode_workspace_size(B, Hq, Hkv, d, max_seqlen, page_size, num_splits);
-  if (workspace == nullptr || workspace_bytes < need)
-    return fail(EA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
-                workspace == nullptr ? (size_t)0 : workspace_bytes);
-  ea::DecodeArgs a{};
+  need = ea_decode_workspace_size(B, Hq, Hkv, d, max_seqlen, page_size, num_splits);
+  a = ea::DecodeArgs{};
   a.q = (const uint16_t*)q;
   a.kc = (const uint16_t*)k_cache;
   a.vc = (const uint16_t*)v_cache;
@@ -519,8 +521,52 @@ ea_status ea_attn_decode_paged(const void* q, const void* k_cache, const void* v
   a.num_pages = num_pages;
   a.num_ranges = choose_ranges(Hq, Hkv, num_splits);
   a.scale_log2 = scale * 1.4426950408889634f;
+  return EA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ea_status ea_attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                               const int* block_table, const int* seq_lens, void* o, float* lse,
+                               int B, int Hq, int Hkv, int d, int page_size, int num_pages,
+                               int max_pages_per_seq, float scale, int num_splits, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  ea::DecodeArgs a;
+  size_t need = 0;
+  if (ea_status st = decode_args(q, k_cache, v_cache, block_table, seq_lens, o, lse, B, Hq, Hkv, d, page_size,
+                                 num_pages, max_pages_per_seq, scale, num_splits, a, need);
+      st != EA_OK)
+    return st;
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(EA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
   ea::decode_bind_workspace(a, workspace);
   return hip_status(ea::launch_decode(a, (hipStream_t)stream), "paged decode launch");
+}
+
+size_t ea_decode_noalloc_max_bytes(void) { return ea::kDecodeScratchBytes; }
+
+ea_status ea_attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                       const int* block_table, const int* seq_lens, void* o, float* lse, int B,
+                                       int Hq, int Hkv, int d, int page_size, int num_pages,
+                                       int max_pages_per_seq, float scale, int num_splits, void* stream) {
+  ea::DecodeArgs a;
+  size_t need = 0;
+  if (ea_status st = decode_args(q, k_cache, v_cache, block_table, seq_lens, o, lse, B, Hq, Hkv, d, page_size,
+                                 num_pages, max_pages_per_seq, scale, num_splits, a, need);
+      st != EA_OK)
+    return st;
+  if (need > ea::kDecodeScratchBytes)
+    return fail(EA_ERR_UNSUPPORTED,
+                "allocation-free decode: its partials need %zu bytes, above the library's fixed %zu "
+                "(use ea_attn_decode_paged with a workspace)",
+                need, ea::kDecodeScratchBytes);
+  void* scratch = nullptr;
+  if (ea_status st = hip_status(ea::decode_scratch(&scratch), "decode scratch lookup"); st != EA_OK) return st;
+  ea::decode_bind_workspace(a, scratch);
+  return hip_status(ea::launch_decode(a, (hipStream_t)stream), "allocation-free paged decode launch");
 }
 
 }  // extern "C"

@@ -49,6 +49,8 @@
 #include "ea_device.h"
 #include "ea_internal.h"
 
+#include <mutex>
+
 namespace ea {
 
 namespace {
@@ -436,6 +438,33 @@ static hipError_t launch_p(const DecodeArgs& a, hipStream_t s) {
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   if (a.num_ranges <= 0 || a.part_o == nullptr || a.plan == nullptr) return hipErrorInvalidValue;
   return (a.page_size % 16 == 0) ? launch_p<true>(a, s) : launch_p<false>(a, s);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free decode: the split partials and the plan live in a
+// file-scope device array instead of a caller workspace. Every device the
+// library runs on holds its own copy until the process ends. In host code the
+// array's name is only a stand-in: its device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* per_device[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (per_device[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    per_device[dev] = p;
+  }
+  *ptr = per_device[dev];
+  return hipSuccess;
 }
 
 int decode_head_groups(int Hkv, int group) {

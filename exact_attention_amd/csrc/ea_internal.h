@@ -124,5 +124,9 @@ size_t decode_workspace_bytes(int B, int Hq, int d, int num_ranges);
 int decode_head_groups(int Hkv, int group);
 // points part_o / part_lse / plan into a workspace of decode_workspace_bytes
 void decode_bind_workspace(DecodeArgs& a, void* workspace);
+// the allocation-free decode's device array: size, and its address on the
+// current device (looked up once per device)
+constexpr size_t kDecodeScratchBytes = (size_t)16 << 20;
+hipError_t decode_scratch(void** ptr);
 
 }  // namespace ea

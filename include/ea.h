@@ -325,6 +325,26 @@ ea_status ea_attn_decode_paged(const void* q, const void* k_cache, const void* v
                                int max_pages_per_seq, float scale, int num_splits,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * ea_attn_decode_paged_noalloc -- ea_attn_decode_paged without a workspace,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation). Arguments,
+ * layouts, results and errors are those of ea_attn_decode_paged minus the
+ * workspace. The split partials and the plan live in a device array of
+ * ea_decode_noalloc_max_bytes() bytes (16 MiB) inside the library, one per
+ * GPU it runs on, held until the process ends; a call whose partials need more
+ * (ea_decode_workspace_size above that size) returns EA_ERR_UNSUPPORTED
+ * before any launch. Nothing is allocated per call. The array holds no state
+ * between calls that a later call reads (it is rewritten before use), but every
+ * call on one GPU uses the same array: calls that may overlap on one GPU (other
+ * streams, other threads) race and give wrong results, so serialise them.
+ */
+size_t ea_decode_noalloc_max_bytes(void);
+ea_status ea_attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                       const int* block_table, const int* seq_lens, void* o, float* lse, int B,
+                                       int Hq, int Hkv, int d, int page_size, int num_pages,
+                                       int max_pages_per_seq, float scale, int num_splits, void* stream);
+
 /* Human-readable description of the last failure on the calling thread
  * (thread-local; valid until the next library call on that thread). */
 const char* ea_last_error(void);
