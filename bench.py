@@ -25,8 +25,10 @@ prefill forward, MFMA-bound); ``roofline_decode`` the decode (HBM-bound),
 a bounded sample of each workload on this host's cores, and ``parity`` compares
 the GPU outputs of the timed launches with those oracle results element by
 element (fp8: per (batch, head) slice, normwise). ``clock`` holds the shader
-clock read from the driver while the prefill runs, and ``config`` the device
-and ROCm version.
+clock the driver reports while the prefill runs and the one measured inside
+the kernel (shader cycles over wall clock ticks of its step loops), on which
+``roofline.at_clock`` scales the MFMA peak; ``config`` holds the device and
+ROCm version.
 """
 from __future__ import annotations
 
@@ -71,8 +73,9 @@ TRAFFIC = {
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=30,
+                   help="untimed steps first: the first tens of launches after idle run slower")
     p.add_argument("--exp-mode", type=int, default=0)
     p.add_argument("--rescale-log2", type=float, default=8.0, help="lazy-rescale threshold of the bf16 prefill")
     p.add_argument("--only", choices=["prefill", "decode", "fp8", "bwd"], default=None,
@@ -248,7 +251,8 @@ class ClockSampler:
                 "sclk_mhz_max": float(s.max()), "samples": int(s.size),
                 "socket_power_w_median": float(np.median(self.power)) if self.power else None,
                 "source": "amdsmi GPU metrics (current gfx clock, mean over XCDs), polled while the causal "
-                          "prefill forward runs back to back"}
+                          "prefill forward runs back to back; the driver's figure, which can stay at the "
+                          "clock's upper limit while the cores run slower (see clock.in_kernel)"}
 
 
 def rocm_version():
@@ -650,19 +654,17 @@ def main():
     if run_prefill and d == 128 and d_v == 128:
         sampler = ClockSampler()
         with sampler:
-            t_clk = time_events(torch, stream, launch_prefill, 400, warmup=0)
-        clk = sampler.result()
-        out["clock"] = clk
-        if clk is not None:
-            f_ghz = clk["sclk_mhz_median"] / 1e3
-            at_clock = PEAK_BF16_TFLOPS * f_ghz / 2.4
-            tf_clk = flops / (t_clk.mean() * 1e-3) / 1e12
-            out["roofline"]["at_clock"] = {
-                "what": "dense bf16 peak scaled to the median shader clock read while the prefill ran "
-                        "(2.5 PF/s at 2.4 GHz)", "peak": at_clock, "achieved": tf_clk, "frac": tf_clk / at_clock}
-    if run_prefill and d == 128 and d_v == 128:
-        # lazy rescale: how many of the waves' steps with keys moved the max
-        # (one untimed launch of the statistics variant of the same kernel)
+            time_events(torch, stream, launch_prefill, 200, warmup=0)
+        out["clock"] = {"driver": sampler.result()}
+        # lazy rescale and the shader clock under this load: back-to-back
+        # launches of the statistics variant of the same kernel (outputs bit
+        # for bit those of the timed kernel); the last launch's per-wave
+        # counts, and its step loops' shader clock cycles (s_memtime) over
+        # wall clock ticks (s_memrealtime at the device's wall clock rate)
+        for _ in range(30):
+            _, _, st = ea.test_fwd_rescale_stats(q, k, v, True, inp.scale, args.rescale_log2)
+        t_st = time_events(torch, stream, lambda: ea.test_fwd_rescale_stats(q, k, v, True, inp.scale,
+                                                                            args.rescale_log2), 1, warmup=0)
         _, _, st = ea.test_fwd_rescale_stats(q, k, v, True, inp.scale, args.rescale_log2)
         st = st.cpu().numpy().astype(np.int64)
         live, resc = int(st[:, :, 0].sum()), int(st[:, :, 1].sum())
@@ -673,6 +675,20 @@ def main():
             "skipped_fraction_after_first_step": 1 - (resc - first) / max(live - first, 1),
             "what": "per wave of 32 rows and 64-key step: the running max moved (O and l rescaled) or not; a "
                     "wave's first step with keys always moves it off -inf"}
+        has = st[:, :, 0] > 0
+        khz = ea.test_wall_clock_khz()
+        mhz = float(st[:, :, 2][has].sum() / st[:, :, 3][has].sum() * khz / 1e3)
+        out["clock"]["in_kernel"] = {
+            "shader_mhz": mhz, "wall_clock_khz": khz, "stats_launch_ms": float(t_st.mean()),
+            "what": "sum over waves of shader clock cycles (s_memtime) / wall clock ticks (s_memrealtime) over the "
+                    "forward's step loops, in the statistics launch after 30 back-to-back launches"}
+        at_clock = PEAK_BF16_TFLOPS * mhz / 2400.0
+        if "roofline" in out:
+            tf = out["roofline"]["achieved"]
+            out["roofline"]["at_clock"] = {
+                "what": "dense bf16 MFMA peak scaled to the shader clock measured inside the kernel under this "
+                        "load (2.5 PF/s at 2.4 GHz)", "clock_mhz": mhz, "peak": at_clock, "achieved": tf,
+                "frac": tf / at_clock}
     if run_extra and run_prefill and d == 128 and d_v == 128:
         # non-causal prefill: same inputs
         o_nc = torch.empty_like(q)

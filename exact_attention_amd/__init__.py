@@ -67,6 +67,7 @@ _SIGNATURES = {
     "ea_test_fwd_rescale_stats_len": ([_c_int] * 3, _c_size_t),
     "ea_test_fwd_rescale_stats": ([_c_void_p] * 5 + [_c_int] * 6 + [_c_float, _c_float, _c_void_p, _c_size_t,
                                                                    _c_void_p], _c_int),
+    "ea_test_wall_clock_khz": ([_c_int, _c_void_p], _c_int),
 }
 
 _lib = None
@@ -351,8 +352,9 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, page_size: int
 
 def test_fwd_rescale_stats(q, k, v, causal: bool, scale: float | None = None, rescale_log2: float = 8.0):
     """Test-only: the default dense forward (d = 128) plus its per-wave
-    lazy-rescale statistics. Returns (o, lse, stats int32 [tiles, 8, 2]:
-    steps with live keys, steps that rescaled)."""
+    lazy-rescale and clock statistics. Returns (o, lse, stats int32
+    [tiles, 8, 4]: steps with live keys, steps that rescaled, shader clock
+    cycles of the step loop, wall clock ticks of the same loop)."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, torch.bfloat16, 4)
     B, Nq, Hq, d = q.shape
@@ -370,7 +372,14 @@ def test_fwd_rescale_stats(q, k, v, causal: bool, scale: float | None = None, re
                                          int(bool(causal)), float(scale), float(rescale_log2), _ptr(stats), n,
                                          _stream(q))
     _check(st, "ea_test_fwd_rescale_stats")
-    return o, lse, stats.view(-1, 8, 2)
+    return o, lse, stats.view(-1, 8, 4)
+
+
+def test_wall_clock_khz(device: int = 0) -> int:
+    """Test-only: the rate of the device's constant wall clock counter (kHz)."""
+    out = _c_int(0)
+    _check(lib().ea_test_wall_clock_khz(int(device), ctypes.byref(out)), "ea_test_wall_clock_khz")
+    return int(out.value)
 
 
 def test_exp2(x: torch.Tensor, mode: int) -> torch.Tensor:

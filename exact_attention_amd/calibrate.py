@@ -15,7 +15,13 @@ cycles at the nominal rate), mfma_lds (the forward's product part: the same 32
 MFMAs fed from LDS), softmax (the forward's softmax of one 64-key step on 32
 scores per lane), exp / fma (32 independent instructions), mfma_agpr
 (mfma_reg with AGPR accumulators), mfma_lds_prio (mfma_lds at raised wave
-priority).
+priority), mix (8 MFMAs from registers, each with 2 exp and 2 fma interleaved:
+256 matrix cycles at the nominal rate), lds_b128 / lds_tr (an 8 KB operand
+tile read from LDS into registers, plain or transposed, then waited for),
+mfma_lds_deep (mfma_lds with 14 reads issued ahead instead of 6), mfma_lds_alt
+(mfma_lds with the two products' MFMAs alternating), fused32 (a 32-key step:
+16 LDS-fed MFMAs interleaved with the softmax of an independent 32-key tile,
+512 matrix cycles at the nominal rate).
 """
 from __future__ import annotations
 
@@ -26,14 +32,19 @@ import json
 import numpy as np
 
 ROLES = {"idle": 0, "mfma_reg": 1, "mfma_lds": 2, "softmax": 3, "exp": 4, "fma": 5, "mfma_agpr": 6,
-         "mfma_lds_prio": 7}
+         "mfma_lds_prio": 7, "mix": 8, "lds_b128": 9, "lds_tr": 10, "mfma_lds_deep": 11, "mfma_lds_alt": 12,
+         "fused32": 13}
 
 PAIRS = [
     ("mfma_reg", "idle"), ("mfma_lds", "idle"), ("idle", "softmax"), ("idle", "exp"), ("idle", "fma"),
     ("mfma_reg", "softmax"), ("mfma_lds", "softmax"), ("mfma_lds_prio", "softmax"), ("mfma_reg", "exp"),
     ("mfma_reg", "fma"), ("mfma_agpr", "idle"), ("mfma_agpr", "softmax"), ("mfma_agpr", "fma"),
     ("mfma_reg", "mfma_reg"), ("softmax", "softmax"), ("mfma_lds", "mfma_lds"), ("exp", "exp"),
-    ("fma", "fma"),
+    ("fma", "fma"), ("fma", "idle"), ("exp", "idle"), ("softmax", "idle"), ("mix", "idle"), ("idle", "mix"),
+    ("mix", "lds_tr"), ("mix", "lds_b128"), ("mix", "mix"), ("lds_tr", "idle"), ("lds_b128", "idle"),
+    ("mfma_reg", "lds_tr"), ("lds_tr", "lds_tr"), ("mix", "softmax"),
+    ("mfma_lds_deep", "idle"), ("mfma_lds_alt", "idle"), ("mfma_lds_deep", "softmax"), ("mfma_lds_alt", "softmax"),
+    ("fused32", "idle"), ("fused32", "fused32"),
 ]
 
 

@@ -169,7 +169,12 @@ ea_status ea_attn_fwd_hd(const void* q, const void* k, const void* v, void* o, f
 size_t ea_test_fwd_rescale_stats_len(int B, int Nq, int Hq) {
   if (B <= 0 || Nq <= 0 || Hq <= 0) return 0;
   const long long tiles = ((B * (long long)Hq + 7) / 8) * 8 * ((Nq + ea::kPpBlockM - 1) / ea::kPpBlockM);
-  return (size_t)tiles * 16;
+  return (size_t)tiles * 32;
+}
+
+ea_status ea_test_wall_clock_khz(int device, int* khz) {
+  if (khz == nullptr) return fail(EA_ERR_INVALID, "khz must be non-null");
+  return hip_status(hipDeviceGetAttribute(khz, hipDeviceAttributeWallClockRate, device), "wall clock rate query");
 }
 
 ea_status ea_test_fwd_rescale_stats(const void* q, const void* k, const void* v, void* o, float* lse, int B,

@@ -338,8 +338,10 @@ __device__ __forceinline__ uint32_t dma_lane_off(int piece, int lane, size_t str
 }
 
 // One work tile: the whole forward of its 256 rows. STATS: also write, per
-// wave, the number of steps with live keys and of lazy rescales to
-// a.stats[2 (8 (8 j + xcd) + wave) + {0, 1}] (plain vector stores).
+// wave, the number of steps with live keys, of lazy rescales, and the shader
+// clock cycles (s_memtime) and constant-rate wall clock ticks (s_memrealtime)
+// its step loop took, to a.stats[4 (8 (8 j + xcd) + wave) + {0, 1, 2, 3}]
+// (plain vector stores).
 template <int D, int DV, bool CAUSAL, bool VARLEN, int EXPMODE, bool STATS = false>
 __device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) {
   constexpr int BN = kFwdBlockN;
@@ -442,6 +444,11 @@ __device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) 
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
+  unsigned long long cyc0 = 0, rt0 = 0;
+  if constexpr (STATS) {
+    cyc0 = __builtin_amdgcn_s_memtime();
+    rt0 = __builtin_amdgcn_s_memrealtime();
+  }
   if (grp == 1) pp_barrier();  // group B runs one phase behind
   for (int s = 0; s <= nkb; s += 3) {
     step(0, s);
@@ -451,14 +458,18 @@ __device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) 
   if (grp == 0) pp_barrier();
   // no DMA may still be writing this workgroup's LDS when it exits
   __builtin_amdgcn_s_waitcnt(0);
-  cr.template store<VARLEN>(a, t.seq, t.h, t.row_lo, t.q0, t.lq);
   if constexpr (STATS) {
+    const unsigned long long cyc1 = __builtin_amdgcn_s_memtime();
+    const unsigned long long rt1 = __builtin_amdgcn_s_memrealtime();
     if (lane == 0) {
-      int* st = a.stats + 2 * (8 * (8 * j + xcd) + w);
+      int* st = a.stats + 4 * (8 * (8 * j + xcd) + w);
       st[0] = cr.n_live;
       st[1] = cr.n_rescale;
+      st[2] = (int)(cyc1 - cyc0);
+      st[3] = (int)(rt1 - rt0);
     }
   }
+  cr.template store<VARLEN>(a, t.seq, t.h, t.row_lo, t.q0, t.lq);
 }
 
 // Persistent walk with the K/V pipeline running on across tiles (the
@@ -713,8 +724,8 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_persistent_kernel(FwdArgs a) {
 }
 
 // Test-only: the default dense forward (persistent ping-pong, d = 128,
-// hardware exp) with per-wave lazy-rescale statistics in a.stats, which must
-// hold 16 ints per work tile.
+// hardware exp) with per-wave lazy-rescale and clock statistics in a.stats,
+// which must hold 32 ints per work tile.
 hipError_t launch_fwd_pp_stats(const FwdArgs& a, bool causal, hipStream_t s) {
   FwdArgs b = a;
   const int grid = fwd_grid(a, false);

@@ -109,6 +109,21 @@ extern "C" ea_status ea_test_exp2(const float* x, float* y, int n, int mode, voi
 //   MFMA_AGPR  MFMA_REG with the accumulators in AGPRs
 //   MFMA_LDS_PRIO MFMA_LDS at raised wave priority (s_setprio 1), as the
 //              forward runs its product part
+//   MIX        8 MFMAs from registers interleaved, one by one, with 2 v_exp_f32
+//              and 2 v_fma_f32 each (independent data): a wave that feeds the
+//              matrix core and the vector ALU at once
+//   LDS_B128   8 ds_read_b128 (an 8 KB operand tile into registers), then a
+//              wait for them
+//   LDS_TR     16 ds_read_b64_tr_b16 (an 8 KB transposed operand tile into
+//              registers), then a wait for them
+//   MFMA_LDS_DEEP MFMA_LDS with 14 operand reads issued before the first
+//              MFMA instead of 6
+//   MFMA_LDS_ALT  MFMA_LDS with the S and P V products alternating, so each
+//              pair of MFMAs needs one plain and two transposed reads
+//   FUSED32    one 32-key step of a wave that overlaps its own softmax with
+//              its own products: 8 MFMAs fed by ds_read_b128, 8 fed by
+//              transposed reads, and the softmax of an independent 32-key
+//              score tile (16 scores per lane), interleaved
 // ---------------------------------------------------------------------------
 namespace {
 
@@ -121,6 +136,10 @@ __device__ __forceinline__ void probe_keep16(const ea::f32x16& x) { asm volatile
 __device__ __forceinline__ ea::f32x16 mfma_agpr(ea::bf16x8 a, ea::bf16x8 b, ea::f32x16 c) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
   return c;
+}
+
+__device__ __forceinline__ void wait_lgkm_probe() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
 }
 
 struct ProbeCounts {
@@ -191,7 +210,8 @@ __global__ __launch_bounds__(512, 1) void pair_probe_kernel(long long* out, int 
     probe_keep16(c1);
     probe_keep16(c2);
     probe_keep16(c3);
-  } else if (role == EA_PROBE_MFMA_LDS || role == EA_PROBE_MFMA_LDS_PRIO) {
+  } else if (role == EA_PROBE_MFMA_LDS || role == EA_PROBE_MFMA_LDS_PRIO || role == EA_PROBE_MFMA_LDS_DEEP ||
+             role == EA_PROBE_MFMA_LDS_ALT) {
     // operand offsets of the forward (bytes): K rows c and c + 32 at d chunk
     // 16 kk + 8 hh; V^T transposed reads of 4 rows x 4 columns per 16 lanes
     int k_off[8], v_off[4][2];
@@ -206,47 +226,188 @@ __global__ __launch_bounds__(512, 1) void pair_probe_kernel(long long* out, int 
     }
     ea::f32x16 s0 = {}, s1 = {}, o[4] = {};
     const bool prio = role == EA_PROBE_MFMA_LDS_PRIO;
+    auto kread = [&](const char EA_LDS* kb, int kk, int half) {
+      return ea::lds_load<ea::bf16x8>(kb + k_off[kk] + half * 64 * 128);
+    };
+    auto vread = [&](const char EA_LDS* vb, int sj, int dt) {
+      const ea::i16x4 lo = ea::ds_read_tr16((const EA_LDS uint16_t*)(vb + v_off[dt][0] + 32 * sj * 128));
+      const ea::i16x4 hi = ea::ds_read_tr16((const EA_LDS uint16_t*)(vb + v_off[dt][1] + 32 * sj * 128));
+      const ea::i32x4 t = {__builtin_bit_cast(ea::i32x2, lo)[0], __builtin_bit_cast(ea::i32x2, lo)[1],
+                           __builtin_bit_cast(ea::i32x2, hi)[0], __builtin_bit_cast(ea::i32x2, hi)[1]};
+      return __builtin_bit_cast(ea::bf16x8, t);
+    };
+    if (role == EA_PROBE_MFMA_LDS_ALT) {
+      // S and P V products alternate: each pair of MFMAs needs one plain and
+      // two transposed reads, so the two read kinds are spread evenly
+      r = probe_run(budget, [&](int it) {
+        const int st = it % 3;
+        const char EA_LDS* kb = (const char EA_LDS*)((EA_LDS uint16_t*)kst + st * kProbeStage);
+        const char EA_LDS* vb = (const char EA_LDS*)((EA_LDS uint16_t*)vst + st * kProbeStage);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kk = i >> 1, half = i & 1, sj = i >> 2, dt = i & 3;
+          const ea::bf16x8 ka = kread(kb, kk, half);
+          const ea::bf16x8 va = vread(vb, sj, dt);
+          if (half) s1 = ea::mfma32x32x16(ka, qa, s1); else s0 = ea::mfma32x32x16(ka, qa, s0);
+          o[dt] = ea::mfma32x32x16(va, qb, o[dt]);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 9, 0);
+#pragma unroll
+        for (int i = 0; i < 13; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+      });
+    } else {
+      // the two products of the forward's MFMA part; the read-ahead pattern is
+      // set per variant by scheduling groups after the body
+      auto body = [&](int it) {
+        const int st = it % 3;
+        const char EA_LDS* kb = (const char EA_LDS*)((EA_LDS uint16_t*)kst + st * kProbeStage);
+        const char EA_LDS* vb = (const char EA_LDS*)((EA_LDS uint16_t*)vst + st * kProbeStage);
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+          const ea::bf16x8 k0 = kread(kb, kk, 0);
+          const ea::bf16x8 k1 = kread(kb, kk, 1);
+          s0 = ea::mfma32x32x16(k0, qa, s0);
+          s1 = ea::mfma32x32x16(k1, qa, s1);
+        }
+#pragma unroll
+        for (int sj = 0; sj < 4; ++sj) {
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) o[dt] = ea::mfma32x32x16(vread(vb, sj, dt), qb, o[dt]);
+        }
+      };
+      if (role == EA_PROBE_MFMA_LDS_DEEP) {
+        r = probe_run(budget, [&](int it) {
+          body(it);
+          // 14 reads primed, one read per S product, then two per P V product
+          __builtin_amdgcn_sched_group_barrier(0x100, 14, 0);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+#pragma unroll
+          for (int i = 0; i < 9; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 7, 0);
+        });
+      } else {
+        r = probe_run(budget, [&](int it) {
+          if (prio) __builtin_amdgcn_s_setprio(1);
+          body(it);
+          __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+#pragma unroll
+          for (int i = 0; i < 13; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+          if (prio) __builtin_amdgcn_s_setprio(0);
+        });
+      }
+    }
+    probe_keep16(s0);
+    probe_keep16(s1);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) probe_keep16(o[dt]);
+  } else if (role == EA_PROBE_FUSED32) {
+    // one 32-key step of a wave that overlaps its own softmax with its own
+    // products: S_next = K Q^T (8 MFMAs, K by ds_read_b128), O += V^T P
+    // (8 MFMAs, V^T by ds_read_b64_tr_b16) and the softmax of an independent
+    // 32 x 32 score tile (16 scores per lane) interleaved in one block
+    int k_off[8], v_off[4][2];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) k_off[kk] = 2 * ea::tile_off<128>(c, 16 * kk + 8 * hh);
+    const int tr_row = 4 * hh + ((lane & 15) >> 2);
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      v_off[dt][0] = 2 * ea::tile_off<128>(tr_row, 32 * dt + tr_col);
+      v_off[dt][1] = 2 * ea::tile_off<128>(tr_row + 8, 32 * dt + tr_col);
+    }
+    ea::f32x16 sn = {}, sc = {}, o[4] = {};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sc[i] = 0.01f * (float)((lane * 7 + i * 13) & 127) - 0.5f;
+    ea::bf16x8 pb0 = qb, pb1 = qa;
+    float m_run = 1.0f, l_run = 0.f;
     r = probe_run(budget, [&](int it) {
       const int st = it % 3;
       const char EA_LDS* kb = (const char EA_LDS*)((EA_LDS uint16_t*)kst + st * kProbeStage);
       const char EA_LDS* vb = (const char EA_LDS*)((EA_LDS uint16_t*)vst + st * kProbeStage);
-      if (prio) __builtin_amdgcn_s_setprio(1);
+      asm volatile("" : "+v"(sc));
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        const ea::bf16x8 k0 = ea::lds_load<ea::bf16x8>(kb + k_off[kk]);
-        const ea::bf16x8 k1 = ea::lds_load<ea::bf16x8>(kb + k_off[kk] + 64 * 128);
-        s0 = ea::mfma32x32x16(k0, qa, s0);
-        s1 = ea::mfma32x32x16(k1, qa, s1);
+        const ea::bf16x8 ka = ea::lds_load<ea::bf16x8>(kb + k_off[kk]);
+        sn = ea::mfma32x32x16(ka, qa, kk == 0 ? ea::f32x16{} : sn);
       }
 #pragma unroll
-      for (int sj = 0; sj < 4; ++sj) {
+      for (int sj = 0; sj < 2; ++sj) {
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
           const ea::i16x4 lo = ea::ds_read_tr16((const EA_LDS uint16_t*)(vb + v_off[dt][0] + 32 * sj * 128));
           const ea::i16x4 hi = ea::ds_read_tr16((const EA_LDS uint16_t*)(vb + v_off[dt][1] + 32 * sj * 128));
           const ea::i32x4 t = {__builtin_bit_cast(ea::i32x2, lo)[0], __builtin_bit_cast(ea::i32x2, lo)[1],
                                __builtin_bit_cast(ea::i32x2, hi)[0], __builtin_bit_cast(ea::i32x2, hi)[1]};
-          o[dt] = ea::mfma32x32x16(__builtin_bit_cast(ea::bf16x8, t), qb, o[dt]);
+          o[dt] = ea::mfma32x32x16(__builtin_bit_cast(ea::bf16x8, t), sj ? pb1 : pb0, o[dt]);
         }
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+      // softmax of the current tile
+      float mx = ea::kNegInf;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      for (int i = 0; i < 8; ++i) mx = __builtin_fmaxf(__builtin_fmaxf(mx, sc[i]), sc[i + 8]);
+      mx = ea::max_with_partner32(mx);
+      const float m_new = __builtin_fmaxf(m_run, mx * 0.127f);
+      if (__ballot(m_new > m_run + 8.0f)) {
+        l_run *= ea::exp2_hw(m_run - m_new);
+        m_run = m_new;
       }
+      float pp[16];
 #pragma unroll
-      for (int i = 0; i < 13; ++i) {
+      for (int i = 0; i < 16; ++i) pp[i] = ea::exp2_hw(__builtin_fmaf(sc[i], 0.127f, -m_run));
+      float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        l0 += pp[i];
+        l1 += pp[i + 8];
+      }
+      l_run += l0 + l1;
+      const ea::i32x4 t0 = {(int)ea::pack_bf16x2(pp[0], pp[1]), (int)ea::pack_bf16x2(pp[2], pp[3]),
+                            (int)ea::pack_bf16x2(pp[4], pp[5]), (int)ea::pack_bf16x2(pp[6], pp[7])};
+      const ea::i32x4 t1 = {(int)ea::pack_bf16x2(pp[8], pp[9]), (int)ea::pack_bf16x2(pp[10], pp[11]),
+                            (int)ea::pack_bf16x2(pp[12], pp[13]), (int)ea::pack_bf16x2(pp[14], pp[15])};
+      pb0 = __builtin_bit_cast(ea::bf16x8, t0);
+      pb1 = __builtin_bit_cast(ea::bf16x8, t1);
+      // interleave: reads two ahead, each MFMA followed by a share of the vector work
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
-      if (prio) __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      }
     });
-    probe_keep16(s0);
-    probe_keep16(s1);
+    probe_keep16(sn);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) probe_keep16(o[dt]);
+    probe_keep(l_run + m_run);
   } else if (role == EA_PROBE_SOFTMAX) {
     float s[32];
 #pragma unroll
@@ -278,6 +439,66 @@ __global__ __launch_bounds__(512, 1) void pair_probe_kernel(long long* out, int 
       for (int i = 0; i < 16; ++i) probe_keep(__builtin_bit_cast(float, ea::pack_bf16x2(p[2 * i], p[2 * i + 1])));
     });
     probe_keep(l_run + m_run);
+  } else if (role == EA_PROBE_MIX) {
+    ea::f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    float x[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = -0.03f * (float)(lane + i);
+    r = probe_run(budget, [&](int) {
+      float y[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) probe_launder(x[i]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        c0 = ea::mfma32x32x16(qa, qb, c0);
+        c1 = ea::mfma32x32x16(qa, qb, c1);
+        c2 = ea::mfma32x32x16(qa, qb, c2);
+        c3 = ea::mfma32x32x16(qa, qb, c3);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) y[i] = ea::exp2_hw(x[i]);
+#pragma unroll
+      for (int i = 16; i < 32; ++i) y[i] = __builtin_fmaf(x[i], 1.0001f, 0.5f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);  // transcendental
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+      }
+#pragma unroll
+      for (int i = 0; i < 32; ++i) probe_keep(y[i]);
+    });
+    probe_keep16(c0);
+    probe_keep16(c1);
+    probe_keep16(c2);
+    probe_keep16(c3);
+  } else if (role == EA_PROBE_LDS_B128 || role == EA_PROBE_LDS_TR) {
+    const int tr_row = 4 * hh + ((lane & 15) >> 2);
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const int kofs = 2 * ea::tile_off<128>(c, 8 * hh);
+    const int vofs = 2 * ea::tile_off<128>(tr_row, tr_col);
+    if (role == EA_PROBE_LDS_B128) {
+      r = probe_run(budget, [&](int it) {
+        const char EA_LDS* kb = (const char EA_LDS*)((EA_LDS uint16_t*)kst + (it % 3) * kProbeStage);
+        ea::bf16x8 t[8];
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) t[kk] = ea::lds_load<ea::bf16x8>(kb + kofs + 32 * kk);
+        wait_lgkm_probe();
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) asm volatile("" ::"v"(t[kk]));
+      });
+    } else {
+      r = probe_run(budget, [&](int it) {
+        const char EA_LDS* vb = (const char EA_LDS*)((EA_LDS uint16_t*)vst + (it % 3) * kProbeStage);
+        ea::i16x4 t[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          t[j] = ea::ds_read_tr16((const EA_LDS uint16_t*)(vb + vofs + 64 * (j & 3) + 4096 * (j >> 2)));
+        wait_lgkm_probe();
+#pragma unroll
+        for (int j = 0; j < 16; ++j) asm volatile("" ::"v"(t[j]));
+      });
+    }
   } else if (role == EA_PROBE_EXP || role == EA_PROBE_FMA) {
     float x[32];
 #pragma unroll
@@ -317,7 +538,7 @@ __global__ __launch_bounds__(512, 1) void pair_probe_kernel(long long* out, int 
 extern "C" ea_status ea_test_pair_probe(long long* out, int blocks, int role_a, int role_b, long long budget,
                                         void* stream) {
   if (out == nullptr || blocks <= 0 || blocks > 4096) return EA_ERR_INVALID;
-  if (role_a < 0 || role_a > EA_PROBE_MFMA_LDS_PRIO || role_b < 0 || role_b > EA_PROBE_MFMA_LDS_PRIO)
+  if (role_a < 0 || role_a > EA_PROBE_FUSED32 || role_b < 0 || role_b > EA_PROBE_FUSED32)
     return EA_ERR_INVALID;
   if (budget <= 0 || budget > (1LL << 32)) return EA_ERR_INVALID;
   if (role_a == EA_PROBE_MFMA_AGPR || role_b == EA_PROBE_MFMA_AGPR) {

@@ -59,7 +59,14 @@ ea_status ea_test_stream_read(const void* buf, size_t bytes, int* out, int block
  * 64-key step on 32 scores per lane), EA_PROBE_EXP (32 independent v_exp_f32),
  * EA_PROBE_FMA (32 independent v_fma_f32), EA_PROBE_MFMA_AGPR (MFMA_REG with
  * AGPR accumulators), EA_PROBE_MFMA_LDS_PRIO (MFMA_LDS at raised wave
- * priority).
+ * priority), EA_PROBE_MIX (8 MFMAs from registers interleaved one by one with
+ * 2 v_exp_f32 and 2 v_fma_f32 each), EA_PROBE_LDS_B128 (8 ds_read_b128 of an
+ * 8 KB operand tile, then a wait), EA_PROBE_LDS_TR (16 ds_read_b64_tr_b16 of
+ * an 8 KB transposed operand tile, then a wait), EA_PROBE_MFMA_LDS_DEEP
+ * (MFMA_LDS with 14 operand reads issued ahead instead of 6),
+ * EA_PROBE_MFMA_LDS_ALT (MFMA_LDS with S and P V products alternating),
+ * EA_PROBE_FUSED32 (a 32-key step whose 16 LDS-fed MFMAs are interleaved
+ * with the softmax of an independent 32-key score tile, in one wave).
  *   out: device int64 array of 16 * blocks elements. 0 < blocks <= 4096,
  *   0 < budget <= 2^32, roles in range; otherwise EA_ERR_INVALID.
  */
@@ -72,16 +79,27 @@ ea_status ea_test_stream_read(const void* buf, size_t bytes, int* out, int block
  * max grows by more than that many powers of two), which also writes, for
  * every work tile t (256 query rows of one (batch, head); tile index as the
  * kernel numbers them) and wave w (0..7, 32 rows each):
- *   stats[2 (8 t + w)]     = steps (64-key tiles) in which the wave saw keys,
- *   stats[2 (8 t + w) + 1] = steps in which it rescaled (its running max grew
+ *   stats[4 (8 t + w)]     = steps (64-key tiles) in which the wave saw keys,
+ *   stats[4 (8 t + w) + 1] = steps in which it rescaled (its running max grew
  *                            by more than the threshold for some row, or
- *                            it met its first keys).
+ *                            it met its first keys),
+ *   stats[4 (8 t + w) + 2] = shader clock cycles (s_memtime) of the tile's
+ *                            step loop on that wave,
+ *   stats[4 (8 t + w) + 3] = wall clock ticks (s_memrealtime, at the rate
+ *                            ea_test_wall_clock_khz reports) of the same loop;
+ *                            their ratio is the shader clock under this load.
  * o and lse are written as by ea_attn_fwd, bit for bit. stats: device int32
  * array of at least ea_test_fwd_rescale_stats_len(B, Nq, Hq) elements (padding
  * tiles keep their contents). Errors as for ea_attn_fwd; EA_ERR_WORKSPACE
  * when stats_len is short.
  */
 size_t ea_test_fwd_rescale_stats_len(int B, int Nq, int Hq);
+/*
+ * ea_test_wall_clock_khz -- *khz = the rate of the device's constant wall
+ * clock counter (s_memrealtime) for HIP device `device`, in kHz. EA_ERR_INVALID
+ * for a null khz, EA_ERR_HIP if the runtime cannot answer.
+ */
+ea_status ea_test_wall_clock_khz(int device, int* khz);
 ea_status ea_test_fwd_rescale_stats(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                                     int Nq, int Nk, int Hq, int Hkv, int causal, float scale, float rescale_log2,
                                     int* stats, size_t stats_len, void* stream);
@@ -94,7 +112,13 @@ enum {
   EA_PROBE_EXP = 4,
   EA_PROBE_FMA = 5,
   EA_PROBE_MFMA_AGPR = 6,
-  EA_PROBE_MFMA_LDS_PRIO = 7
+  EA_PROBE_MFMA_LDS_PRIO = 7,
+  EA_PROBE_MIX = 8,
+  EA_PROBE_LDS_B128 = 9,
+  EA_PROBE_LDS_TR = 10,
+  EA_PROBE_MFMA_LDS_DEEP = 11,
+  EA_PROBE_MFMA_LDS_ALT = 12,
+  EA_PROBE_FUSED32 = 13
 };
 ea_status ea_test_pair_probe(long long* out, int blocks, int role_a, int role_b, long long budget, void* stream);
 

@@ -94,3 +94,11 @@ def test_prefill_workload_skipped_fraction():
         f"{1 - resc / live:.4f}, after the first step {1 - (resc - waves) / (live - waves):.4f}")
     assert np.array_equal(st[:, :, 0], live_steps(4, 8192, 8192, 16, True))
     assert resc < live
+    # the loop's clock stamps: every wave of a tile with keys spent cycles
+    # and wall ticks in it, and their ratio is a plausible shader clock
+    has = st[:, :, 0] > 0
+    cyc, ticks = st[:, :, 2].astype(np.int64), st[:, :, 3].astype(np.int64)
+    assert np.all(cyc[has] > 0) and np.all(ticks[has] > 0)
+    mhz = cyc[has].sum() / ticks[has].sum() * ea.test_wall_clock_khz() / 1e3
+    log(f"prefill: shader clock over the step loops {mhz:.0f} MHz")
+    assert 300 < mhz < 3000
