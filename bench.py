@@ -61,8 +61,6 @@ TRAFFIC = {
     "ea::fwd_pp_persistent_kernel<128, 128, causal>": 580_212_736,
     # fwd_pp_kernel<128, 128, causal>: 239,567 KiB fetched, 133,467 KiB written
     "ea::fwd_pp_kernel<128, 128, causal>": 627_302_400,
-    # fwd_mx8_sp_persistent_kernel<causal, e4m3>: 165,478 KiB fetched, 137,988 KiB written
-    "ea::fwd_mx8_sp_persistent_kernel<causal, e4m3>": 480_198_656,
     # decode_split_kernel<true> + combine: 2,373,166 KiB fetched, 5,807 KiB written
     "ea::decode_split_kernel<page16> + ea::decode_combine_kernel": 4_866_191_360,
     # fwd_mx8_sp_kernel<causal, e4m3>: 173,648 KiB fetched, 133,336 KiB written
@@ -619,8 +617,9 @@ def main():
             out["fp8"]["ratio_to_bf16"] = tf8 / out["value"]
         out["roofline_fp8"] = {"bound": "mfma", "achieved": tf8, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                                "frac": tf8 / PEAK_FP8_TFLOPS,
-                               "kernel": {0: "ea::fwd_mx8_sp_persistent_kernel", 4: "ea::fwd_mx8_sp_persistent_kernel",
-                                          3: "ea::fwd_mx8_sp_kernel", 1: "ea::fwd_mx8_kernel"}.get(
+                               "kernel": {0: "ea::fwd_mx8_pp_persistent_kernel", 4: "ea::fwd_mx8_pp_persistent_kernel",
+                                          2: "ea::fwd_mx8_pp_kernel", 3: "ea::fwd_mx8_sp_kernel",
+                                          1: "ea::fwd_mx8_kernel"}.get(
                                               args.fp8_kernel, f"fp8 kernel {args.fp8_kernel}")
                                          + f"<causal, {m8.fmt}>"}
         out["roofline_fp8"]["traffic"] = TRAFFIC.get(out["roofline_fp8"]["kernel"])

@@ -320,15 +320,15 @@ ea_status ea_attn_fwd_mx8_fmt(const void* q8, const void* k8, const void* v8, co
   if (tuning != nullptr) tt = *tuning;
   if (tt.exp_mode != EA_EXP_HW || tt.natural_order != 0)
     return fail(EA_ERR_UNSUPPORTED, "MX fp8 forward: hardware exponential and heaviest-first order only");
-  if (tt.kernel == EA_FWD_KERNEL_PINGPONG || tt.kernel == EA_FWD_KERNEL_UNROLL_KV)
-    return fail(EA_ERR_UNSUPPORTED, "MX fp8 forward: kernel 0, 1, 3 or 4 (no ping-pong or unroll-KV kernel)");
+  if (tt.kernel == EA_FWD_KERNEL_UNROLL_KV)
+    return fail(EA_ERR_UNSUPPORTED, "MX fp8 forward: kernel 0, 1, 2, 3 or 4 (no unroll-KV kernel)");
+
   // P is rounded to e4m3 with scale 1 and is at most 2^rescale_log2, so the
   // threshold must keep it under e4m3's largest finite value 448 (2^8.807...)
   if (tt.rescale_log2 > kMx8MaxRescaleLog2)
     return fail(EA_ERR_UNSUPPORTED, "MX fp8 forward: rescale_log2 %g lets P exceed e4m3's 448 (at most %g)",
                 (double)tt.rescale_log2, (double)kMx8MaxRescaleLog2);
-  // the pipelined kernel is the faster one on fp8 (its products are cheap
-  // next to the softmax, which it overlaps with them)
+  // the 8-wave kernels take 256-row blocks, the 4-wave one 128
   const bool pipelined = tt.kernel != EA_FWD_KERNEL_4WAVE;
   ea::Mx8Args a{};
   a.q = (const uint8_t*)q8;
@@ -349,14 +349,17 @@ ea_status ea_attn_fwd_mx8_fmt(const void* q8, const void* k8, const void* v8, co
   a.scale_log2 = scale * 1.4426950408889634f;
   a.tau = tt.rescale_log2;
   a.fmt = in_format;
-  // AUTO: the pipelined kernel in its persistent form (2.6% faster at
-  // B=2 H=16 N=16384 d=128 causal: 1.52 against 1.56 ms)
+  // AUTO: the ping-pong kernel in its persistent form (B=2 H=16 N=16384
+  // d=128 causal: 1.21 ms against 1.29 ms for the software-pipelined kernel)
   if (tt.kernel == EA_FWD_KERNEL_PERSISTENT || tt.kernel == EA_FWD_KERNEL_AUTO) {
     a.persist_wgs = persistent_workgroups();
     if (a.persist_wgs <= 0) return fail(EA_ERR_HIP, "device CU count unavailable");
   }
-  const hipError_t e = pipelined ? ea::launch_fwd_mx8_sp(a, causal != 0, (hipStream_t)stream)
-                                 : ea::launch_fwd_mx8(a, causal != 0, (hipStream_t)stream);
+  const bool pingpong = tt.kernel == EA_FWD_KERNEL_PINGPONG || tt.kernel == EA_FWD_KERNEL_PERSISTENT ||
+                        tt.kernel == EA_FWD_KERNEL_AUTO;
+  const hipError_t e = pingpong    ? ea::launch_fwd_mx8_pp(a, causal != 0, (hipStream_t)stream)
+                       : pipelined ? ea::launch_fwd_mx8_sp(a, causal != 0, (hipStream_t)stream)
+                                   : ea::launch_fwd_mx8(a, causal != 0, (hipStream_t)stream);
   return hip_status(e, "MX fp8 forward launch");
 }
 

@@ -707,30 +707,415 @@ __device__ __forceinline__ void mx8_sp_tile(const Mx8Args& a, const int xcd, con
   }
 }
 
+// ---------------------------------------------------------------------------
+// Ping-pong variant (same method and numerics; the bf16 ping-pong kernel's
+// schedule with the scaled products). 8 waves in two groups of four: wave w
+// and wave w + 4 share a SIMD, and workgroup barriers keep the groups half a
+// step apart, so while one group issues the eight MX MFMAs of a step (S_s =
+// K_s Q^T and O += V_{s-1} P_{s-1}) from LDS operands, the other runs the
+// softmax of S_{s-1} on the vector ALU. A single wave that interleaves both
+// streams itself issues its vector work at half the rate of two waves; here
+// the matrix core of each SIMD always has one wave feeding it and the vector
+// work of a step is not split into slots around the products.
+// Each wave owns 32 query rows, interleaved between the groups (wave w: rows
+// 64 (w mod 4) + 32 (w div 4)) so both waves of a SIMD meet the causal
+// diagonal at the same step. K/V tiles (64 keys x 128 B) and their scales
+// arrive by LDS DMA -- K issued by group A, V by group B, each at the end of
+// its MFMA part -- into three stages per operand: a stage holds the 8 KB
+// tile and, behind it, 256
+// scale bytes -- for K the 64 dwords of its keys (one e8m0 byte per 32-wide
+// block of d), for V the two 32-key blocks' 128 bytes (one per d column) --
+// so the MFMA part reads every operand, scales included, from LDS. Stages
+// are distinct LDS objects and the loop is unrolled by three, so the
+// compiler's wait tracking sees which stage each read uses. Two changes to
+// the bf16 schedule move vector work out of the softmax phase, which bounds
+// this kernel (the fp8 products take half the matrix-core time of bf16 ones
+// while the exponentials cost the same): the row sum l is accumulated by the
+// matrix core (a fifth P V product against a tile of ones), and the masking
+// and the row max of S_s run in the MFMA part, under its P V products.
+template <bool CAUSAL, int FMT>
+__device__ __forceinline__ void mx8_pp_tile(const Mx8Args& a, const int xcd, const int j) {
+  constexpr int D = 128, BM = kPpBlockM, BN = kFwdBlockN;
+  constexpr int TILE = BN * D;  // bytes per K or V tile
+  constexpr int NDT = D / 32;
+  constexpr int STAGE = TILE + 256;  // tile, then its scale bytes
+  __shared__ __attribute__((aligned(1024))) uint8_t ks0[STAGE], ks1[STAGE], ks2[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs0[STAGE], vs1[STAGE], vs2[STAGE];
+
+  // ---------------- tile assignment: XCD-grouped, heaviest causal row blocks first
+  const int kg = j / a.n_mb;
+  const int r0 = j - kg * a.n_mb;
+  const int g = xcd + 8 * kg;
+  if (g >= a.B * a.Hq) return;
+  const int b = uniform(g / a.Hq);
+  const int h = uniform(g - b * a.Hq);
+  const int mb = uniform(a.n_mb - 1 - r0);
+  const int hk = uniform(h / a.group);
+  const int N = a.N;
+  const int row_lo = mb * BM;
+  int nkeys = N;
+  if constexpr (CAUSAL) nkeys = min(N, row_lo + BM);
+  const int nkb = uniform((nkeys + BN - 1) / BN);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = uniform(tid >> 6), hh = lane >> 5, c = lane & 31;
+  const int grp = w >> 2;
+  const int wave_first_q = row_lo + 64 * (w & 3) + 32 * grp;
+  const int qi = wave_first_q + c;
+  const size_t qstride = (size_t)a.Hq * D, kstride = (size_t)a.Hkv * D;
+
+  // ---------------- Q^T operand and its scales (B of S^T), kept in VGPRs
+  i32x8 qf[2];
+  int qsc[2];
+  {
+    const uint8_t* qp = a.q + ((size_t)b * N + qi) * qstride + (size_t)h * D;
+    uint32_t s4 = 0x7f7f7f7fu;
+    if (qi < N) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const i32x4 lo = *(const i32x4*)(qp + 64 * ks + 16 * hh);
+        const i32x4 hi = *(const i32x4*)(qp + 64 * ks + 32 + 16 * hh);
+        qf[ks] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+      s4 = *(const uint32_t*)(a.qs + (((size_t)b * N + qi) * a.Hq + h) * 4);
+    } else {
+      qf[0] = i32x8{};
+      qf[1] = i32x8{};
+    }
+    qsc[0] = (s4 >> (8 * hh)) & 0xFF;
+    qsc[1] = (s4 >> (8 * (2 + hh))) & 0xFF;
+  }
+
+  // ---------------- DMA. Tiles: wave w of the issuing group fills 1 KB pieces
+  // 2 (w mod 4) and 2 (w mod 4) + 1 of a tile; lane s of piece p lands at tile byte
+  // 1024 p + 16 s = row 8 p + s / 8, slot s % 8, and fetches the global chunk
+  // (s % 8) ^ swz8(row) of that row. A tile at or past nkb gets no records,
+  // so its DMA writes zeros without touching memory; only the last tile can
+  // be partial. Scales (one dword per lane): wave 0 the K scale dwords of the
+  // tile's 64 keys, wave 5 the V scale bytes of its two 32-key blocks (lane s:
+  // block s / 32, columns 4 (s % 32) .. +3).
+  const uint8_t* kg_base = a.k + ((size_t)b * N) * kstride + (size_t)hk * D;
+  const uint8_t* vg_base = a.v + ((size_t)b * N) * kstride + (size_t)hk * D;
+  uint32_t dma_off[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int drow = 8 * (2 * (w & 3) + i) + (lane >> 3);
+    dma_off[i] = (uint32_t)(drow * (int)kstride + (((lane & 7) ^ swz8(drow)) << 4));
+  }
+  const uint32_t nrec_full = (uint32_t)uniform((BN - 1) * (int)kstride + D);
+  const uint32_t nrec_last = (uint32_t)uniform(nkb > 0 ? (min(N - (nkb - 1) * BN, BN) - 1) * (int)kstride + D : 0);
+  const uint8_t* ksc_base = a.ks + ((size_t)b * N * a.Hkv + hk) * 4;
+  const int nkb32 = N / 32;
+  const uint8_t* vsc_base = a.vs + ((size_t)b * nkb32 * a.Hkv + hk) * D;
+  const uint32_t ksc_off = (uint32_t)(lane * a.Hkv * 4);
+  const uint32_t vsc_off = (uint32_t)((lane >> 5) * a.Hkv * D + 4 * (lane & 31));
+  auto dma_k = [&](EA_LDS uint8_t* stage, int t) __attribute__((always_inline)) {
+    const uint32_t nrec = t < nkb - 1 ? nrec_full : (t == nkb - 1 ? nrec_last : 0u);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(kg_base + (size_t)t * (BN * kstride), nrec);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) buffer_load16_lds(rs, (EA_LDS void*)(stage + 1024 * (2 * (w & 3) + i)), dma_off[i]);
+    if (w == 0) {
+      const int keys = t < nkb ? min(N - t * BN, BN) : 0;
+      const __amdgpu_buffer_rsrc_t rsc =
+          make_rsrc(ksc_base + (size_t)t * BN * a.Hkv * 4, keys > 0 ? (uint32_t)((keys - 1) * a.Hkv * 4 + 4) : 0u);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsc, (EA_LDS void*)(stage + TILE), 4, (int)ksc_off, 0, 0, 0);
+    }
+  };
+  auto dma_v = [&](EA_LDS uint8_t* stage, int t) __attribute__((always_inline)) {
+    const uint32_t nrec = t < nkb - 1 ? nrec_full : (t == nkb - 1 ? nrec_last : 0u);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(vg_base + (size_t)t * (BN * kstride), nrec);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) buffer_load16_lds(rs, (EA_LDS void*)(stage + 1024 * (2 * (w & 3) + i)), dma_off[i]);
+    if (w == 5) {
+      const int blocks = t < nkb ? min(nkb32 - 2 * t, 2) : 0;
+      const __amdgpu_buffer_rsrc_t rsc = make_rsrc(vsc_base + (size_t)(2 * t) * a.Hkv * D,
+                                                   blocks > 0 ? (uint32_t)((blocks - 1) * a.Hkv * D + D) : 0u);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsc, (EA_LDS void*)(stage + TILE), 4, (int)vsc_off, 0, 0, 0);
+    }
+  };
+  auto kstage = [&](int r) __attribute__((always_inline)) -> EA_LDS uint8_t* {
+    return r == 0 ? (EA_LDS uint8_t*)ks0 : r == 1 ? (EA_LDS uint8_t*)ks1 : (EA_LDS uint8_t*)ks2;
+  };
+  auto vstage = [&](int r) __attribute__((always_inline)) -> EA_LDS uint8_t* {
+    return r == 0 ? (EA_LDS uint8_t*)vs0 : r == 1 ? (EA_LDS uint8_t*)vs1 : (EA_LDS uint8_t*)vs2;
+  };
+
+  // LDS byte offsets of this lane's operand reads: K rows c and c + 32
+  // (chunks 4 k2 + hh and 4 k2 + 2 + hh), V^T transposed reads, the K scale
+  // dword of key c, the V scale byte of (block hh, column 32 dt + c)
+  int k_off[2][2];
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2) {
+    k_off[k2][0] = tile8_off(c, 64 * k2 + 16 * hh);
+    k_off[k2][1] = tile8_off(c, 64 * k2 + 32 + 16 * hh);
+  }
+  const int jj = (lane & 15) >> 1;
+  const int tr_row = 4 * hh + jj + 4 * (jj >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+  int v_off[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) v_off[dt] = tile8_off(tr_row, 32 * dt + tr_col);
+  int ksc_lds = TILE + 4 * c;
+  int vsc_lds = TILE + 128 * hh + c;
+
+  float m_run = kNegInf;
+  f32x16 oacc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16{};
+  // the running row sum l, accumulated by the matrix core: a fifth P V
+  // product whose A operand is all ones (e4m3 1.0) leaves, in every element
+  // of lane (c, hh), the sum over the tile's keys of row c's e4m3-rounded P --
+  // the same values that multiply V
+  f32x16 lacc = f32x16{};
+  const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                      0x38383838, 0x38383838, 0x38383838, 0x38383838};
+  f32x16 s0 = f32x16{}, s1 = f32x16{};
+  i32x8 pb = i32x8{};  // P^T (e4m3) of the last softmax phase
+  const float sl = a.scale_log2;
+  const float tau = a.tau;
+
+  float m_new = kNegInf;  // the row max the MFMA part found for the next softmax phase
+
+  // ---- MFMA part of step s: S_s = K_s Q^T into s0, s1, then l and O +=
+  // V_{s-1} P_{s-1} (pb), and under those five products the masking and the
+  // row max of S_s (vector work that only needs S_s, done here so the
+  // softmax phase holds only what needs the new max). For a tile this wave
+  // skips, the softmax phase left P = 0; stages past the end hold zeros from
+  // the DMA (scale code 0 is 2^-127, finite), and the V stage read at the
+  // first step is zeroed, so the extra products add exact zeros.
+  auto mfma_part = [&](const EA_LDS uint8_t* kst, const EA_LDS uint8_t* vst, int s) __attribute__((always_inline)) {
+    // the offsets pass through an empty asm, so the stage base folds into
+    // the ds_read offset field here instead of a register per stage
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      k_off[k2][0] = launder(k_off[k2][0]);
+      k_off[k2][1] = launder(k_off[k2][1]);
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) v_off[dt] = launder(v_off[dt]);
+    ksc_lds = launder(ksc_lds);
+    vsc_lds = launder(vsc_lds);
+    __builtin_amdgcn_s_setprio(1);
+    // K scale of (key row, d block 2 k2 + hh) is byte 2 k2 + hh of its
+    // dword: after a shift by 8 hh it is byte 2 k2, which the MFMA selects
+    const int ksh0 = (int)(lds_load<uint32_t>(kst + ksc_lds) >> (8 * hh));
+    const int ksh1 = (int)(lds_load<uint32_t>(kst + ksc_lds + 128) >> (8 * hh));
+    i32x8 ka[4];
+#pragma unroll
+    for (int jx = 0; jx < 4; ++jx) {
+      const int t = jx & 1, k2 = jx >> 1;
+      const i32x4 lo = lds_load<i32x4>(kst + k_off[k2][0] + 32 * D * t);
+      const i32x4 hi = lds_load<i32x4>(kst + k_off[k2][1] + 32 * D * t);
+      ka[jx] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+    int vsc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) vsc[dt] = (int)lds_load<uint8_t>(vst + vsc_lds + 32 * dt);
+    i32x8 va[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const i32x2 q0 = ds_read_tr8(vst + v_off[dt]);
+      const i32x2 q1 = ds_read_tr8(vst + v_off[dt] + 16 * D);
+      const i32x2 q2 = ds_read_tr8(vst + v_off[dt] + 32 * D);
+      const i32x2 q3 = ds_read_tr8(vst + v_off[dt] + 48 * D);
+      va[dt] = i32x8{q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
+    }
+    s0 = mfma_mx8_sel<0, FMT, FMT>(ka[0], qf[0], f32x16{}, ksh0, qsc[0]);
+    s1 = mfma_mx8_sel<0, FMT, FMT>(ka[1], qf[0], f32x16{}, ksh1, qsc[0]);
+    s0 = mfma_mx8_sel<2, FMT, FMT>(ka[2], qf[1], s0, ksh0, qsc[1]);
+    s1 = mfma_mx8_sel<2, FMT, FMT>(ka[3], qf[1], s1, ksh1, qsc[1]);
+    // the K scales and operands (10 reads) first, then four reads after each
+    // S product and the last four behind them: every product's operands were
+    // asked for at least one product (64 cycles) earlier
+    __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    // masking (diagonal and ragged tiles only: this branch waits for S_s)
+    const int kbase = s * BN;
+    bool need_mask = kbase + BN > N;
+    if constexpr (CAUSAL) need_mask = need_mask || (kbase + BN - 1 > wave_first_q);
+    if (need_mask) {
+      int lim = N;
+      if constexpr (CAUSAL) lim = min(N, qi + 1);
+      const int rel = lim - kbase - 4 * hh;  // element i is valid iff its key offset < rel
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int ko = 8 * (i >> 2) + (i & 3);
+        s0[i] = (ko < rel) ? s0[i] : kNegInf;
+        s1[i] = (ko + 32 < rel) ? s1[i] : kNegInf;
+      }
+    }
+    lacc = mfma_mx8<kFmtE4M3, kFmtE4M3>(ones, pb, lacc, kScaleOne, kScaleOne);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) oacc[dt] = mfma_mx8<FMT, kFmtE4M3>(va[dt], pb, oacc[dt], vsc[dt], kScaleOne);
+    // row max over this lane's 32 keys in two chains of three-input max,
+    // then over the partner lane's 32
+    float mx0 = kNegInf, mx1 = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      mx0 = __builtin_fmaxf(__builtin_fmaxf(mx0, s0[i]), s1[i]);
+      mx1 = __builtin_fmaxf(__builtin_fmaxf(mx1, s0[i + 1]), s1[i + 1]);
+    }
+    const float mx = max_with_partner32(__builtin_fmaxf(mx0, mx1));
+    m_new = __builtin_fmaxf(m_run, mx * sl);
+    // a product, then a share of the vector work, five times
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+    __builtin_amdgcn_s_setprio(0);
+    // the products are issued here, before the barrier (the compiler would
+    // otherwise sink them into the softmax phase, next to their first use)
+    keep(lacc);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) keep(oacc[dt]);
+    keep(s0);
+    keep(s1);
+    keep(m_new);
+  };
+
+  // ---- softmax phase of step s: P_s (e4m3, in pb) from S_s and the row max
+  // m_new of the MFMA part; lazy rescale of O and l with threshold tau (log2)
+  auto valu_part = [&](bool act) __attribute__((always_inline)) {
+    if (!act) {
+      pb = i32x8{};
+      return;
+    }
+    if (__ballot(m_new > m_run + tau)) {
+      const float alpha = (m_run == kNegInf) ? 0.f : exp2_hw(m_run - m_new);
+      lacc *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+      m_run = m_new;
+    }
+    const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s0[i] = exp2_hw(__builtin_fmaf(s0[i], sl, neg_m));
+      s1[i] = exp2_hw(__builtin_fmaf(s1[i], sl, neg_m));
+    }
+    // P^T -> e4m3 (scale 1): bytes 0..15 key tile 0, 16..31 key tile 1
+#pragma unroll
+    for (int wd = 0; wd < 4; ++wd) {
+      pb[wd] = pack_fp8x4(s0[4 * wd], s0[4 * wd + 1], s0[4 * wd + 2], s0[4 * wd + 3]);
+      pb[4 + wd] = pack_fp8x4(s1[4 * wd], s1[4 * wd + 1], s1[4 * wd + 2], s1[4 * wd + 3]);
+    }
+  };
+
+  // a tile is fully masked for this wave (wave-uniform) if its first key lies
+  // beyond the wave's last row
+  auto tile_dead = [&](int s) __attribute__((always_inline)) { return CAUSAL && s * BN > wave_first_q + 31; };
+
+  // ---- one step: MFMA part, DMA, barrier, softmax phase, barrier. Group B
+  // starts one barrier late. At the end of its MFMA part group A issues
+  // K_{s+2} (into the stage K_{s-1} left, which both groups finished reading
+  // in step s - 1) and waits for it at the end of its next softmax phase;
+  // group B issues V_{s+1} (into the stage of V_{s-2}) and waits for it at the
+  // end of its next MFMA part. Either wait leaves only the newest pieces in
+  // flight and comes before the barrier after which the other group reads
+  // them. Waves 0 and 5 issue one scale DMA more.
+  auto step = [&](int r, int s) __attribute__((always_inline)) {
+    const bool act = s < nkb && !tile_dead(s);
+    mfma_part(kstage(r), vstage((r + 2) % 3), s);
+    if (grp == 0) {
+      dma_k(kstage((r + 2) % 3), s + 2);
+    } else {
+      dma_v(vstage((r + 1) % 3), s + 1);
+      // V_s (issued one step earlier) has landed before the barrier after
+      // which group A reads it
+      if (w == 5) {
+        wait_vmcnt<3>();
+      } else {
+        wait_vmcnt<2>();
+      }
+    }
+    pp_barrier();
+    valu_part(act);
+    if (grp == 0) {
+      if (w == 0) {
+        wait_vmcnt<3>();
+      } else {
+        wait_vmcnt<2>();
+      }
+    }
+    pp_barrier();
+  };
+
+  // prologue: K_0, K_1 and V_0 with their scales; the V stage (tile and
+  // scales) that step 0 multiplies by P = 0 is zeroed so it holds no NaN code
+  lds_store<i32x4>((EA_LDS uint8_t*)vs2 + 16 * tid, i32x4{});
+  if (tid < 16) lds_store<i32x4>((EA_LDS uint8_t*)vs2 + TILE + 16 * tid, i32x4{});
+  if (nkb > 0) {
+    if (grp == 0) {
+      dma_k(kstage(0), 0);
+      dma_k(kstage(1), 1);
+    } else {
+      dma_v(vstage(0), 0);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  if (grp == 1) pp_barrier();  // group B runs one phase behind
+  for (int s = 0; s <= nkb; s += 3) {
+    step(0, s);
+    if (s + 1 <= nkb) step(1, s + 1);
+    if (s + 2 <= nkb) step(2, s + 2);
+  }
+  if (grp == 0) pp_barrier();
+  // no DMA may still be writing this workgroup's LDS when it exits
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // ---------------- epilogue (every element of lacc holds this row's l)
+  const float l_tot = lacc[0];
+  const float inv = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
+  if (qi < N) {
+    uint16_t* op = a.o + ((size_t)b * N + qi) * qstride + (size_t)h * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * dt + 8 * g4 + 4 * hh;
+        uint2 val;
+        val.x = pack_bf16x2(oacc[dt][4 * g4] * inv, oacc[dt][4 * g4 + 1] * inv);
+        val.y = pack_bf16x2(oacc[dt][4 * g4 + 2] * inv, oacc[dt][4 * g4 + 3] * inv);
+        *(uint2*)(op + d0) = val;
+      }
+    }
+    if (a.lse != nullptr && hh == 0) {
+      const float v = (l_tot > 0.f && m_run != kNegInf) ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
+      a.lse[((size_t)b * a.Hq + h) * N + qi] = v;
+    }
+  }
+}
+
+template <bool CAUSAL, int FMT>
+__global__ __launch_bounds__(512, 1) void fwd_mx8_pp_kernel(Mx8Args a) {
+  mx8_pp_tile<CAUSAL, FMT>(a, blockIdx.x & 7, blockIdx.x >> 3);
+}
+
+template <bool CAUSAL, int FMT>
+__global__ __launch_bounds__(512, 1) void fwd_mx8_pp_persistent_kernel(Mx8Args a) {
+  persistent_snake(uniform(a.tiles_per_xcd), [&](int xcd, int j) { mx8_pp_tile<CAUSAL, FMT>(a, xcd, j); });
+}
+
 template <bool CAUSAL, int FMT>
 __global__ __launch_bounds__(512, 1) void fwd_mx8_sp_kernel(Mx8Args a) {
   mx8_sp_tile<CAUSAL, FMT>(a, blockIdx.x & 7, blockIdx.x >> 3);
 }
 
-// persistent form: one workgroup per CU (persistent_snake in ea_fwd_common.h)
-template <bool CAUSAL, int FMT>
-__global__ __launch_bounds__(512, 1) void fwd_mx8_sp_persistent_kernel(Mx8Args a) {
-  persistent_snake(uniform(a.tiles_per_xcd), [&](int xcd, int j) { mx8_sp_tile<CAUSAL, FMT>(a, xcd, j); });
-}
 
 template <int FMT>
 static hipError_t launch_mx8_f(const Mx8Args& a, bool causal, bool pipelined, hipStream_t s) {
   const int grid = 8 * ((a.B * a.Hq + 7) / 8) * a.n_mb;
-  if (pipelined && a.persist_wgs > 0) {
-    Mx8Args b = a;
-    b.tiles_per_xcd = grid / 8;
-    const int w = max(1, min(a.persist_wgs / 8, b.tiles_per_xcd));  // workgroups per XCD
-    if (causal) {
-      hipLaunchKernelGGL((fwd_mx8_sp_persistent_kernel<true, FMT>), dim3(8 * w), dim3(512), 0, s, b);
-    } else {
-      hipLaunchKernelGGL((fwd_mx8_sp_persistent_kernel<false, FMT>), dim3(8 * w), dim3(512), 0, s, b);
-    }
-  } else if (pipelined) {
+  if (pipelined) {
     if (causal) {
       hipLaunchKernelGGL((fwd_mx8_sp_kernel<true, FMT>), dim3(grid), dim3(512), 0, s, a);
     } else {
@@ -744,6 +1129,32 @@ static hipError_t launch_mx8_f(const Mx8Args& a, bool causal, bool pipelined, hi
     }
   }
   return hipGetLastError();
+}
+
+// persistent form (one workgroup per CU walking the XCD-grouped tile list,
+// persistent_snake in ea_fwd_common.h) when a.persist_wgs > 0
+template <int FMT>
+static hipError_t launch_mx8_pp_f(const Mx8Args& a, bool causal, hipStream_t s) {
+  const int grid = 8 * ((a.B * a.Hq + 7) / 8) * a.n_mb;
+  if (a.persist_wgs > 0) {
+    Mx8Args b = a;
+    b.tiles_per_xcd = grid / 8;
+    const int w = max(1, min(a.persist_wgs / 8, b.tiles_per_xcd));  // workgroups per XCD
+    if (causal) {
+      hipLaunchKernelGGL((fwd_mx8_pp_persistent_kernel<true, FMT>), dim3(8 * w), dim3(512), 0, s, b);
+    } else {
+      hipLaunchKernelGGL((fwd_mx8_pp_persistent_kernel<false, FMT>), dim3(8 * w), dim3(512), 0, s, b);
+    }
+  } else if (causal) {
+    hipLaunchKernelGGL((fwd_mx8_pp_kernel<true, FMT>), dim3(grid), dim3(512), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((fwd_mx8_pp_kernel<false, FMT>), dim3(grid), dim3(512), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_mx8_pp(const Mx8Args& a, bool causal, hipStream_t s) {
+  return a.fmt == kFmtE5M2 ? launch_mx8_pp_f<kFmtE5M2>(a, causal, s) : launch_mx8_pp_f<kFmtE4M3>(a, causal, s);
 }
 
 hipError_t launch_fwd_mx8_sp(const Mx8Args& a, bool causal, hipStream_t s) {

@@ -67,12 +67,16 @@ struct Mx8Args {
   float scale_log2;
   float tau;
   int fmt;  // Q/K/V codes: 0 = OCP e4m3, 1 = OCP e5m2
-  int persist_wgs;    // pipelined kernel: > 0 runs the persistent form (workgroups, multiple of 8)
+  int persist_wgs;    // ping-pong kernel: > 0 runs the persistent form (workgroups, multiple of 8)
   int tiles_per_xcd;  // set by the launcher for the persistent form
 };
 hipError_t launch_fwd_mx8(const Mx8Args& a, bool causal, hipStream_t s);
-// 8-wave software-pipelined MX fp8 forward; a.n_mb counts kPpBlockM-row blocks
+// 8-wave software-pipelined MX fp8 forward (one workgroup per tile); a.n_mb
+// counts kPpBlockM-row blocks
 hipError_t launch_fwd_mx8_sp(const Mx8Args& a, bool causal, hipStream_t s);
+// 8-wave ping-pong MX fp8 forward (persistent when a.persist_wgs > 0); a.n_mb
+// counts kPpBlockM-row blocks
+hipError_t launch_fwd_mx8_pp(const Mx8Args& a, bool causal, hipStream_t s);
 
 // Backward (bf16, dense BSHD): dQ, dK, dV of O = softmax(scale Q K^T) V for
 // the output gradient dout, from the forward's O and lse.

@@ -216,9 +216,11 @@ ea_status ea_attn_fwd_mx8(const void* q8, const void* k8, const void* v8,
 /*
  * ea_attn_fwd_mx8_tuned -- ea_attn_fwd_mx8 with forward tuning (NULL = the
  * defaults). tuning->kernel selects EA_FWD_KERNEL_4WAVE,
- * EA_FWD_KERNEL_PIPELINED or EA_FWD_KERNEL_PERSISTENT (the pipelined kernel
- * with one workgroup per CU; AUTO: that persistent form); EA_FWD_KERNEL_PINGPONG,
- * EA_FWD_KERNEL_UNROLL_KV,
+ * EA_FWD_KERNEL_PINGPONG (8 waves in two groups alternating the scaled
+ * products and the softmax, as the bf16 ping-pong kernel), EA_FWD_KERNEL_PERSISTENT
+ * (that kernel with one workgroup per CU; AUTO: this form) or
+ * EA_FWD_KERNEL_PIPELINED (8 waves, each interleaving its own products and
+ * softmax); EA_FWD_KERNEL_UNROLL_KV,
  * exp_mode other than EA_EXP_HW and natural_order = 1 return
  * EA_ERR_UNSUPPORTED. rescale_log2 is the lazy-rescale threshold, which also
  * bounds P before its e4m3 rounding (P <= 2^rescale_log2): values above 8.807

@@ -116,7 +116,6 @@ def test_mx8_tuning_errors(lib):
     def call(t):
         return f(P, P, P, P, P, P, P, None, 1, 64, 2, 2, 128, 1, 0.1, ctypes.byref(t), None)
 
-    assert call(ea.tuning(kernel=2)) == -2      # no ping-pong fp8 kernel
     assert call(ea.tuning(exp_mode=1)) == -2    # hardware exponential only
     assert call(ea.tuning(natural_order=1)) == -2
     assert call(ea.tuning(kernel=5)) == -2      # no unroll-KV fp8 kernel
