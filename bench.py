@@ -65,6 +65,8 @@ TRAFFIC = {
     "ea::decode_split_kernel<page16> + ea::decode_combine_kernel": 4_866_191_360,
     # fwd_mx8_sp_kernel<causal, e4m3>: 173,648 KiB fetched, 133,336 KiB written
     "ea::fwd_mx8_sp_kernel<causal, e4m3>": 492_166_827,
+    # fwd_mx8_pp_persistent_kernel<causal, e4m3>: 165,571 KiB fetched, 133,285 KiB written
+    "ea::fwd_mx8_pp_persistent_kernel<causal, e4m3>": 475_573_248,
 }
 
 

@@ -5,11 +5,16 @@ output o and fp32 lse (from ea.attn_fwd on the same inputs), and an output
 gradient dout drawn iid N(0,1) and rounded to bf16. The oracle computes dq, dk,
 dv from q, k, v, dout alone (full-row softmax in fp64).
 
-Tolerance (per (batch, head) slice of each gradient): the kernel rounds P and
-dS to bf16 (relative 2^-9) as MFMA operands, reads the forward's bf16 o for
-D = rowsum(dout * o), and stores bf16; each output element is a sum of up to
-N such terms. The criteria are normwise ||g - g_ref||_F <= 1e-2 ||g_ref||_F
-and elementwise |g - g_ref| <= 1e-2 max|g_ref| + 1e-2 |g_ref|.
+Tolerance (per (batch, head) slice of each gradient), from the bf16 steps of
+the computation, each a relative rounding of at most u = 2^-9: the kernel
+rounds P and dS to bf16 as MFMA operands (independent errors of u per term
+of a sum over up to N keys or rows, which average out), takes D =
+rowsum(dout * o) from the forward's bf16 o (one more u on every dS term of a
+row, the same sign across the row), and stores bf16 (u per element). The
+criteria allow about 2.5 u normwise, ||g - g_ref||_F <= 5e-3 ||g_ref||_F, and
+elementwise |g - g_ref| <= 4 u max|g_ref| + 2 u |g_ref| (the first term
+covers the summed operand roundings, which scale with the slice, not the
+element; the second the output rounding and the D error).
 """
 import numpy as np
 import pytest
@@ -21,8 +26,10 @@ from _helpers import dev_bf16, f64, host_bits, log
 
 pytestmark = pytest.mark.gpu
 
-NORM_TOL = 1e-2
-ELEM_TOL = 1e-2
+U = 2.0 ** -9       # bf16 unit roundoff
+NORM_TOL = 5e-3
+ELEM_ABS = 4 * U    # times max |g_ref| over the slice
+ELEM_REL = 2 * U    # times |g_ref|
 
 
 def run_bwd(inp, do_bits, schedule=0):
@@ -46,7 +53,7 @@ def check(got, ref, what):
                 assert np.all(g == 0), f"{what}[b={b},h={h}] should be zero"
                 continue
             worst_n = max(worst_n, np.linalg.norm(g - r) / den)
-            lim = ELEM_TOL * np.abs(r).max() + ELEM_TOL * np.abs(r)
+            lim = ELEM_ABS * np.abs(r).max() + ELEM_REL * np.abs(r)
             worst_e = max(worst_e, float(np.max(np.abs(g - r) / lim)))
     log(f"  {what}: normwise {worst_n:.2e}, elementwise {worst_e:.2f} of the bound")
     assert np.isfinite(got).all(), what
