@@ -728,11 +728,11 @@ __device__ __forceinline__ void mx8_sp_tile(const Mx8Args& a, const int xcd, con
 // so the MFMA part reads every operand, scales included, from LDS. Stages
 // are distinct LDS objects and the loop is unrolled by three, so the
 // compiler's wait tracking sees which stage each read uses. Two changes to
-// the bf16 schedule move vector work out of the softmax phase, which bounds
-// this kernel (the fp8 products take half the matrix-core time of bf16 ones
-// while the exponentials cost the same): the row sum l is accumulated by the
-// matrix core (a fifth P V product against a tile of ones), and the masking
-// and the row max of S_s run in the MFMA part, under its P V products.
+// the bf16 schedule move work out of the softmax phase, which bounds this
+// kernel (the fp8 products take half the matrix-core time of bf16 ones while
+// the exponentials cost the same): the masking and the row max of S_s run in
+// the MFMA part, under its P V products, and each group issues half of the
+// DMA at the end of its MFMA part.
 template <bool CAUSAL, int FMT>
 __device__ __forceinline__ void mx8_pp_tile(const Mx8Args& a, const int xcd, const int j) {
   constexpr int D = 128, BM = kPpBlockM, BN = kFwdBlockN;
@@ -858,17 +858,10 @@ __device__ __forceinline__ void mx8_pp_tile(const Mx8Args& a, const int xcd, con
   int ksc_lds = TILE + 4 * c;
   int vsc_lds = TILE + 128 * hh + c;
 
-  float m_run = kNegInf;
+  float m_run = kNegInf, l_run = 0.f;
   f32x16 oacc[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16{};
-  // the running row sum l, accumulated by the matrix core: a fifth P V
-  // product whose A operand is all ones (e4m3 1.0) leaves, in every element
-  // of lane (c, hh), the sum over the tile's keys of row c's e4m3-rounded P --
-  // the same values that multiply V
-  f32x16 lacc = f32x16{};
-  const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                      0x38383838, 0x38383838, 0x38383838, 0x38383838};
   f32x16 s0 = f32x16{}, s1 = f32x16{};
   i32x8 pb = i32x8{};  // P^T (e4m3) of the last softmax phase
   const float sl = a.scale_log2;
@@ -876,9 +869,9 @@ __device__ __forceinline__ void mx8_pp_tile(const Mx8Args& a, const int xcd, con
 
   float m_new = kNegInf;  // the row max the MFMA part found for the next softmax phase
 
-  // ---- MFMA part of step s: S_s = K_s Q^T into s0, s1, then l and O +=
-  // V_{s-1} P_{s-1} (pb), and under those five products the masking and the
-  // row max of S_s (vector work that only needs S_s, done here so the
+  // ---- MFMA part of step s: S_s = K_s Q^T into s0, s1, then O += V_{s-1}
+  // P_{s-1} (pb), and under those four products the masking and the row max
+  // of S_s (vector work that only needs S_s, done here so the
   // softmax phase holds only what needs the new max). For a tile this wave
   // skips, the softmax phase left P = 0; stages past the end hold zeros from
   // the DMA (scale code 0 is 2^-127, finite), and the V stage read at the
@@ -949,7 +942,6 @@ __device__ __forceinline__ void mx8_pp_tile(const Mx8Args& a, const int xcd, con
         s1[i] = (ko + 32 < rel) ? s1[i] : kNegInf;
       }
     }
-    lacc = mfma_mx8<kFmtE4M3, kFmtE4M3>(ones, pb, lacc, kScaleOne, kScaleOne);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) oacc[dt] = mfma_mx8<FMT, kFmtE4M3>(va[dt], pb, oacc[dt], vsc[dt], kScaleOne);
     // row max over this lane's 32 keys in two chains of three-input max,
@@ -962,18 +954,17 @@ __device__ __forceinline__ void mx8_pp_tile(const Mx8Args& a, const int xcd, con
     }
     const float mx = max_with_partner32(__builtin_fmaxf(mx0, mx1));
     m_new = __builtin_fmaxf(m_run, mx * sl);
-    // a product, then a share of the vector work, five times
+    // a product, then a share of the vector work, four times
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 3; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
     __builtin_amdgcn_s_setprio(0);
     // the products are issued here, before the barrier (the compiler would
     // otherwise sink them into the softmax phase, next to their first use)
-    keep(lacc);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) keep(oacc[dt]);
     keep(s0);
@@ -990,7 +981,7 @@ __device__ __forceinline__ void mx8_pp_tile(const Mx8Args& a, const int xcd, con
     }
     if (__ballot(m_new > m_run + tau)) {
       const float alpha = (m_run == kNegInf) ? 0.f : exp2_hw(m_run - m_new);
-      lacc *= alpha;
+      l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
       m_run = m_new;
@@ -1001,6 +992,14 @@ __device__ __forceinline__ void mx8_pp_tile(const Mx8Args& a, const int xcd, con
       s0[i] = exp2_hw(__builtin_fmaf(s0[i], sl, neg_m));
       s1[i] = exp2_hw(__builtin_fmaf(s1[i], sl, neg_m));
     }
+    // the row sum over P in fp32, before its e4m3 rounding
+    float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      ls0 += s0[i];
+      ls1 += s1[i];
+    }
+    l_run += ls0 + ls1;
     // P^T -> e4m3 (scale 1): bytes 0..15 key tile 0, 16..31 key tile 1
 #pragma unroll
     for (int wd = 0; wd < 4; ++wd) {
@@ -1073,8 +1072,8 @@ __device__ __forceinline__ void mx8_pp_tile(const Mx8Args& a, const int xcd, con
   // no DMA may still be writing this workgroup's LDS when it exits
   __builtin_amdgcn_s_waitcnt(0);
 
-  // ---------------- epilogue (every element of lacc holds this row's l)
-  const float l_tot = lacc[0];
+  // ---------------- epilogue
+  const float l_tot = sum_with_partner32(l_run);
   const float inv = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
   if (qi < N) {
     uint16_t* op = a.o + ((size_t)b * N + qi) * qstride + (size_t)h * D;
