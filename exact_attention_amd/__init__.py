@@ -68,6 +68,10 @@ _SIGNATURES = {
     "ea_test_fwd_rescale_stats": ([_c_void_p] * 5 + [_c_int] * 6 + [_c_float, _c_float, _c_void_p, _c_size_t,
                                                                    _c_void_p], _c_int),
     "ea_test_wall_clock_khz": ([_c_int, _c_void_p], _c_int),
+    "ea_test_fwd_tiles": ([_c_int] * 3, _c_size_t),
+    "ea_test_decode_gather": ([_c_void_p] * 5 + [_c_int] * 8 + [_c_void_p, _c_void_p, _c_size_t, _c_void_p,
+                                                                _c_size_t, _c_void_p], _c_int),
+    "ea_test_fwd_tile_order": ([_c_int] * 5 + [_c_void_p, _c_size_t, _c_void_p], _c_int),
 }
 
 _lib = None
@@ -350,6 +354,31 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, page_size: int
     return o, lse
 
 
+def test_decode_gather(q, k_cache, v_cache, block_table, seq_lens, *, num_splits: int = 0, fill: int = 0x7FC1):
+    """Test-only page-gather dump of the paged decode: the K and V rows its
+    split kernel gathers, by (sequence, token, KV head), as dense bf16
+    [B, max_pages * page, Hkv, d] tensors; rows it does not write keep the
+    16-bit pattern ``fill``. Arguments as for attn_decode_paged."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _shape(v_cache, "v_cache", k_cache.shape)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    B, Hq, d = q.shape
+    P, ps, Hkv, _ = k_cache.shape
+    max_pages = block_table.shape[1]
+    shape = (B, max_pages * ps, Hkv, d)
+    dk = torch.full(shape, fill, dtype=torch.int16, device=q.device)
+    dv = torch.full(shape, fill, dtype=torch.int16, device=q.device)
+    need = decode_workspace_size(B, Hq, Hkv, d, max_pages * ps, ps, num_splits)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = lib().ea_test_decode_gather(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+                                     B, Hq, Hkv, d, ps, P, max_pages, int(num_splits), _ptr(dk), _ptr(dv),
+                                     dk.numel(), _ptr(ws), ws.numel(), _stream(q))
+    _check(st, "ea_test_decode_gather")
+    return dk, dv
+
+
 def test_fwd_rescale_stats(q, k, v, causal: bool, scale: float | None = None, rescale_log2: float = 8.0):
     """Test-only: the default dense forward (d = 128) plus its per-wave
     lazy-rescale and clock statistics. Returns (o, lse, stats int32
@@ -373,6 +402,18 @@ def test_fwd_rescale_stats(q, k, v, causal: bool, scale: float | None = None, re
                                          _stream(q))
     _check(st, "ea_test_fwd_rescale_stats")
     return o, lse, stats.view(-1, 8, 4)
+
+
+def test_fwd_tile_order(B: int, Nq: int, Nk: int, Hq: int, causal: bool, device="cuda"):
+    """Test-only: (batch, head, 256-row block) of every work tile of the dense
+    forward in dispatch order, as computed on the device; -1 rows are padding.
+    Returns an int32 tensor [tiles, 3] on the host."""
+    n = int(lib().ea_test_fwd_tiles(B, Nq, Hq))
+    out = torch.full((3 * n,), -2, dtype=torch.int32, device=device)
+    st = lib().ea_test_fwd_tile_order(B, Nq, Nk, Hq, int(bool(causal)), _ptr(out), 3 * n,
+                                      _stream(out))
+    _check(st, "ea_test_fwd_tile_order")
+    return out.view(n, 3).cpu()
 
 
 def test_wall_clock_khz(device: int = 0) -> int:

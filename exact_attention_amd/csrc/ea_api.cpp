@@ -172,6 +172,31 @@ size_t ea_test_fwd_rescale_stats_len(int B, int Nq, int Hq) {
   return (size_t)tiles * 32;
 }
 
+size_t ea_test_fwd_tiles(int B, int Nq, int Hq) {
+  if (B <= 0 || Nq <= 0 || Hq <= 0) return 0;
+  return (size_t)(((B * (long long)Hq + 7) / 8) * 8 * ((Nq + ea::kPpBlockM - 1) / ea::kPpBlockM));
+}
+
+ea_status ea_test_fwd_tile_order(int B, int Nq, int Nk, int Hq, int causal, int* out, size_t out_len, void* stream) {
+  if (out == nullptr) return fail(EA_ERR_INVALID, "out must be non-null");
+  if (B <= 0 || Nq <= 0 || Nk <= 0 || Hq <= 0) return fail(EA_ERR_INVALID, "B, Nq, Nk and Hq must be positive");
+  if (causal != 0 && causal != 1) return fail(EA_ERR_INVALID, "causal must be 0 or 1");
+  if ((long long)B * Nq >= (1LL << 31) || (long long)B * Nk >= (1LL << 31))
+    return fail(EA_ERR_UNSUPPORTED, "B * N must be below 2^31");
+  const size_t need = 3 * ea_test_fwd_tiles(B, Nq, Hq);
+  if (out_len < need) return fail(EA_ERR_WORKSPACE, "out needs %zu ints, %zu given", need, out_len);
+  ea::FwdArgs a{};
+  a.nseq = B;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.Hq = Hq;
+  a.Hkv = Hq;
+  a.group = 1;
+  a.total_q = B * Nq;
+  a.n_mb = (Nq + ea::kPpBlockM - 1) / ea::kPpBlockM;
+  return hip_status(ea::launch_fwd_tile_order(a, causal != 0, out, (hipStream_t)stream), "tile order launch");
+}
+
 ea_status ea_test_wall_clock_khz(int device, int* khz) {
   if (khz == nullptr) return fail(EA_ERR_INVALID, "khz must be non-null");
   return hip_status(hipDeviceGetAttribute(khz, hipDeviceAttributeWallClockRate, device), "wall clock rate query");
@@ -552,6 +577,33 @@ ea_status ea_attn_decode_paged(const void* q, const void* k_cache, const void* v
                 workspace == nullptr ? (size_t)0 : workspace_bytes);
   ea::decode_bind_workspace(a, workspace);
   return hip_status(ea::launch_decode(a, (hipStream_t)stream), "paged decode launch");
+}
+
+ea_status ea_test_decode_gather(const void* q, const void* k_cache, const void* v_cache, const int* block_table,
+                                const int* seq_lens, int B, int Hq, int Hkv, int d, int page_size, int num_pages,
+                                int max_pages_per_seq, int num_splits, void* dump_k, void* dump_v,
+                                size_t dump_elems, void* workspace, size_t workspace_bytes, void* stream) {
+  ea::DecodeArgs a;
+  size_t need = 0;
+  // the split kernel writes no output or lse; dump_k stands in for the
+  // output pointer that the shared checks require
+  if (ea_status st = decode_args(q, k_cache, v_cache, block_table, seq_lens, dump_k, nullptr, B, Hq, Hkv, d,
+                                 page_size, num_pages, max_pages_per_seq, 1.0f, num_splits, a, need);
+      st != EA_OK)
+    return st;
+  if (!dump_k || !dump_v) return fail(EA_ERR_INVALID, "dump buffers must be non-null");
+  const size_t want = (size_t)B * max_pages_per_seq * page_size * Hkv * d;
+  if (dump_elems < want) return fail(EA_ERR_WORKSPACE, "dump buffers need %zu elements, %zu given", want, dump_elems);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(EA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  ea::decode_bind_workspace(a, workspace);
+  a.o = nullptr;
+  a.lse = nullptr;
+  a.dump_k = (uint16_t*)dump_k;
+  a.dump_v = (uint16_t*)dump_v;
+  a.dump_t = max_pages_per_seq * page_size;
+  return hip_status(ea::launch_decode_gather_dump(a, (hipStream_t)stream), "decode gather dump launch");
 }
 
 size_t ea_decode_noalloc_max_bytes(void) { return ea::kDecodeScratchBytes; }

@@ -96,7 +96,10 @@ __device__ __forceinline__ int range_start(int w, int Tc, int W) {
   return (int)(((long long)w * Tc) / W);
 }
 
-template <bool PAGE16>
+// DUMP (test-only): every wave of a KV head's first column block also writes
+// the K and V rows it staged for each chunk, as gathered, to a.dump_k /
+// a.dump_v at (sequence, token, KV head).
+template <bool PAGE16, bool DUMP = false>
 __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(DecodeArgs a) {
   constexpr int D = kD;
   constexpr int TILE = kChunk * D;  // bf16 elements per K or V chunk
@@ -246,6 +249,22 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(DecodeArgs
         lds_store<i32x4>(vs + st_off[u], rv[u]);
       }
     };
+    // rk[u] / rv[u] hold chunk row 4 u + grp, columns 8 col .. 8 col + 7
+    auto dump = [&](int ci) {
+      if constexpr (DUMP) {
+        if (c_lo == 0) {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int t = t_begin + kChunk * ci + 4 * u + grp;
+            if (t < t_end) {
+              const size_t at = (((size_t)b * a.dump_t + t) * a.Hkv + hkv) * D + 8 * col;
+              *(i32x4*)(a.dump_k + at) = rk[u];
+              *(i32x4*)(a.dump_v + at) = rv[u];
+            }
+          }
+        }
+      }
+    };
 
     float m_run = kNegInf, l_run = 0.f;
     f32x4 oacc[D / 16];
@@ -263,6 +282,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(DecodeArgs
       gload_rows(row_index(ent0, slot0));
     }
     sstore();
+    dump(0);
     __builtin_amdgcn_s_waitcnt(0);
     for (int ci = 0; ci < nck; ++ci) {
       const int t0 = t_begin + kChunk * ci;
@@ -326,7 +346,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(DecodeArgs
                          __builtin_bit_cast(i32x2, hi)[0], __builtin_bit_cast(i32x2, hi)[1]};
         oacc[mt] = mfma16x16x32(__builtin_bit_cast(bf16x8, t), pb, oacc[mt]);
       }
-      if (ci + 1 < nck) sstore();
+      if (ci + 1 < nck) {
+        sstore();
+        dump(ci + 1);
+      }
     }
 
     // ---- this piece's normalised partial output and log-sum-exp
@@ -432,6 +455,18 @@ static hipError_t launch_p(const DecodeArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(a.B * a.Hq), dim3(kD), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_gather_dump(const DecodeArgs& a, hipStream_t s) {
+  if (a.num_ranges <= 0 || a.part_o == nullptr || a.plan == nullptr || a.dump_k == nullptr || a.dump_v == nullptr)
+    return hipErrorInvalidValue;
+  const dim3 grid(a.num_ranges, decode_head_groups(a.Hkv, a.group));
+  if (a.page_size % 16 == 0) {
+    hipLaunchKernelGGL((decode_split_kernel<true, true>), grid, dim3(64 * kWaves), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((decode_split_kernel<false, true>), grid, dim3(64 * kWaves), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -739,6 +739,32 @@ hipError_t launch_fwd_pp_stats(const FwdArgs& a, bool causal, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Test-only: work tile t of the dense per-tile launch (t = 8 j + XCD, the
+// dispatch order) as (sequence, head, row block), or -1s for a padding entry,
+// from the same pp_locate the kernels call. One wave per tile: pp_locate
+// takes its arguments as wave-uniform.
+template <bool CAUSAL>
+__global__ __launch_bounds__(64) void fwd_tile_order_kernel(FwdArgs a, int* out) {
+  const int t = blockIdx.x;
+  PpTile tile;
+  const bool ok = pp_locate<CAUSAL, false>(a, t & 7, t >> 3, tile);
+  if (threadIdx.x == 0) {
+    out[3 * t] = ok ? tile.seq : -1;
+    out[3 * t + 1] = ok ? tile.h : -1;
+    out[3 * t + 2] = ok ? tile.row_lo / kPpBlockM : -1;
+  }
+}
+
+hipError_t launch_fwd_tile_order(const FwdArgs& a, bool causal, int* out, hipStream_t s) {
+  const int grid = fwd_grid(a, false);
+  if (causal) {
+    hipLaunchKernelGGL((fwd_tile_order_kernel<true>), dim3(grid), dim3(64), 0, s, a, out);
+  } else {
+    hipLaunchKernelGGL((fwd_tile_order_kernel<false>), dim3(grid), dim3(64), 0, s, a, out);
+  }
+  return hipGetLastError();
+}
+
 // Persistent form with the K/V pipeline running on across tiles (pp_walk);
 // equal head dims only: the next tile's Q of (192, 128) does not fit beside
 // its stages in LDS.

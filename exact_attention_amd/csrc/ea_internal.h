@@ -47,6 +47,8 @@ hipError_t launch_fwd_pp(const FwdArgs& a, int d, int dv, bool causal, bool varl
 // writing per-wave live-step and lazy-rescale counts to a.stats (16 ints per
 // work tile); a.n_mb counts kPpBlockM-row blocks, a.persist_wgs is set
 hipError_t launch_fwd_pp_stats(const FwdArgs& a, bool causal, hipStream_t s);
+// test-only: (sequence, head, row block) of every dense work tile, 3 ints each
+hipError_t launch_fwd_tile_order(const FwdArgs& a, bool causal, int* out, hipStream_t s);
 
 // varlen batch order (heaviest sequence first): weights[b] and order[virtual] = actual
 hipError_t launch_lpt_order(const int* cu_q, const int* cu_k, int n, int causal, int block_m, int* weights,
@@ -121,8 +123,15 @@ struct DecodeArgs {
   int num_pages;     // pool size: page indices outside [0, num_pages) read as zeros
   int num_ranges;    // W: equal shares of the batch's chunks, one workgroup each
   float scale_log2;
+  // test-only gather dump: the K and V rows each chunk staged, by sequence and
+  // token, into dense [B, dump_t, Hkv, d] buffers (null otherwise)
+  uint16_t* dump_k;
+  uint16_t* dump_v;
+  int dump_t;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+// the split kernel alone, writing the gather dump as well (a.dump_* set)
+hipError_t launch_decode_gather_dump(const DecodeArgs& a, hipStream_t s);
 size_t decode_workspace_bytes(int B, int Hq, int d, int num_ranges);
 // workgroups along y: groups of 8 (KV head, 16-column block of its query heads) pairs
 int decode_head_groups(int Hkv, int group);

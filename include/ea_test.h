@@ -95,6 +95,38 @@ ea_status ea_test_stream_read(const void* buf, size_t bytes, int* out, int block
  */
 size_t ea_test_fwd_rescale_stats_len(int B, int Nq, int Hq);
 /*
+ * ea_test_fwd_tiles / ea_test_fwd_tile_order -- the work order of the dense
+ * bf16 forward ("FlashAttention4 close reading", section 3.3: the cache-aware
+ * hierarchical LPT traversal). ea_test_fwd_tiles returns the number of work
+ * tiles of the per-tile launch (0 for non-positive sizes);
+ * ea_test_fwd_tile_order writes, for every tile t in dispatch order (t = 8 j
+ * + XCD), out[3 t .. 3 t + 2] = (batch, head, 256-row block), or -1s for a
+ * padding entry, computed by the kernels' own tile-location code. out: device
+ * int32 array of at least 3 ea_test_fwd_tiles(B, Nq, Hq) elements
+ * (EA_ERR_WORKSPACE otherwise); EA_ERR_INVALID for a null out, non-positive
+ * sizes or causal not 0/1; EA_ERR_UNSUPPORTED for B * N >= 2^31.
+ */
+size_t ea_test_fwd_tiles(int B, int Nq, int Hq);
+ea_status ea_test_fwd_tile_order(int B, int Nq, int Nk, int Hq, int causal, int* out, size_t out_len, void* stream);
+/*
+ * ea_test_decode_gather -- the page-gather dump of the paged decode ("Faster,
+ * more flexible FlashAttention-4 for LLM inference", PR 1999/2104 sections:
+ * token t of sequence b lives in page block_table[b, t / page_size], slot
+ * t % page_size). Runs the decode's split kernel on the arguments of
+ * ea_attn_decode_paged (q, caches, block table, lengths, sizes, num_splits,
+ * workspace) and, besides its partials, writes every K and V row it gathers
+ * for a chunk to dump_k / dump_v, dense [B, max_pages_per_seq * page_size,
+ * Hkv, d] bf16 at (sequence, token, KV head), through the same loads the
+ * decode uses: tokens at or past a sequence's (clamped) length are not
+ * written; rows of page indices outside [0, num_pages) read as zeros.
+ * dump_elems: the capacity of each dump buffer in elements (EA_ERR_WORKSPACE
+ * when short); other errors as for ea_attn_decode_paged.
+ */
+ea_status ea_test_decode_gather(const void* q, const void* k_cache, const void* v_cache, const int* block_table,
+                                const int* seq_lens, int B, int Hq, int Hkv, int d, int page_size, int num_pages,
+                                int max_pages_per_seq, int num_splits, void* dump_k, void* dump_v,
+                                size_t dump_elems, void* workspace, size_t workspace_bytes, void* stream);
+/*
  * ea_test_wall_clock_khz -- *khz = the rate of the device's constant wall
  * clock counter (s_memrealtime) for HIP device `device`, in kHz. EA_ERR_INVALID
  * for a null khz, EA_ERR_HIP if the runtime cannot answer.

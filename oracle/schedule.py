@@ -50,6 +50,21 @@ def lpt_order(cu_q, cu_k, causal: bool, block_m: int, block_n: int) -> list[int]
     return sorted(range(n), key=lambda b: (-w[b], b))
 
 
+def hierarchical_tile_order(batches: int, heads: int, n_mblocks: int, section: int) -> list[tuple[int, int, int]]:
+    """Dense work tiles (batch, head, mblock) in the cache-aware hierarchical
+    LPT traversal [P2 §3.3]: batch outermost; within a batch the heads in
+    sections of ``section`` consecutive heads; within a section the row blocks
+    from the last (the longest causal main loop) down to the first; for each
+    row block the section's heads in turn."""
+    out = []
+    for b in range(batches):
+        for h0 in range(0, heads, section):
+            for mb in reversed(range(n_mblocks)):
+                for h in range(h0, min(h0 + section, heads)):
+                    out.append((b, h, mb))
+    return out
+
+
 def list_schedule_makespan(durations, processors: int) -> int:
     """Greedy dispatch in the given order: each task goes to the processor
     that becomes free first [P2 §3.3]. Returns the finishing time of the last

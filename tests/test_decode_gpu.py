@@ -276,3 +276,57 @@ def test_gather_exact_dominant_key(page_size):
                                        for h in range(Hq)]) for b in range(len(L))])
             assert np.array_equal(got, want), f"page {page_size} trial {trial} splits {ns}"
     log(f"  page {page_size}: {3 * 2 * len(L) * Hq} gathered rows bit-exact")
+
+
+def _host_gather(pg):
+    """Host indexing of the paged pool: token t of sequence b is slot t % page
+    of page block_table[b, t // page] ("Faster, more flexible FlashAttention-4
+    for LLM inference", PR 1999/2104 sections); a page index outside the pool
+    reads as zeros. Returns, per sequence, its rows [L_b, Hkv, d] as bf16 bits
+    for K and V."""
+    P, ps = pg.k_cache.shape[:2]
+    out = []
+    for b in range(pg.block_table.shape[0]):
+        L = int(min(max(int(pg.seq_lens[b]), 0), pg.block_table.shape[1] * ps))
+        ks, vs = [], []
+        for t in range(L):
+            page = int(pg.block_table[b, t // ps])
+            if 0 <= page < P:
+                ks.append(pg.k_cache[page, t % ps])
+                vs.append(pg.v_cache[page, t % ps])
+            else:
+                ks.append(np.zeros_like(pg.k_cache[0, 0]))
+                vs.append(np.zeros_like(pg.v_cache[0, 0]))
+        shape = (0,) + pg.k_cache.shape[2:]
+        out.append((np.array(ks).reshape(-1, *shape[1:]) if ks else np.zeros(shape, np.uint16),
+                    np.array(vs).reshape(-1, *shape[1:]) if vs else np.zeros(shape, np.uint16)))
+    return out
+
+
+@pytest.mark.parametrize("page_size", [16, 32, 5, 1])
+@pytest.mark.parametrize("num_splits", [0, 3])
+def test_page_gather_dump(page_size, num_splits):
+    """The page-gather dump: the K and V rows the decode's split kernel stages
+    for every chunk, through its own loads, equal host indexing of the pool
+    through the block table bit for bit -- permuted table, ragged and empty
+    sequences, NaN-poisoned tails, table entries outside the pool (rows of
+    zeros) -- and nothing is written past a sequence's length."""
+    import exact_attention_amd as ea
+    L = [1, 15, 16, 17, 100, 333, 0, 64]
+    pg = W.paged(len(L), 8, 2, 128, page_size, L, seed=270 + page_size, permute=True)
+    P = pg.k_cache.shape[0]
+    pg.block_table[5, 1] = P + 7     # past the pool
+    pg.block_table[4, 0] = -3        # negative
+    log(f"gather dump page {page_size} splits {num_splits}")
+    fill = 0x7FC1
+    dk, dv = ea.test_decode_gather(dev_bf16(pg.q), dev_bf16(pg.k_cache), dev_bf16(pg.v_cache),
+                                   torch.from_numpy(pg.block_table).cuda(), torch.from_numpy(pg.seq_lens).cuda(),
+                                   num_splits=num_splits, fill=fill)
+    torch.cuda.synchronize()
+    gk = dk.cpu().numpy().view(np.uint16)
+    gv = dv.cpu().numpy().view(np.uint16)
+    for b, (hk, hv) in enumerate(_host_gather(pg)):
+        n = hk.shape[0]
+        assert np.array_equal(gk[b, :n], hk), f"K rows of sequence {b}"
+        assert np.array_equal(gv[b, :n], hv), f"V rows of sequence {b}"
+        assert np.all(gk[b, n:] == fill) and np.all(gv[b, n:] == fill), f"rows past the end of sequence {b}"

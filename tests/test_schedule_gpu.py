@@ -1,5 +1,6 @@
-"""GPU tests of the varlen LPT batch order (ea_varlen_lpt_order) against the
-scheduling oracle, and of the forward walking sequences in that order."""
+"""GPU tests of the work order against the scheduling oracle: the varlen LPT
+batch order (ea_varlen_lpt_order), the forward walking sequences in that
+order, and the dense forward's own tile order (the hierarchical traversal)."""
 import numpy as np
 import pytest
 import torch
@@ -88,3 +89,26 @@ def test_order_entry_out_of_range_contributes_no_rows():
     o, _ = run_varlen_ordered(inp, 2, order)
     a, b = int(inp.cu_q[1]), int(inp.cu_q[2])
     assert np.array_equal(o[:a], o_all[:a]) and np.array_equal(o[b:], o_all[b:])
+
+
+@pytest.mark.parametrize("B,Hq,N,causal", [(4, 16, 8192, True), (2, 8, 1000, False), (1, 32, 700, True),
+                                           (3, 2, 600, True), (1, 3, 300, False)])
+def test_dense_order_is_hierarchical_lpt(B, Hq, N, causal):
+    """The dense forward's work tiles, in dispatch order and as the kernels
+    locate them on the device, follow the cache-aware hierarchical LPT
+    traversal of "FlashAttention4 close reading" section 3.3 with sections of
+    8 (batch, head) groups -- one per XCD, so each XCD's L2 serves one head at
+    a time -- laid end to end; with Hq a multiple of 8 that is the page's
+    batch-outermost loop with sections of 8 heads."""
+    import exact_attention_amd as ea
+    got = [tuple(int(x) for x in r) for r in ea.test_fwd_tile_order(B, N, N, Hq, causal).numpy()]
+    n_mb = -(-N // 256)
+    groups = B * Hq
+    padded = 8 * -(-groups // 8)
+    want = []
+    for _, g, mb in S.hierarchical_tile_order(1, padded, n_mb, 8):
+        want.append((g // Hq, g % Hq, mb) if g < groups else (-1, -1, -1))
+    log(f"tile order B={B} Hq={Hq} N={N} causal={causal}: {len(got)} tiles")
+    assert got == want
+    if Hq % 8 == 0:
+        assert [t for t in got if t[0] >= 0] == S.hierarchical_tile_order(B, Hq, n_mb, 8)

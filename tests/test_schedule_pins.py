@@ -81,3 +81,25 @@ def test_planted_mistake_is_caught():
     cu_k = [0, 64, 320, 512, 640]
     w = [S.seq_weight(64, L, False, 256, 64) for L in (64, 256, 192, 128)]
     assert sorted(range(4), key=lambda b: (w[b], b)) != [1, 2, 3, 0]
+
+
+def test_hierarchical_traversal_example():
+    # the page's printed traversal: batch 0, sections of two heads, row blocks
+    # from the last to the first, the section's heads for each row block
+    import json
+    import pathlib
+    fx = json.loads((pathlib.Path(__file__).parent / "golden" / "traversal_example.json").read_text())
+    want = [tuple(x) for x in fx["order_batch0"]]
+    assert S.hierarchical_tile_order(fx["batches"], fx["heads"], fx["mblocks"], fx["section"]) == want
+    # "then batch 1": with two batches the second one's tiles all follow
+    two = S.hierarchical_tile_order(2, 4, 4, 2)
+    assert two[:16] == want and all(b == 1 for b, _, _ in two[16:]) and len(two) == 32
+    # every (batch, head, mblock) exactly once, whatever the section size
+    for sec in (1, 3, 4, 8):
+        o = S.hierarchical_tile_order(3, 5, 7, sec)
+        assert sorted(o) == sorted((b, h, m) for b in range(3) for h in range(5) for m in range(7))
+        # within a batch and section, row blocks never increase
+        for b in range(3):
+            for h in range(5):
+                mbs = [m for (bb, hh, m) in o if bb == b and hh == h]
+                assert mbs == sorted(mbs, reverse=True)
