@@ -249,7 +249,7 @@ FP8_FORMATS = {"e4m3": 0, "e5m2": 1}
 def attn_fwd_mx8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = True, scale: float | None = None,
                  *, tuning: FwdTuning | None = None, want_lse: bool = True, fmt: str = "e4m3"):
     """MX fp8 forward. q8/k8/v8 [B,N,H,d] uint8 codes in ``fmt`` ("e4m3" or
-    "e5m2"); q_scale/k_scale [B,N,H,d/32] and v_scale [B,N/32,Hkv,d] uint8
+    "e5m2"); q_scale/k_scale [B,H,N,d/32] (head-major) and v_scale [B,N/32,Hkv,d] uint8
     e8m0. Returns (o bf16, lse)."""
     if fmt not in FP8_FORMATS:
         raise ValueError(f"fmt must be one of {sorted(FP8_FORMATS)}")
@@ -262,8 +262,8 @@ def attn_fwd_mx8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = True, sca
     _shape(v8, "v8", (B, N, Hkv, d))
     if d % 32 or N % 32:
         raise ValueError(f"N ({N}) and d ({d}) must be multiples of 32 (the MX block)")
-    _shape(q_scale, "q_scale", (B, N, Hq, d // 32))
-    _shape(k_scale, "k_scale", (B, N, Hkv, d // 32))
+    _shape(q_scale, "q_scale", (B, Hq, N, d // 32))
+    _shape(k_scale, "k_scale", (B, Hkv, N, d // 32))
     _shape(v_scale, "v_scale", (B, N // 32, Hkv, d))
     _on_gpu(*named)
     if scale is None:

@@ -125,7 +125,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mx8_kernel(Mx8Args a) {
         const i32x4 hi = *(const i32x4*)(qp + 64 * ks + 32 + 16 * hh);
         qf[ks] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
-      s4 = *(const uint32_t*)(a.qs + (((size_t)b * N + qi) * a.Hq + h) * 4);
+      s4 = *(const uint32_t*)(a.qs + (((size_t)b * a.Hq + h) * N + qi) * 4);
     } else {
       qf[0] = i32x8{};
       qf[1] = i32x8{};
@@ -137,10 +137,10 @@ __global__ __launch_bounds__(256, 2) void fwd_mx8_kernel(Mx8Args a) {
   // ---------------- K/V tiles (buffer loads, zero past the end) and scales
   const uint8_t* kg_base = a.k + ((size_t)b * N) * kstride + (size_t)hk * D;
   const uint8_t* vg_base = a.v + ((size_t)b * N) * kstride + (size_t)hk * D;
-  const uint8_t* ksc_base = a.ks + ((size_t)b * N * a.Hkv + hk) * 4;
+  const uint8_t* ksc_base = a.ks + ((size_t)b * a.Hkv + hk) * N * 4;
   const int nkb32 = N / 32;
   const uint8_t* vsc_base = a.vs + ((size_t)b * nkb32 * a.Hkv + hk) * D;
-  const __amdgpu_buffer_rsrc_t rs_ksc = make_rsrc(ksc_base, (uint32_t)((N - 1) * a.Hkv * 4 + 4));
+  const __amdgpu_buffer_rsrc_t rs_ksc = make_rsrc(ksc_base, (uint32_t)((N - 1) * 4 + 4));
   const __amdgpu_buffer_rsrc_t rs_vsc = make_rsrc(vsc_base, (uint32_t)((nkb32 - 1) * a.Hkv * D + D));
   uint32_t g_off[CPT];
   int s_off[CPT];
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mx8_kernel(Mx8Args a) {
     const int key0 = kb * BN + c;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
-      rks[t] = __builtin_amdgcn_raw_buffer_load_b32(rs_ksc, (key0 + 32 * t) * a.Hkv * 4, 0, 0);
+      rks[t] = __builtin_amdgcn_raw_buffer_load_b32(rs_ksc, (key0 + 32 * t) * 4, 0, 0);
     const int kb32 = kb * 2 + hh;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -391,7 +391,7 @@ __device__ __forceinline__ void mx8_sp_tile(const Mx8Args& a, const int xcd, con
         const i32x4 hi = *(const i32x4*)(qp + 64 * ks + 32 + 16 * hh);
         qf[ks] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
-      s4 = *(const uint32_t*)(a.qs + (((size_t)b * N + qi) * a.Hq + h) * 4);
+      s4 = *(const uint32_t*)(a.qs + (((size_t)b * a.Hq + h) * N + qi) * 4);
     } else {
       qf[0] = i32x8{};
       qf[1] = i32x8{};
@@ -427,15 +427,15 @@ __device__ __forceinline__ void mx8_sp_tile(const Mx8Args& a, const int xcd, con
 
   // ---------------- scales: K scale dwords of keys 64 t + c and 64 t + 32 + c,
   // V scale bytes of key block 2 t + hh, columns 32 dt + c (zero past the end)
-  const uint8_t* ksc_base = a.ks + ((size_t)b * N * a.Hkv + hk) * 4;
+  const uint8_t* ksc_base = a.ks + ((size_t)b * a.Hkv + hk) * N * 4;
   const int nkb32 = N / 32;
   const uint8_t* vsc_base = a.vs + ((size_t)b * nkb32 * a.Hkv + hk) * D;
-  const __amdgpu_buffer_rsrc_t rs_ksc = make_rsrc(ksc_base, (uint32_t)((N - 1) * a.Hkv * 4 + 4));
+  const __amdgpu_buffer_rsrc_t rs_ksc = make_rsrc(ksc_base, (uint32_t)((N - 1) * 4 + 4));
   const __amdgpu_buffer_rsrc_t rs_vsc = make_rsrc(vsc_base, (uint32_t)((nkb32 - 1) * a.Hkv * D + D));
   auto load_kscale = [&](int t, uint32_t (&dst)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < 2; ++u)
-      dst[u] = __builtin_amdgcn_raw_buffer_load_b32(rs_ksc, (t * BN + 32 * u + c) * a.Hkv * 4, 0, 0);
+      dst[u] = __builtin_amdgcn_raw_buffer_load_b32(rs_ksc, (t * BN + 32 * u + c) * 4, 0, 0);
   };
   auto load_vscale = [&](int t, uint32_t (&dst)[NDT]) __attribute__((always_inline)) {
 #pragma unroll
@@ -777,7 +777,7 @@ __device__ __forceinline__ void mx8_pp_tile(const Mx8Args& a, const int xcd, con
         const i32x4 hi = *(const i32x4*)(qp + 64 * ks + 32 + 16 * hh);
         qf[ks] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
-      s4 = *(const uint32_t*)(a.qs + (((size_t)b * N + qi) * a.Hq + h) * 4);
+      s4 = *(const uint32_t*)(a.qs + (((size_t)b * a.Hq + h) * N + qi) * 4);
     } else {
       qf[0] = i32x8{};
       qf[1] = i32x8{};
@@ -804,10 +804,10 @@ __device__ __forceinline__ void mx8_pp_tile(const Mx8Args& a, const int xcd, con
   }
   const uint32_t nrec_full = (uint32_t)uniform((BN - 1) * (int)kstride + D);
   const uint32_t nrec_last = (uint32_t)uniform(nkb > 0 ? (min(N - (nkb - 1) * BN, BN) - 1) * (int)kstride + D : 0);
-  const uint8_t* ksc_base = a.ks + ((size_t)b * N * a.Hkv + hk) * 4;
+  const uint8_t* ksc_base = a.ks + ((size_t)b * a.Hkv + hk) * N * 4;
   const int nkb32 = N / 32;
   const uint8_t* vsc_base = a.vs + ((size_t)b * nkb32 * a.Hkv + hk) * D;
-  const uint32_t ksc_off = (uint32_t)(lane * a.Hkv * 4);
+  const uint32_t ksc_off = (uint32_t)(lane * 4);
   const uint32_t vsc_off = (uint32_t)((lane >> 5) * a.Hkv * D + 4 * (lane & 31));
   auto dma_k = [&](EA_LDS uint8_t* stage, int t) __attribute__((always_inline)) {
     const uint32_t nrec = t < nkb - 1 ? nrec_full : (t == nkb - 1 ? nrec_last : 0u);
@@ -817,7 +817,7 @@ __device__ __forceinline__ void mx8_pp_tile(const Mx8Args& a, const int xcd, con
     if (w == 0) {
       const int keys = t < nkb ? min(N - t * BN, BN) : 0;
       const __amdgpu_buffer_rsrc_t rsc =
-          make_rsrc(ksc_base + (size_t)t * BN * a.Hkv * 4, keys > 0 ? (uint32_t)((keys - 1) * a.Hkv * 4 + 4) : 0u);
+          make_rsrc(ksc_base + (size_t)t * BN * 4, keys > 0 ? (uint32_t)((keys - 1) * 4 + 4) : 0u);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsc, (EA_LDS void*)(stage + TILE), 4, (int)ksc_off, 0, 0, 0);
     }
   };

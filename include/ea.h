@@ -199,8 +199,9 @@ ea_status ea_attn_fwd_varlen_ordered(const void* q, const void* k, const void* v
 /*
  * ea_attn_fwd_mx8 -- forward with MX-scaled FP8 (OCP e4m3) inputs.
  *   q8, k8, v8     [B, N, H*, d] e4m3 codes (uint8)
- *   q_scale, k_scale [B, N, H*, d/32] e8m0 scale bytes (2^(s-127)), one per 32
- *                  consecutive elements along d;
+ *   q_scale, k_scale [B, H*, N, d/32] e8m0 scale bytes (2^(s-127)), one per 32
+ *                  consecutive elements along d; head-major, so the scales of
+ *                  a tile of rows of one head are contiguous;
  *   v_scale        [B, N/32, Hkv, d] e8m0, one per 32 consecutive keys
  *                  (the contraction dimension of P V) -- "Low-precision
  *                  FlashAttention-4: end-to-end block-scaled attention for

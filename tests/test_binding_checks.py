@@ -83,7 +83,7 @@ def test_varlen_mismatches():
 
 def mx_args(B=1, N=64, Hq=2, Hkv=1, d=128):
     return (z((B, N, Hq, d), u8), z((B, N, Hkv, d), u8), z((B, N, Hkv, d), u8),
-            z((B, N, Hq, d // 32), u8), z((B, N, Hkv, d // 32), u8), z((B, N // 32, Hkv, d), u8))
+            z((B, Hq, N, d // 32), u8), z((B, Hkv, N, d // 32), u8), z((B, N // 32, Hkv, d), u8))
 
 
 def test_mx8_consistent_shapes_only_fail_on_device():
@@ -91,8 +91,8 @@ def test_mx8_consistent_shapes_only_fail_on_device():
 
 
 @pytest.mark.parametrize("i,shape,name", [
-    (1, (1, 32, 1, 128), "k8"), (2, (1, 32, 1, 128), "v8"), (3, (1, 64, 1, 4), "q_scale"),
-    (4, (1, 64, 1, 8), "k_scale"), (5, (1, 64, 1, 128), "v_scale")])
+    (1, (1, 32, 1, 128), "k8"), (2, (1, 32, 1, 128), "v8"), (3, (1, 1, 64, 8), "q_scale"),
+    (4, (1, 64, 1, 4), "k_scale"), (5, (1, 64, 1, 128), "v_scale")])
 def test_mx8_mismatch(i, shape, name):
     a = list(mx_args())
     a[i] = z(shape, u8)

@@ -65,7 +65,7 @@ def test_ea_attn_fwd_mx8_plain():
     import exact_attention_amd as ea
     lib = ea.lib()
     m = W.mx8(1, 512, 2, 128, True, seed=820)
-    t = [torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in (m.q8, m.k8, m.v8, m.q_scale, m.k_scale,
+    t = [torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in (m.q8, m.k8, m.v8, m.q_scale_dev, m.k_scale_dev,
                                                                       m.v_scale)]
     o = torch.empty((1, 512, 2, 128), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((1, 2, 512), dtype=torch.float32, device="cuda")

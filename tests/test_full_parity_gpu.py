@@ -134,7 +134,7 @@ def test_fp8_prefill_every_slice():
     m = W.fp8_prefill()
     log(f"full parity: MX fp8 prefill shape={m.q8.shape}")
     t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()  # noqa: E731
-    o, lse = ea.attn_fwd_mx8(t(m.q8), t(m.k8), t(m.v8), t(m.q_scale), t(m.k_scale), t(m.v_scale), m.causal,
+    o, lse = ea.attn_fwd_mx8(t(m.q8), t(m.k8), t(m.v8), t(m.q_scale_dev), t(m.k_scale_dev), t(m.v_scale), m.causal,
                              m.scale, fmt=m.fmt)
     torch.cuda.synchronize()
     o, lse = f64(host_bits(o)), lse.cpu().numpy().astype(np.float64)

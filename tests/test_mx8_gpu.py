@@ -29,7 +29,7 @@ KERNELS = [1, 2, 3, 4]
 def run_mx8(m, kernel=0):
     import exact_attention_amd as ea
     t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
-    o, lse = ea.attn_fwd_mx8(t(m.q8), t(m.k8), t(m.v8), t(m.q_scale), t(m.k_scale), t(m.v_scale),
+    o, lse = ea.attn_fwd_mx8(t(m.q8), t(m.k8), t(m.v8), t(m.q_scale_dev), t(m.k_scale_dev), t(m.v_scale),
                              m.causal, m.scale, tuning=ea.tuning(kernel=kernel), fmt=m.fmt)
     torch.cuda.synchronize()
     return f64(host_bits(o)), lse.cpu().numpy().astype(np.float64)

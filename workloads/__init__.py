@@ -455,7 +455,9 @@ class MX8:
     """MX fp8 inputs (OCP e4m3 codes + e8m0 scales).
 
     q8/k8/v8 [B,N,H,d] uint8; q_scale/k_scale [B,N,H,d/32] (blocks along d);
-    v_scale [B,N/32,H,d] (blocks along the sequence)."""
+    v_scale [B,N/32,H,d] (blocks along the sequence). The library takes the
+    Q and K scales head-major, [B,H,N,d/32]: ``q_scale_dev`` / ``k_scale_dev``
+    (the same bytes, transposed)."""
     q8: np.ndarray
     k8: np.ndarray
     v8: np.ndarray
@@ -465,6 +467,14 @@ class MX8:
     causal: bool
     scale: float
     fmt: str = "e4m3"    # element format of q8 / k8 / v8
+
+    @property
+    def q_scale_dev(self) -> np.ndarray:
+        return np.ascontiguousarray(self.q_scale.transpose(0, 2, 1, 3))
+
+    @property
+    def k_scale_dev(self) -> np.ndarray:
+        return np.ascontiguousarray(self.k_scale.transpose(0, 2, 1, 3))
 
 
 def mx8(B: int, N: int, H: int, d: int, causal: bool, seed: int, scale: float | None = None,
