@@ -22,7 +22,9 @@ def host_bits(t: torch.Tensor) -> np.ndarray:
 
 
 def f64(bits: np.ndarray) -> np.ndarray:
-    return (np.asarray(bits).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    # NaN bit patterns (poisoned rows outside the sequences) stay NaN
+    with np.errstate(invalid="ignore"):
+        return (np.asarray(bits).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
 def assert_o_close(got, ref, what="o", atol=O_ATOL, rtol=O_RTOL):
@@ -41,7 +43,8 @@ def assert_lse_close(got, ref, what="lse", atol=LSE_ATOL):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     both_inf = np.isneginf(got) & np.isneginf(ref)
-    d = np.where(both_inf, 0.0, np.abs(got - ref))
+    with np.errstate(invalid="ignore"):  # -inf - -inf where both are -inf: masked out below
+        d = np.where(both_inf, 0.0, np.abs(got - ref))
     worst = float(np.nanmax(d)) if d.size else 0.0
     assert not np.isnan(d).any() and worst <= atol, f"{what}: max |err| {worst:.3e} > {atol}"
     return worst
