@@ -255,6 +255,18 @@ class ClockSampler:
                           "clock's upper limit while the cores run slower (see clock.in_kernel)"}
 
 
+def device_market_name():
+    """The GPU's marketing name from the driver (amdsmi), when torch reports none."""
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        h = amdsmi.amdsmi_get_processor_handles()[0]
+        name = amdsmi.amdsmi_get_gpu_asic_info(h).get("market_name")
+        return str(name) if name else None
+    except Exception:  # noqa: BLE001 -- no driver metrics: the field stays null
+        return None
+
+
 def rocm_version():
     try:
         with open("/opt/rocm/.info/version") as f:
@@ -767,7 +779,8 @@ def main():
                 "what": "register-operand bf16 MFMA loop on all CUs (ea_test_mfma_loop), this GPU",
                 "unit": "TFLOP/s", "value": r, "frac": (out["roofline"]["achieved"] / r) if r else None}
     props = torch.cuda.get_device_properties(dev)
-    cfg["device"] = props.name
+    cfg["device"] = device_market_name() or props.name
+    cfg["device_runtime_name"] = props.name
     cfg["gcn_arch"] = getattr(props, "gcnArchName", None)
     cfg["cus"] = props.multi_processor_count
     cfg["versions"] = rocm_version()

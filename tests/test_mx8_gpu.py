@@ -60,7 +60,10 @@ def check_normwise(o, ro, lse, rl, what):
 @pytest.mark.parametrize("shape", [
     (1, 256, 2, 2, True), (1, 256, 2, 2, False),
     (2, 320, 4, 2, True),      # N % 64 != 0 (ragged tail tile), GQA 2:1
-    (1, 96, 1, 1, False), (1, 1024, 2, 1, True)])
+    (1, 96, 1, 1, False), (1, 1024, 2, 1, True),
+    (1, 32, 1, 1, True),       # a single half tile
+    (3, 64, 8, 2, True),       # GQA 4:1, one tile, several batches
+    (1, 2080, 2, 2, False)])   # last 256-row block holds 32 rows
 @pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
 def test_mx8_small(shape, kernel, fmt):
