@@ -866,14 +866,12 @@ __device__ __forceinline__ void mx8_pp_tile(const Mx8Args& a, const int xcd, con
   i32x8 pb = i32x8{};  // P^T (e4m3) of the last softmax phase
   const float sl = a.scale_log2;
   const float tau = a.tau;
+  const float thr = __builtin_amdgcn_exp2f(tau);  // 2^tau
 
-  float m_new = kNegInf;  // the row max the MFMA part found for the next softmax phase
-
-  // ---- MFMA part of step s: S_s = K_s Q^T into s0, s1, then O += V_{s-1}
-  // P_{s-1} (pb), and under those four products the masking and the row max
-  // of S_s (vector work that only needs S_s, done here so the
-  // softmax phase holds only what needs the new max). For a tile this wave
-  // skips, the softmax phase left P = 0; stages past the end hold zeros from
+  // ---- MFMA part of step s: S_s = K_s Q^T into s0, s1, the masking of S_s
+  // (diagonal and ragged tiles), then O += V_{s-1} P_{s-1} (pb). Vector work
+  // placed under the four P V products measured slower than the same work
+  // in the softmax phase. For a tile this wave skips, the softmax phase left P = 0; stages past the end hold zeros from
   // the DMA (scale code 0 is 2^-127, finite), and the V stage read at the
   // first step is zeroed, so the extra products add exact zeros.
   auto mfma_part = [&](const EA_LDS uint8_t* kst, const EA_LDS uint8_t* vst, int s) __attribute__((always_inline)) {
@@ -944,24 +942,7 @@ __device__ __forceinline__ void mx8_pp_tile(const Mx8Args& a, const int xcd, con
     }
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) oacc[dt] = mfma_mx8<FMT, kFmtE4M3>(va[dt], pb, oacc[dt], vsc[dt], kScaleOne);
-    // row max over this lane's 32 keys in two chains of three-input max,
-    // then over the partner lane's 32
-    float mx0 = kNegInf, mx1 = kNegInf;
-#pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-      mx0 = __builtin_fmaxf(__builtin_fmaxf(mx0, s0[i]), s1[i]);
-      mx1 = __builtin_fmaxf(__builtin_fmaxf(mx1, s0[i + 1]), s1[i + 1]);
-    }
-    const float mx = max_with_partner32(__builtin_fmaxf(mx0, mx1));
-    m_new = __builtin_fmaxf(m_run, mx * sl);
-    // a product, then a share of the vector work, four times
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     __builtin_amdgcn_s_setprio(0);
     // the products are issued here, before the barrier (the compiler would
     // otherwise sink them into the softmax phase, next to their first use)
@@ -969,43 +950,63 @@ __device__ __forceinline__ void mx8_pp_tile(const Mx8Args& a, const int xcd, con
     for (int dt = 0; dt < NDT; ++dt) keep(oacc[dt]);
     keep(s0);
     keep(s1);
-    keep(m_new);
   };
 
-  // ---- softmax phase of step s: P_s (e4m3, in pb) from S_s and the row max
-  // m_new of the MFMA part; lazy rescale of O and l with threshold tau (log2)
+  // ---- softmax phase of step s: P_s (e4m3, in pb) from S_s, with the lazy
+  // rescale of O and l (threshold tau, log2) decided without the row max in
+  // the common case. P is first formed against the running max m. If every
+  // lane's sum of its 32 new P values is at most 2^tau, no P exceeds 2^tau, so
+  // no row max exceeds m + tau and the rule keeps m: the P already formed are
+  // the ones it forms. Otherwise (and while a row has no max yet) the row max
+  // is taken from S_s, which is still intact, and the rule applied as
+  // written, forming P again if m moved.
+  auto p_half = [&](const f32x16& sv, int w0, float neg_m) __attribute__((always_inline)) -> float {
+    // P over one 32-key half (this lane's 16 scores): fp32 sum, and P^T as
+    // e4m3 (scale 1) in four dwords of pb: bytes 0..15 key tile 0, 16..31 tile 1
+    float ls = 0.f;
+#pragma unroll
+    for (int wd = 0; wd < 4; ++wd) {
+      float p[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        p[k] = exp2_hw(__builtin_fmaf(sv[4 * wd + k], sl, neg_m));
+        ls += p[k];
+      }
+      pb[w0 + wd] = pack_fp8x4(p[0], p[1], p[2], p[3]);
+    }
+    return ls;
+  };
   auto valu_part = [&](bool act) __attribute__((always_inline)) {
     if (!act) {
       pb = i32x8{};
       return;
     }
-    if (__ballot(m_new > m_run + tau)) {
-      const float alpha = (m_run == kNegInf) ? 0.f : exp2_hw(m_run - m_new);
-      l_run *= alpha;
+    const float ls0 = p_half(s0, 0, (m_run == kNegInf) ? 0.f : -m_run);
+    float lsum = ls0 + p_half(s1, 4, (m_run == kNegInf) ? 0.f : -m_run);
+    if (__ballot(!(lsum <= thr) || m_run == kNegInf)) {
+      // row max over this lane's 32 keys in two chains of three-input max,
+      // then over the partner lane's 32
+      float mx0 = kNegInf, mx1 = kNegInf;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
-      m_run = m_new;
-    }
-    const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
+      for (int i = 0; i < 16; i += 2) {
+        mx0 = __builtin_fmaxf(__builtin_fmaxf(mx0, s0[i]), s1[i]);
+        mx1 = __builtin_fmaxf(__builtin_fmaxf(mx1, s0[i + 1]), s1[i + 1]);
+      }
+      const float mx = max_with_partner32(__builtin_fmaxf(mx0, mx1));
+      const float m_new = __builtin_fmaxf(m_run, mx * sl);
+      if (__ballot(m_new > m_run + tau)) {
+        const float alpha = (m_run == kNegInf) ? 0.f : exp2_hw(m_run - m_new);
+        l_run *= alpha;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      s0[i] = exp2_hw(__builtin_fmaf(s0[i], sl, neg_m));
-      s1[i] = exp2_hw(__builtin_fmaf(s1[i], sl, neg_m));
+        for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+        m_run = m_new;
+        const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
+        const float l0 = p_half(s0, 0, neg_m);
+        lsum = l0 + p_half(s1, 4, neg_m);
+      }
     }
-    // the row sum over P in fp32, before its e4m3 rounding
-    float ls0 = 0.f, ls1 = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      ls0 += s0[i];
-      ls1 += s1[i];
-    }
-    l_run += ls0 + ls1;
-    // P^T -> e4m3 (scale 1): bytes 0..15 key tile 0, 16..31 key tile 1
-#pragma unroll
-    for (int wd = 0; wd < 4; ++wd) {
-      pb[wd] = pack_fp8x4(s0[4 * wd], s0[4 * wd + 1], s0[4 * wd + 2], s0[4 * wd + 3]);
-      pb[4 + wd] = pack_fp8x4(s1[4 * wd], s1[4 * wd + 1], s1[4 * wd + 2], s1[4 * wd + 3]);
-    }
+    // the row sum in fp32, before the e4m3 rounding of P
+    l_run += lsum;
   };
 
   // a tile is fully masked for this wave (wave-uniform) if its first key lies

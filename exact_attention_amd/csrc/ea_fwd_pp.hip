@@ -233,8 +233,8 @@ struct PpCore {
     __builtin_amdgcn_s_setprio(0);
   }
 
-  // ---- VALU part of step s of a tile: softmax of S_s into P_s (bf16,
-  // computed in place over S), m, l, rescale. act: the tile holds keys this
+  // ---- VALU part of step s of a tile: softmax of S_s into P_s (bf16, in
+  // pb), m, l, rescale. act: the tile holds keys this
   // wave sees. qi: this lane's query row; wave_first_q: the wave's first row;
   // lk: keys of the sequence; off = lk - lq (bottom-right causal alignment).
   __device__ __forceinline__ void valu_part(int s, bool act, int qi, int wave_first_q, int lk, int off, float sl,
@@ -258,38 +258,56 @@ struct PpCore {
         s1[i] = (ko + 32 < rel) ? s1[i] : kNegInf;
       }
     }
-    float mx = kNegInf;
-#pragma unroll
-    // max(max(acc, a), b) per pair of scores folds into one three-input max
-    for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s0[i]), s1[i]);
-    mx = max_with_partner32(mx);
-    const float m_new = __builtin_fmaxf(m_run, mx * sl);
+    // Lazy rescale (threshold tau, log2) decided without the row max in the
+    // common case: P is first formed against the running max m. If every
+    // lane's sum of its 32 new P values is at most 2^tau, no P exceeds 2^tau,
+    // so no row max exceeds m + tau and the rule keeps m: the P already
+    // formed are the ones it forms. Otherwise (and while a row has no max
+    // yet) the row max is taken from S, still intact, and the rule applied as
+    // written, forming P again if m moved.
     if constexpr (STATS) ++n_live;
-    if (__ballot(m_new > m_run + tau)) {
-      if constexpr (STATS) ++n_rescale;
-      const float alpha = (m_run == kNegInf) ? 0.f : exp2_hw(m_run - m_new);
-      l_run *= alpha;
+    float lsum = form_p((m_run == kNegInf) ? 0.f : -m_run, sl);
+    if (__ballot(!(lsum <= __builtin_amdgcn_exp2f(tau)) || m_run == kNegInf)) {
+      float mx = kNegInf;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
-      m_run = m_new;
-    }
-    const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
+      // max(max(acc, a), b) per pair of scores folds into one three-input max
+      for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s0[i]), s1[i]);
+      mx = max_with_partner32(mx);
+      const float m_new = __builtin_fmaxf(m_run, mx * sl);
+      if (__ballot(m_new > m_run + tau)) {
+        if constexpr (STATS) ++n_rescale;
+        const float alpha = (m_run == kNegInf) ? 0.f : exp2_hw(m_run - m_new);
+        l_run *= alpha;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      s0[i] = pp_exp2<EXPMODE>(__builtin_fmaf(s0[i], sl, neg_m), i);
-      s1[i] = pp_exp2<EXPMODE>(__builtin_fmaf(s1[i], sl, neg_m), i);
+        for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+        m_run = m_new;
+        lsum = form_p((m_run == kNegInf) ? 0.f : -m_run, sl);
+      }
     }
-    float ls0 = 0.f, ls1 = 0.f;
+    // the row sum in fp32, before the bf16 rounding of P
+    l_run += lsum;
+  }
+
+  // P = 2^(S sl + neg_m) over this lane's 32 scores (S is left intact): P^T
+  // as bf16 MFMA operands in pb (keys 0..15 of s0, 16..31, then s1), and the
+  // fp32 sum of the 32 values
+  __device__ __forceinline__ float form_p(float neg_m, float sl) {
+    float ls = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      ls0 += s0[i];
-      ls1 += s1[i];
+    for (int st = 0; st < 4; ++st) {
+      const f32x16& sv = st < 2 ? s0 : s1;
+      const int i0 = 8 * (st & 1);
+      float p[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        p[k] = pp_exp2<EXPMODE>(__builtin_fmaf(sv[i0 + k], sl, neg_m), i0 + k);
+        ls += p[k];
+      }
+      const i32x4 t = {(int)pack_bf16x2(p[0], p[1]), (int)pack_bf16x2(p[2], p[3]), (int)pack_bf16x2(p[4], p[5]),
+                       (int)pack_bf16x2(p[6], p[7])};
+      pb[st] = __builtin_bit_cast(bf16x8, t);
     }
-    l_run += ls0 + ls1;
-    pb[0] = pack_p8<0>(s0);
-    pb[1] = pack_p8<8>(s0);
-    pb[2] = pack_p8<0>(s1);
-    pb[3] = pack_p8<8>(s1);
+    return ls;
   }
 
   // ---- end of a tile: O = acc / l (bf16), lse = ln2 * (m + log2 l)
