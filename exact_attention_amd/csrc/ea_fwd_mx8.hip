@@ -867,6 +867,7 @@ __device__ __forceinline__ void mx8_pp_tile(const Mx8Args& a, const int xcd, con
   const float sl = a.scale_log2;
   const float tau = a.tau;
   const float thr = __builtin_amdgcn_exp2f(tau);  // 2^tau
+  float neg_m_run = 0.f, thr_run = -1.f;
 
   // ---- MFMA part of step s: S_s = K_s Q^T into s0, s1, the masking of S_s
   // (diagonal and ragged tiles), then O += V_{s-1} P_{s-1} (pb). Vector work
@@ -886,7 +887,9 @@ __device__ __forceinline__ void mx8_pp_tile(const Mx8Args& a, const int xcd, con
     for (int dt = 0; dt < NDT; ++dt) v_off[dt] = launder(v_off[dt]);
     ksc_lds = launder(ksc_lds);
     vsc_lds = launder(vsc_lds);
-    __builtin_amdgcn_s_setprio(1);
+    // (at normal wave priority: here the softmax phase, not this part, sets
+    // the step's length, and raising this part's priority, as the bf16
+    // kernel does, measured 0.7% slower)
     // K scale of (key row, d block 2 k2 + hh) is byte 2 k2 + hh of its
     // dword: after a shift by 8 hh it is byte 2 k2, which the MFMA selects
     const int ksh0 = (int)(lds_load<uint32_t>(kst + ksc_lds) >> (8 * hh));
@@ -943,7 +946,6 @@ __device__ __forceinline__ void mx8_pp_tile(const Mx8Args& a, const int xcd, con
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) oacc[dt] = mfma_mx8<FMT, kFmtE4M3>(va[dt], pb, oacc[dt], vsc[dt], kScaleOne);
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    __builtin_amdgcn_s_setprio(0);
     // the products are issued here, before the barrier (the compiler would
     // otherwise sink them into the softmax phase, next to their first use)
 #pragma unroll
@@ -961,29 +963,31 @@ __device__ __forceinline__ void mx8_pp_tile(const Mx8Args& a, const int xcd, con
   // is taken from S_s, which is still intact, and the rule applied as
   // written, forming P again if m moved.
   auto p_half = [&](const f32x16& sv, int w0, float neg_m) __attribute__((always_inline)) -> float {
-    // P over one 32-key half (this lane's 16 scores): fp32 sum, and P^T as
-    // e4m3 (scale 1) in four dwords of pb: bytes 0..15 key tile 0, 16..31 tile 1
-    float ls = 0.f;
+    // P over one 32-key half (this lane's 16 scores): fp32 sum (four partial
+    // sums, so the adds do not form one dependent chain), and P^T as e4m3
+    // (scale 1) in four dwords of pb: bytes 0..15 key tile 0, 16..31 tile 1
+    float ls[4];
 #pragma unroll
     for (int wd = 0; wd < 4; ++wd) {
       float p[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         p[k] = exp2_hw(__builtin_fmaf(sv[4 * wd + k], sl, neg_m));
-        ls += p[k];
+        ls[k] = wd == 0 ? p[k] : ls[k] + p[k];
       }
       pb[w0 + wd] = pack_fp8x4(p[0], p[1], p[2], p[3]);
     }
-    return ls;
+    return (ls[0] + ls[1]) + (ls[2] + ls[3]);
   };
   auto valu_part = [&](bool act) __attribute__((always_inline)) {
     if (!act) {
       pb = i32x8{};
       return;
     }
-    const float ls0 = p_half(s0, 0, (m_run == kNegInf) ? 0.f : -m_run);
-    float lsum = ls0 + p_half(s1, 4, (m_run == kNegInf) ? 0.f : -m_run);
-    if (__ballot(!(lsum <= thr) || m_run == kNegInf)) {
+    const float ls0 = p_half(s0, 0, neg_m_run);
+    float lsum = ls0 + p_half(s1, 4, neg_m_run);
+    // thr_run is 2^tau, or -1 while the row has no max (the test then fails)
+    if (__ballot(!(lsum <= thr_run))) {
       // row max over this lane's 32 keys in two chains of three-input max,
       // then over the partner lane's 32
       float mx0 = kNegInf, mx1 = kNegInf;
@@ -1000,9 +1004,10 @@ __device__ __forceinline__ void mx8_pp_tile(const Mx8Args& a, const int xcd, con
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
         m_run = m_new;
-        const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
-        const float l0 = p_half(s0, 0, neg_m);
-        lsum = l0 + p_half(s1, 4, neg_m);
+        neg_m_run = (m_run == kNegInf) ? 0.f : -m_run;
+        thr_run = (m_run == kNegInf) ? -1.f : thr;
+        const float l0 = p_half(s0, 0, neg_m_run);
+        lsum = l0 + p_half(s1, 4, neg_m_run);
       }
     }
     // the row sum in fp32, before the e4m3 rounding of P

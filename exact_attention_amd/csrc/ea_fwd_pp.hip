@@ -134,6 +134,11 @@ struct PpCore {
   f32x16 s0, s1;
   bf16x8 pb[4];
   float m_run, l_run;
+  // -m (0 while the row has no max) and the lazy-rescale test's bound on the
+  // sum of a step's P: 2^tau, or -1 while the row has no max (the test then
+  // fails); both change only when m does
+  float neg_m_run, thr_run;
+  float thr_tau = 1.f;  // 2^tau
   int n_live = 0, n_rescale = 0;  // STATS only
 
   __device__ __forceinline__ void init() {
@@ -161,9 +166,13 @@ struct PpCore {
   __device__ __forceinline__ void reset() {
     m_run = kNegInf;
     l_run = 0.f;
+    neg_m_run = 0.f;
+    thr_run = -1.f;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16{};
   }
+  __device__ __forceinline__ void set_tau(float tau) { thr_tau = __builtin_amdgcn_exp2f(tau); }
+
   // first query row of this wave in a tile starting at row_lo
   __device__ __forceinline__ int wave_row(int row_lo) const { return row_lo + 64 * (w & 3) + 32 * grp; }
 
@@ -266,8 +275,8 @@ struct PpCore {
     // yet) the row max is taken from S, still intact, and the rule applied as
     // written, forming P again if m moved.
     if constexpr (STATS) ++n_live;
-    float lsum = form_p((m_run == kNegInf) ? 0.f : -m_run, sl);
-    if (__ballot(!(lsum <= __builtin_amdgcn_exp2f(tau)) || m_run == kNegInf)) {
+    float lsum = form_p(neg_m_run, sl);
+    if (__ballot(!(lsum <= thr_run))) {
       float mx = kNegInf;
 #pragma unroll
       // max(max(acc, a), b) per pair of scores folds into one three-input max
@@ -281,7 +290,9 @@ struct PpCore {
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
         m_run = m_new;
-        lsum = form_p((m_run == kNegInf) ? 0.f : -m_run, sl);
+        neg_m_run = (m_run == kNegInf) ? 0.f : -m_run;
+        thr_run = (m_run == kNegInf) ? -1.f : thr_tau;
+        lsum = form_p(neg_m_run, sl);
       }
     }
     // the row sum in fp32, before the bf16 rounding of P
@@ -301,7 +312,7 @@ struct PpCore {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         p[k] = pp_exp2<EXPMODE>(__builtin_fmaf(sv[i0 + k], sl, neg_m), i0 + k);
-        ls += p[k];
+        ls = (st == 0 && k == 0) ? p[k] : ls + p[k];
       }
       const i32x4 t = {(int)pack_bf16x2(p[0], p[1]), (int)pack_bf16x2(p[2], p[3]), (int)pack_bf16x2(p[4], p[5]),
                        (int)pack_bf16x2(p[6], p[7])};
@@ -381,6 +392,7 @@ __device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) 
 
   PpCore<D, DV, CAUSAL, EXPMODE, STATS> cr;
   cr.init();
+  cr.set_tau(a.tau);
   const int tid = threadIdx.x;
   const int lane = cr.lane, w = cr.w, grp = cr.grp;
   const int wrow = cr.wave_row(t.row_lo);  // wave's first query row
@@ -550,6 +562,7 @@ __device__ __forceinline__ void pp_walk(const FwdArgs& a) {
 
   PpCore<D, D, CAUSAL, EXPMODE> cr;
   cr.init();
+  cr.set_tau(a.tau);
   const int tid = threadIdx.x;
   const int lane = cr.lane, w = cr.w, grp = cr.grp;
   const size_t kstride = (size_t)a.Hkv * D, qstride = (size_t)a.Hq * D;
