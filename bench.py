@@ -168,6 +168,38 @@ def mfma_loop_rate(torch, ea, dev, reps=5):
     return flops / (float(np.median(ts)) * 1e-3) / 1e12
 
 
+def mfma_loop_data_rate(torch, ea, dev, fmt, reps=5):
+    """TFLOP/s of the random-operand calibration loop (ea_test_mfma_loop_data:
+    fmt 0 bf16 32x32x16, fmt 1 MX e4m3 32x32x64; every MFMA takes new operands
+    drawn N(0,1) like the workloads', so the matrix cores toggle as in the
+    attention products), 8 waves per workgroup, 1024 workgroups, median of
+    reps launches, or None."""
+    blocks = 1024
+    iters = 4000 if fmt == 0 else 1000
+    nbytes = ea.lib().ea_test_mfma_loop_data_bytes(fmt)
+    g = torch.Generator().manual_seed(11 + fmt)
+    if fmt == 0:
+        ops = torch.randn(nbytes // 2, generator=g).to(torch.bfloat16).view(torch.uint8).to(dev)
+    else:
+        ops = torch.randn(nbytes, generator=g).to(torch.float8_e4m3fn).view(torch.uint8).to(dev)
+    out = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
+    s = torch.cuda.current_stream(dev)
+    ts = []
+    for i in range(reps + 1):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        if ea.lib().ea_test_mfma_loop_data(ea._ptr(ops), ops.numel(), ea._ptr(out), blocks, iters, fmt,
+                                           s.cuda_stream) != 0:
+            return None
+        e1.record(s)
+        torch.cuda.synchronize()
+        if i:
+            ts.append(e0.elapsed_time(e1))
+    flops = blocks * 8.0 * iters * 16 * (32768 if fmt == 0 else 131072)
+    return flops / (float(np.median(ts)) * 1e-3) / 1e12
+
+
 def stream_read_rate(torch, ea, dev, reps=5):
     """GB/s of the library's streaming-read calibration (ea_test_stream_read:
     4 GiB read once by 8192 workgroups of 256 threads, 16 loads of 16 B in
@@ -776,6 +808,14 @@ def main():
             out["roofline"]["mfma_loop"] = {
                 "what": "register-operand bf16 MFMA loop on all CUs (ea_test_mfma_loop), this GPU",
                 "unit": "TFLOP/s", "value": r, "frac": (out["roofline"]["achieved"] / r) if r else None}
+        for key, fmt, dt_name in (("roofline", 0, "bf16"), ("roofline_fp8", 1, "MX e4m3")):
+            if key in out:
+                r = mfma_loop_data_rate(torch, ea, dev, fmt)
+                out[key]["mfma_loop_random"] = {
+                    "what": f"{dt_name} MFMA loop on all CUs with new N(0,1) operands for every MFMA "
+                            "(ea_test_mfma_loop_data): the matrix-core rate under this GPU's power limit on "
+                            "data like the workload's", "unit": "TFLOP/s", "value": r,
+                    "frac": (out[key]["achieved"] / r) if r else None}
     props = torch.cuda.get_device_properties(dev)
     cfg["device"] = device_market_name() or props.name
     cfg["device_runtime_name"] = props.name

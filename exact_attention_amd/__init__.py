@@ -62,6 +62,8 @@ _SIGNATURES = {
     "ea_attn_decode_paged_noalloc": ([_c_void_p] * 7 + [_c_int] * 7 + [_c_float, _c_int, _c_void_p], _c_int),
     "ea_test_exp2": ([_c_void_p, _c_void_p, _c_int, _c_int, _c_void_p], _c_int),
     "ea_test_mfma_loop": ([_c_void_p, _c_int, _c_int, _c_void_p], _c_int),
+    "ea_test_mfma_loop_data_bytes": ([_c_int], _c_size_t),
+    "ea_test_mfma_loop_data": ([_c_void_p, _c_size_t, _c_void_p, _c_int, _c_int, _c_int, _c_void_p], _c_int),
     "ea_test_stream_read": ([_c_void_p, _c_size_t, _c_void_p, _c_int, _c_void_p], _c_int),
     "ea_test_pair_probe": ([_c_void_p, _c_int, _c_int, _c_int, ctypes.c_longlong, _c_void_p], _c_int),
     "ea_test_fwd_rescale_stats_len": ([_c_int] * 3, _c_size_t),

@@ -39,6 +39,57 @@ __global__ __launch_bounds__(512) void mfma_loop_kernel(float* out, int iters) {
   out[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// The same loop with operands that change from one MFMA to the next: each
+// lane holds kDataSets (A, B) operand pairs read once from a caller buffer
+// (for instance random N(0,1) values, like the attention workloads'), and
+// consecutive MFMAs take consecutive pairs, so the matrix core's inputs
+// toggle as they do under a real contraction. The loop above repeats one
+// operand pair, which draws less power, so under the same power limit it runs
+// at a higher clock. FMT 0: v_mfma_f32_32x32x16_bf16 (pairs of bf16x8);
+// FMT 1: v_mfma_scale_f32_32x32x64_f8f6f4 with e4m3 operands (pairs of 32
+// bytes) and unit scales.
+constexpr int kDataSets = 8;
+template <int FMT>
+__global__ __launch_bounds__(512) void mfma_loop_data_kernel(const ea::i32x4* __restrict__ ops, float* out,
+                                                             int iters) {
+  constexpr int W = FMT == 0 ? 1 : 2;  // 16-byte pieces per operand
+  const ea::i32x4* src = ops + (size_t)threadIdx.x * kDataSets * 2 * W;
+  ea::i32x4 a[kDataSets][W], b[kDataSets][W];
+#pragma unroll
+  for (int j = 0; j < kDataSets; ++j) {
+#pragma unroll
+    for (int u = 0; u < W; ++u) {
+      a[j][u] = src[(2 * j) * W + u];
+      b[j][u] = src[(2 * j + 1) * W + u];
+    }
+  }
+  ea::f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  auto mf = [&](int ja, int jb, ea::f32x16 c) __attribute__((always_inline)) {
+    if constexpr (FMT == 0) {
+      return ea::mfma32x32x16(__builtin_bit_cast(ea::bf16x8, a[ja][0]), __builtin_bit_cast(ea::bf16x8, b[jb][0]), c);
+    } else {
+      const ea::i32x8 av = {a[ja][0][0], a[ja][0][1], a[ja][0][2], a[ja][0][3],
+                            a[ja][1][0], a[ja][1][1], a[ja][1][2], a[ja][1][3]};
+      const ea::i32x8 bv = {b[jb][0][0], b[jb][0][1], b[jb][0][2], b[jb][0][3],
+                            b[jb][1][0], b[jb][1][1], b[jb][1][2], b[jb][1][3]};
+      return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 0, 0, 0, 127, 0, 127);
+    }
+  };
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 16; j += 4) {
+      c0 = mf(j % kDataSets, (j + 3) % kDataSets, c0);
+      c1 = mf((j + 1) % kDataSets, (j + 4) % kDataSets, c1);
+      c2 = mf((j + 2) % kDataSets, (j + 5) % kDataSets, c2);
+      c3 = mf((j + 3) % kDataSets, (j + 6) % kDataSets, c3);
+    }
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sum += c0[i] + c1[i] + c2[i] + c3[i];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = sum;
+}
+
 // A streaming read: each thread reads kStreamUnroll 16-byte chunks per pass
 // (grid-stride, non-temporal) and folds them into one value, so the launch
 // measures the HBM read rate a plain kernel sustains on this device.
@@ -71,6 +122,26 @@ extern "C" ea_status ea_test_stream_read(const void* buf, size_t bytes, int* out
 extern "C" ea_status ea_test_mfma_loop(float* out, int blocks, int iters, void* stream) {
   if (out == nullptr || blocks <= 0 || iters <= 0 || blocks > 65536) return EA_ERR_INVALID;
   hipLaunchKernelGGL(mfma_loop_kernel, dim3(blocks), dim3(512), 0, (hipStream_t)stream, out, iters);
+  return hipGetLastError() == hipSuccess ? EA_OK : EA_ERR_HIP;
+}
+
+extern "C" size_t ea_test_mfma_loop_data_bytes(int fmt) {
+  if (fmt != 0 && fmt != 1) return 0;
+  return (size_t)512 * kDataSets * 2 * (fmt == 0 ? 16 : 32);
+}
+
+extern "C" ea_status ea_test_mfma_loop_data(const void* operands, size_t operands_bytes, float* out, int blocks,
+                                            int iters, int fmt, void* stream) {
+  if (operands == nullptr || out == nullptr || blocks <= 0 || iters <= 0 || blocks > 65536 || (fmt != 0 && fmt != 1))
+    return EA_ERR_INVALID;
+  if (operands_bytes < ea_test_mfma_loop_data_bytes(fmt)) return EA_ERR_WORKSPACE;
+  if (fmt == 0) {
+    hipLaunchKernelGGL(mfma_loop_data_kernel<0>, dim3(blocks), dim3(512), 0, (hipStream_t)stream,
+                       (const ea::i32x4*)operands, out, iters);
+  } else {
+    hipLaunchKernelGGL(mfma_loop_data_kernel<1>, dim3(blocks), dim3(512), 0, (hipStream_t)stream,
+                       (const ea::i32x4*)operands, out, iters);
+  }
   return hipGetLastError() == hipSuccess ? EA_OK : EA_ERR_HIP;
 }
 

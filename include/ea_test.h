@@ -35,6 +35,29 @@ ea_status ea_test_exp2(const float* x, float* y, int n, int mode, void* stream);
 ea_status ea_test_mfma_loop(float* out, int blocks, int iters, void* stream);
 
 /*
+ * ea_test_mfma_loop_data -- the same calibration with operands that change
+ * from one MFMA to the next, as in a real contraction: each of the 512 threads
+ * of a workgroup reads 8 operand pairs once from operands (thread t at byte
+ * t * 8 * 2 * P, pair j = (A, B) at 2 j P and (2 j + 1) P, P = 16 bytes for
+ * fmt 0, 32 for fmt 1) and each MFMA takes the next pair. fmt 0:
+ * v_mfma_f32_32x32x16_bf16, 32768 FLOP each; fmt 1:
+ * v_mfma_scale_f32_32x32x64_f8f6f4 with OCP e4m3 operands and unit e8m0
+ * scales, 131072 FLOP each. blocks workgroups of 8 waves issue iters x 16
+ * MFMAs each: FLOPs per launch = blocks * 8 * iters * 16 * (FLOP per MFMA).
+ * With random operands the matrix cores draw more power than with the fixed
+ * operands of ea_test_mfma_loop, and under the device's power limit the rate
+ * is what a contraction on such data can sustain.
+ *   operands: device buffer of at least ea_test_mfma_loop_data_bytes(fmt)
+ *   bytes (EA_ERR_WORKSPACE otherwise); out: device float array of blocks *
+ *   512 elements (one value per lane). EA_ERR_INVALID for null pointers,
+ *   blocks outside 1..65536, iters <= 0 or fmt not 0/1.
+ * ea_test_mfma_loop_data_bytes returns that size (0 for a bad fmt).
+ */
+size_t ea_test_mfma_loop_data_bytes(int fmt);
+ea_status ea_test_mfma_loop_data(const void* operands, size_t operands_bytes, float* out, int blocks, int iters,
+                                 int fmt, void* stream);
+
+/*
  * ea_test_stream_read -- calibration of the HBM read rate: blocks workgroups
  * of 256 threads read the device buffer buf once, 16 bytes per load, 16 loads
  * in flight per thread (grid-stride, non-temporal), and fold it into one value

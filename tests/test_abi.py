@@ -158,6 +158,22 @@ def test_mfma_loop_argument_errors(lib):
     assert lib.ea_test_mfma_loop(P, 1 << 17, 10, None) == -1
 
 
+def test_mfma_loop_data_argument_errors(lib):
+    assert lib.ea_test_mfma_loop_data_bytes(0) == 512 * 8 * 2 * 16
+    assert lib.ea_test_mfma_loop_data_bytes(1) == 512 * 8 * 2 * 32
+    assert lib.ea_test_mfma_loop_data_bytes(2) == 0
+    n0 = lib.ea_test_mfma_loop_data_bytes(0)
+    f = lib.ea_test_mfma_loop_data
+    assert f(None, n0, P, 4, 10, 0, None) == -1
+    assert f(P, n0, None, 4, 10, 0, None) == -1
+    assert f(P, n0, P, 0, 10, 0, None) == -1
+    assert f(P, n0, P, 1 << 17, 10, 0, None) == -1
+    assert f(P, n0, P, 4, 0, 0, None) == -1
+    assert f(P, n0, P, 4, 10, 2, None) == -1
+    assert f(P, n0 - 1, P, 4, 10, 0, None) == -4
+    assert f(P, n0, P, 4, 10, 1, None) == -4     # fp8 pairs take twice the bytes
+
+
 def test_bwd_argument_errors(lib):
     ws = lib.ea_attn_bwd_workspace_size(1, 2, 8)
     assert ws >= 2 * 2 * 8 * 4 and lib.ea_attn_bwd_workspace_size(0, 2, 8) == 0

@@ -57,6 +57,22 @@ def test_mfma_loop_calibration_runs():
     assert torch.isfinite(out).all()
 
 
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_mfma_loop_data_calibration_runs(fmt):
+    """The random-operand calibration loop (bf16, then MX e4m3) launches and
+    writes a finite value on every lane."""
+    import exact_attention_amd as ea
+    nbytes = ea.lib().ea_test_mfma_loop_data_bytes(fmt)
+    g = torch.Generator().manual_seed(7)
+    x = torch.randn(nbytes // 2, generator=g) * 0.05
+    ops = (x.to(torch.bfloat16).view(torch.uint8) if fmt == 0
+           else torch.randn(nbytes, generator=g).to(torch.float8_e4m3fn).view(torch.uint8)).to("cuda")
+    out = torch.full((8 * 512,), float("nan"), dtype=torch.float32, device="cuda")
+    assert ea.lib().ea_test_mfma_loop_data(ea._ptr(ops), ops.numel(), ea._ptr(out), 8, 10, fmt, None) == 0
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+
+
 def test_stream_read_calibration_reads_every_byte():
     """The streaming-read calibration used by bench.py visits every 16-byte
     chunk once: with all chunks zero but one, exactly one thread's folded
