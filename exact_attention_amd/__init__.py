@@ -71,6 +71,7 @@ _SIGNATURES = {
                                                                    _c_void_p], _c_int),
     "ea_test_wall_clock_khz": ([_c_int, _c_void_p], _c_int),
     "ea_test_fwd_tiles": ([_c_int] * 3, _c_size_t),
+    "ea_test_varlen_lds_order": ([_c_void_p, _c_void_p, _c_int, _c_int, _c_void_p, _c_void_p], _c_int),
     "ea_test_decode_gather": ([_c_void_p] * 5 + [_c_int] * 8 + [_c_void_p, _c_void_p, _c_size_t, _c_void_p,
                                                                 _c_size_t, _c_void_p], _c_int),
     "ea_test_fwd_tile_order": ([_c_int] * 5 + [_c_void_p, _c_size_t, _c_void_p], _c_int),
@@ -207,10 +208,14 @@ def varlen_lpt_order(cu_seqlens_q, cu_seqlens_k, causal: bool, block_m: int = 25
 
 def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, causal: bool = False,
                     scale: float | None = None, *, tuning: FwdTuning | None = None, want_lse: bool = True,
-                    seq_order: torch.Tensor | None = None):
+                    seq_order: torch.Tensor | None = None, input_order: bool = False):
     """Packed variable-length forward. q [Tq,Hq,d], k/v [Tk,Hkv,d] bf16 (THD);
     cu_seqlens int32 [S+1] on the GPU; seq_order (int32 [S] on the GPU, e.g.
     from varlen_lpt_order) sets the order the workgroups visit the sequences.
+    Without one, the default kernels (d = 128) order up to 512 sequences
+    heaviest first themselves when there are fewer (sequence, head) groups
+    than CUs (ea_attn_fwd_varlen); input_order=True keeps the input order
+    instead. The results do not depend on the order.
     Returns (o [Tq,Hq,d], lse [Hq,Tq])."""
     if seq_order is not None:
         _need(seq_order, "seq_order", torch.int32, 1)
@@ -237,10 +242,15 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, caus
         scale = 1.0 / math.sqrt(d)
     o = torch.empty_like(q)
     lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device) if want_lse else None
-    st = lib().ea_attn_fwd_varlen_ordered(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens_q),
-                                          _ptr(cu_seqlens_k), S, Tq, Tk, int(max_seqlen_q), Hq, Hkv, d,
-                                          int(bool(causal)), float(scale), _ptr(seq_order),
-                                          ctypes.byref(tuning) if tuning is not None else None, _stream(q))
+    tun = ctypes.byref(tuning) if tuning is not None else None
+    if seq_order is None and not input_order:
+        st = lib().ea_attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens_q),
+                                      _ptr(cu_seqlens_k), S, Tq, Tk, int(max_seqlen_q), Hq, Hkv, d,
+                                      int(bool(causal)), float(scale), tun, _stream(q))
+    else:
+        st = lib().ea_attn_fwd_varlen_ordered(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens_q),
+                                              _ptr(cu_seqlens_k), S, Tq, Tk, int(max_seqlen_q), Hq, Hkv, d,
+                                              int(bool(causal)), float(scale), _ptr(seq_order), tun, _stream(q))
     _check(st, "ea_attn_fwd_varlen")
     return o, lse
 

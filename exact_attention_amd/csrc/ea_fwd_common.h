@@ -95,6 +95,50 @@ __device__ __forceinline__ void persistent_snake(int per_xcd, F&& tile) {
   }
 }
 
+// Weight of a packed sequence in the heaviest-first (LPT) batch order of
+// "FlashAttention4 close reading", section 3.3: the key tiles (block_n keys
+// each) of the main loop of its last block of block_m query rows -- causal,
+// bottom-right aligned: keys up to that block's last row; non-causal: all
+// keys -- and 0 for a sequence without queries.
+__device__ __forceinline__ int lpt_weight(long long lq, long long lk, int causal, int block_m, int block_n) {
+  long long wt = 0;
+  if (lq > 0) {
+    long long nkeys = lk;
+    if (causal) {
+      const long long n_mb = (lq + block_m - 1) / block_m;
+      nkeys = min(lk, n_mb * block_m + lk - lq);
+    }
+    if (nkeys < 0) nkeys = 0;
+    wt = (nkeys + block_n - 1) / block_n;
+  }
+  return (int)min(wt, (long long)0x7fffffff);
+}
+
+// The heaviest-first order of n packed sequences, computed by one
+// workgroup of at least n threads into LDS: w[b] = weight of sequence b, then
+// order[rank(b)] = b with rank(b) = #{heavier} + #{equal and earlier} (a
+// stable descending sort by counting). Every thread of the workgroup must
+// call it (it holds two workgroup barriers).
+__device__ __forceinline__ void lpt_order_lds(const int* cu_q, const int* cu_k, int n, int causal, int block_m,
+                                              int block_n, EA_LDS int* w, EA_LDS int* order) {
+  const int b = threadIdx.x;
+  int wb = 0;
+  if (b < n) {
+    wb = lpt_weight((long long)cu_q[b + 1] - cu_q[b], (long long)cu_k[b + 1] - cu_k[b], causal, block_m, block_n);
+    w[b] = wb;
+  }
+  __syncthreads();
+  if (b < n) {
+    int rank = 0;
+    for (int t = 0; t < n; ++t) {
+      const int wt = w[t];
+      rank += (wt > wb) || (wt == wb && t < b);
+    }
+    order[rank] = b;
+  }
+  __syncthreads();
+}
+
 template <int EXPMODE>
 __device__ __forceinline__ float pp_exp2(float x, int i) {
   if constexpr (EXPMODE == 0) {

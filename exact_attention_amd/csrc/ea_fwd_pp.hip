@@ -385,8 +385,19 @@ __device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) 
   __shared__ __attribute__((aligned(1024))) uint16_t ks0[TILE], ks1[TILE], ks2[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t vs0[VTILE], vs1[VTILE], vs2[VTILE];
 
+  // packed sequences without a caller's order: the heaviest-first order,
+  // computed by the workgroup itself into LDS (lpt_order_lds; wave-uniform
+  // condition, every thread takes part)
+  __shared__ int lpt_w[VARLEN ? kLptLds : 1], lpt_o[VARLEN ? kLptLds : 1];
+  FwdArgs al = a;
+  if constexpr (VARLEN) {
+    if (a.lpt_auto) {
+      lpt_order_lds(a.cu_q, a.cu_k, a.nseq, CAUSAL ? 1 : 0, kPpBlockM, BN, (EA_LDS int*)lpt_w, (EA_LDS int*)lpt_o);
+      al.seq_order = lpt_o;
+    }
+  }
   PpTile t;
-  if (!pp_locate<CAUSAL, VARLEN>(a, xcd, j, t)) return;
+  if (!pp_locate<CAUSAL, VARLEN>(al, xcd, j, t)) return;
   const int off = t.lk - t.lq;  // bottom-right causal alignment
   const int nkb = t.nkb;
 

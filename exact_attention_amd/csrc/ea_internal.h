@@ -23,6 +23,8 @@ struct FwdArgs {
   float tau;           // lazy-rescale threshold in log2 units
   int natural;         // 1: ascending row-block order
   const int* seq_order;  // packed only: virtual -> actual sequence, or null (input order)
+  int lpt_auto;        // packed, seq_order null, nseq <= kLptLds: the ping-pong kernel's
+                       // workgroups order the sequences heaviest first themselves
   int persist_wgs;     // ping-pong kernel: > 0 runs the persistent form with this many
                        // workgroups (a multiple of 8, one per CU); 0: one workgroup per tile
   int tiles_per_xcd;   // set by the launcher for the persistent form
@@ -34,6 +36,9 @@ struct FwdArgs {
 constexpr int kFwdBlockM = 128;  // query rows per workgroup (4 waves x 32)
 constexpr int kFwdBlockN = 64;   // keys per K/V tile
 constexpr int kPpBlockM = 256;   // query rows per workgroup of the 8-wave ping-pong kernel
+// most packed sequences whose heaviest-first order a ping-pong workgroup
+// computes itself, one per thread of its 512
+constexpr int kLptLds = 512;
 
 // grid size for the forward (workgroups)
 int fwd_grid(const FwdArgs& a, bool varlen);
@@ -51,6 +56,9 @@ hipError_t launch_fwd_pp_stats(const FwdArgs& a, bool causal, hipStream_t s);
 hipError_t launch_fwd_tile_order(const FwdArgs& a, bool causal, int* out, hipStream_t s);
 
 // varlen batch order (heaviest sequence first): weights[b] and order[virtual] = actual
+// Test-only: the heaviest-first order a ping-pong workgroup computes for
+// itself (n <= kLptLds sequences, 256-row blocks) into out[n].
+hipError_t launch_lpt_lds_order(const int* cu_q, const int* cu_k, int n, int causal, int* out, hipStream_t s);
 hipError_t launch_lpt_order(const int* cu_q, const int* cu_k, int n, int causal, int block_m, int* weights,
                             int* order, hipStream_t s);
 

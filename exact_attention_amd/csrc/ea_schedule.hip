@@ -13,6 +13,7 @@
 //    #{equal and earlier} -- with the weights streamed through LDS in tiles,
 //    O(n^2) comparisons spread over n threads; order[rank(b)] = b.
 #include "ea_device.h"
+#include "ea_fwd_common.h"
 #include "ea_internal.h"
 
 namespace ea {
@@ -25,19 +26,7 @@ __global__ __launch_bounds__(kSchedThreads) void lpt_weight_kernel(const int* cu
                                                                    int causal, int block_m, int block_n, int* w) {
   const int b = blockIdx.x * kSchedThreads + threadIdx.x;
   if (b >= n) return;
-  const long long lq = (long long)cu_q[b + 1] - cu_q[b];
-  const long long lk = (long long)cu_k[b + 1] - cu_k[b];
-  long long wt = 0;
-  if (lq > 0) {
-    long long nkeys = lk;
-    if (causal) {
-      const long long n_mb = (lq + block_m - 1) / block_m;
-      nkeys = min(lk, n_mb * block_m + lk - lq);
-    }
-    if (nkeys < 0) nkeys = 0;
-    wt = (nkeys + block_n - 1) / block_n;
-  }
-  w[b] = (int)min(wt, (long long)0x7fffffff);
+  w[b] = lpt_weight((long long)cu_q[b + 1] - cu_q[b], (long long)cu_k[b + 1] - cu_k[b], causal, block_m, block_n);
 }
 
 __global__ __launch_bounds__(kSchedThreads) void lpt_rank_kernel(const int* w, int n, int* order) {
@@ -59,7 +48,21 @@ __global__ __launch_bounds__(kSchedThreads) void lpt_rank_kernel(const int* w, i
   if (b < n) order[rank] = b;
 }
 
+// Test-only: the order the forward's workgroups compute for themselves
+// (lpt_order_lds), written out by one workgroup of the forward's size.
+__global__ __launch_bounds__(512) void lpt_lds_kernel(const int* cu_q, const int* cu_k, int n, int causal,
+                                                      int block_m, int* out) {
+  __shared__ int w[kLptLds], order[kLptLds];
+  lpt_order_lds(cu_q, cu_k, n, causal, block_m, kFwdBlockN, (EA_LDS int*)w, (EA_LDS int*)order);
+  if ((int)threadIdx.x < n) out[threadIdx.x] = order[threadIdx.x];
+}
+
 }  // namespace
+
+hipError_t launch_lpt_lds_order(const int* cu_q, const int* cu_k, int n, int causal, int* out, hipStream_t s) {
+  hipLaunchKernelGGL(lpt_lds_kernel, dim3(1), dim3(512), 0, s, cu_q, cu_k, n, causal, kPpBlockM, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_lpt_order(const int* cu_q, const int* cu_k, int n, int causal, int block_m, int* weights,
                             int* order, hipStream_t s) {

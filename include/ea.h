@@ -153,6 +153,12 @@ ea_status ea_attn_fwd_hd(const void* q, const void* k, const void* v, void* o, f
  *   Rows outside every sequence are neither read nor written.
  * Packing without padding follows the unpadded-batch advice in "FlashAttention:
  * not less compute, less data movement", section 05.
+ * Work order: when the batch has fewer (sequence, head) groups than the GPU
+ * has CUs and at most 512 sequences, the default kernels (d = 128; 8-wave
+ * ping-pong) visit the sequences heaviest first (the order of
+ * ea_varlen_lpt_order, computed by each workgroup in its LDS), so the longest
+ * sequences' tiles start first; otherwise in input order. The results do not
+ * depend on the order.
  */
 ea_status ea_attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                              const int* cu_seqlens_q, const int* cu_seqlens_k, int num_seqs,

@@ -118,6 +118,20 @@ ea_status ea_test_stream_read(const void* buf, size_t bytes, int* out, int block
  */
 size_t ea_test_fwd_rescale_stats_len(int B, int Nq, int Hq);
 /*
+ * ea_test_varlen_lds_order -- the heaviest-first order that the ping-pong
+ * forward's workgroups compute for themselves when ea_attn_fwd_varlen gets no
+ * order ("FlashAttention4 close reading", section 3.3: weight = 64-key tiles
+ * of a sequence's last 256-row block, heaviest first, equal weights in input
+ * order), computed by one workgroup with the forward's own device code.
+ *   order: device int32 [num_seqs], written: order[v] = actual sequence.
+ *   EA_ERR_INVALID for null pointers, num_seqs <= 0 or causal not 0/1;
+ *   EA_ERR_UNSUPPORTED for num_seqs > 512 (the forward then keeps the input
+ *   order).
+ */
+ea_status ea_test_varlen_lds_order(const int* cu_seqlens_q, const int* cu_seqlens_k, int num_seqs, int causal,
+                                   int* order, void* stream);
+
+/*
  * ea_test_fwd_tiles / ea_test_fwd_tile_order -- the work order of the dense
  * bf16 forward ("FlashAttention4 close reading", section 3.3: the cache-aware
  * hierarchical LPT traversal). ea_test_fwd_tiles returns the number of work

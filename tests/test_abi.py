@@ -174,6 +174,15 @@ def test_mfma_loop_data_argument_errors(lib):
     assert f(P, n0, P, 4, 10, 1, None) == -4     # fp8 pairs take twice the bytes
 
 
+def test_varlen_lds_order_argument_errors(lib):
+    f = lib.ea_test_varlen_lds_order
+    assert f(None, P, 4, 1, P, None) == -1
+    assert f(P, P, 4, 1, None, None) == -1
+    assert f(P, P, 0, 1, P, None) == -1
+    assert f(P, P, 4, 2, P, None) == -1
+    assert f(P, P, 513, 1, P, None) == -2      # beyond one workgroup's threads
+
+
 def test_bwd_argument_errors(lib):
     ws = lib.ea_attn_bwd_workspace_size(1, 2, 8)
     assert ws >= 2 * 2 * 8 * 4 and lib.ea_attn_bwd_workspace_size(0, 2, 8) == 0

@@ -49,6 +49,52 @@ def test_order_of_the_pages_example():
     assert order == [1, 2, 3, 0]
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_workgroup_order_matches_oracle(causal):
+    """The order the ping-pong forward's workgroups compute for themselves
+    (default varlen call) equals the scheduling oracle's LPT order with
+    256-row blocks: weights, ties in input order, sequences without queries."""
+    import exact_attention_amd as ea
+    rng = np.random.default_rng(43)
+    for n in (1, 2, 7, 64, 300, 512):
+        lq = rng.integers(0, 9000, n)
+        lk = np.maximum(lq + rng.integers(-300, 600, n) * (rng.random(n) < 0.5), 0)
+        lq[rng.random(n) < 0.05] = 0
+        lk[: n // 3] = lk[0]
+        cu_q, cu_k = cu_of(lq), cu_of(lk)
+        out = torch.full((n,), -7, dtype=torch.int32, device="cuda")
+        log(f"workgroup LPT order n={n} causal={causal}")
+        dq, dk = torch.from_numpy(cu_q).cuda(), torch.from_numpy(cu_k).cuda()  # alive until the kernel ran
+        st = ea.lib().ea_test_varlen_lds_order(ea._ptr(dq), ea._ptr(dk), n, int(causal), ea._ptr(out), None)
+        assert st == 0
+        torch.cuda.synchronize()
+        assert out.cpu().numpy().tolist() == S.lpt_order(cu_q, cu_k, causal, 256, 64)
+
+
+@pytest.mark.parametrize("kernel", [0, 2, 4])
+@pytest.mark.parametrize("causal", [True, False])
+def test_default_varlen_order_is_bitwise_the_input_order(kernel, causal):
+    """The default varlen forward (its workgroups walk the sequences heaviest
+    first) gives the bits of the input-order walk, and matches the oracle."""
+    import exact_attention_amd as ea
+    L = [40, 1300, 7, 600, 2100, 0, 333, 5000, 1]
+    inp = W.varlen(L, L, 4, 2, 128, causal, seed=44)
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()  # noqa: E731
+    q, k, v = t(inp.q).view(torch.bfloat16), t(inp.k).view(torch.bfloat16), t(inp.v).view(torch.bfloat16)
+    cu = t(inp.cu_q)
+    log(f"default varlen order, kernel {kernel} causal {causal}")
+    res = []
+    for inorder in (False, True):
+        o, lse = ea.attn_fwd_varlen(q, k, v, cu, cu, max(L), causal, inp.scale, tuning=ea.tuning(kernel=kernel),
+                                    input_order=inorder)
+        torch.cuda.synchronize()
+        res.append((f64(host_bits(o)), lse.cpu().numpy().astype(np.float64)))
+    assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1])
+    ro, rl = oracle.attention_varlen(f64(inp.q), f64(inp.k), f64(inp.v), inp.cu_q, inp.cu_k, causal, inp.scale)
+    assert_o_close(res[0][0], ro)
+    assert_lse_close(res[0][1], rl)
+
+
 def run_varlen_ordered(inp, kernel, order=None, poison=None):
     import exact_attention_amd as ea
     t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()  # noqa: E731
