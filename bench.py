@@ -725,6 +725,27 @@ def main():
             "shader_mhz": mhz, "wall_clock_khz": khz, "stats_launch_ms": float(t_st.mean()),
             "what": "sum over waves of shader clock cycles (s_memtime) / wall clock ticks (s_memrealtime) over the "
                     "forward's step loops, in the statistics launch after 30 back-to-back launches"}
+        # where a step's cycles go: the phase-stamped launch of the same kernel
+        # (one launch after the statistics launches; it runs a few per cent
+        # slower than the plain kernel because of the stamps' waits)
+        _, _, cy = ea.test_fwd_phase_cycles(q, k, v, True, inp.scale)
+        cy = cy.cpu().numpy().astype(np.float64)
+        steps = cy[:, :, 6].sum(axis=0)
+        tiles = cy[:, :, 7].sum(axis=0)
+        part = cy[:, :, :4].sum(axis=0) / steps[:, None]
+        bound = cy[:, :, 4:6].sum(axis=0) / tiles[:, None]
+        wave_cycles = cy[:, :, :6].sum()
+        out["prefill"]["phases"] = {
+            "what": "shader cycles per 64-key step and per tile, mean over waves (ea_test_fwd_phase_cycles); "
+                    "waves 0-3 issue the K/V DMA at the start of their VALU part; a wave's MFMA part runs beside "
+                    "the other group's VALU part on the same SIMD; ideal MFMA part = 32 MFMAs x 32 cycles = 1024",
+            "group_a_per_step": {"mfma_part": float(part[:4, 0].mean()), "wait_after_mfma": float(part[:4, 1].mean()),
+                                 "valu_part_with_dma": float(part[:4, 2].mean()),
+                                 "wait_after_valu": float(part[:4, 3].mean())},
+            "group_b_per_step": {"mfma_part": float(part[4:, 0].mean()), "wait_after_mfma": float(part[4:, 1].mean()),
+                                 "valu_part": float(part[4:, 2].mean()), "wait_after_valu": float(part[4:, 3].mean())},
+            "per_tile": {"prologue": float(bound[:, 0].mean()), "epilogue": float(bound[:, 1].mean())},
+            "tile_boundary_share": float(cy[:, :, 4:6].sum() / wave_cycles)}
         at_clock = PEAK_BF16_TFLOPS * mhz / 2400.0
         if "roofline" in out:
             tf = out["roofline"]["achieved"]

@@ -71,6 +71,8 @@ _SIGNATURES = {
                                                                    _c_void_p], _c_int),
     "ea_test_wall_clock_khz": ([_c_int, _c_void_p], _c_int),
     "ea_test_fwd_tiles": ([_c_int] * 3, _c_size_t),
+    "ea_test_fwd_phase_cycles_len": ([_c_int] * 3, _c_size_t),
+    "ea_test_fwd_phase_cycles": ([_c_void_p] * 5 + [_c_int] * 6 + [_c_float, _c_void_p, _c_size_t, _c_void_p], _c_int),
     "ea_test_varlen_lds_order": ([_c_void_p, _c_void_p, _c_int, _c_int, _c_void_p, _c_void_p], _c_int),
     "ea_test_decode_gather": ([_c_void_p] * 5 + [_c_int] * 8 + [_c_void_p, _c_void_p, _c_size_t, _c_void_p,
                                                                 _c_size_t, _c_void_p], _c_int),
@@ -414,6 +416,33 @@ def test_fwd_rescale_stats(q, k, v, causal: bool, scale: float | None = None, re
                                          _stream(q))
     _check(st, "ea_test_fwd_rescale_stats")
     return o, lse, stats.view(-1, 8, 4)
+
+
+def test_fwd_phase_cycles(q, k, v, causal: bool, scale: float | None = None):
+    """Test-only: the default dense forward (d = 128) with shader-clock stamps
+    at its phase edges. Returns (o, lse, cycles uint64 as int64 [workgroups, 8,
+    8]: per wave the summed cycles of the MFMA parts, the barrier waits after
+    them, the VALU parts, the barrier waits after those, the tile prologues and
+    epilogues, then the steps and the tiles)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, torch.bfloat16, 4)
+    B, Nq, Hq, d = q.shape
+    _, Nk, Hkv, _ = k.shape
+    if d != 128 or tuple(v.shape) != tuple(k.shape) or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("q [B,Nq,Hq,128], k/v [B,Nk,Hkv,128]")
+    _on_gpu(("q", q), ("k", k), ("v", v))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    n = int(lib().ea_test_fwd_phase_cycles_len(B, Nq, Hq))
+    if n == 0:
+        raise EAError("ea_test_fwd_phase_cycles_len: no CU count")
+    cyc = torch.zeros(n, dtype=torch.int64, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    st = lib().ea_test_fwd_phase_cycles(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Nq, Nk, Hq, Hkv,
+                                        int(bool(causal)), float(scale), _ptr(cyc), n, _stream(q))
+    _check(st, "ea_test_fwd_phase_cycles")
+    return o, lse, cyc.view(-1, 8, 8)
 
 
 def test_fwd_tile_order(B: int, Nq: int, Nk: int, Hq: int, causal: bool, device="cuda"):

@@ -236,7 +236,57 @@ ea_status ea_test_fwd_rescale_stats(const void* q, const void* k, const void* v,
   a.stats = stats;
   a.persist_wgs = persistent_workgroups();
   if (a.persist_wgs <= 0) return fail(EA_ERR_HIP, "device CU count unavailable");
-  return hip_status(ea::launch_fwd_pp_stats(a, causal != 0, (hipStream_t)stream), "statistics forward launch");
+  return hip_status(ea::launch_fwd_pp_stats(a, causal != 0, 1, (hipStream_t)stream), "statistics forward launch");
+}
+
+size_t ea_test_fwd_phase_cycles_len(int B, int Nq, int Hq) {
+  if (B <= 0 || Nq <= 0 || Hq <= 0) return 0;
+  ea::FwdArgs a{};
+  a.nseq = B;
+  a.Nq = Nq;
+  a.Hq = Hq;
+  a.n_mb = (Nq + ea::kPpBlockM - 1) / ea::kPpBlockM;
+  a.persist_wgs = persistent_workgroups();
+  if (a.persist_wgs <= 0) return 0;
+  return (size_t)ea::fwd_pp_persistent_grid(a) * 64;
+}
+
+ea_status ea_test_fwd_phase_cycles(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Nq,
+                                   int Nk, int Hq, int Hkv, int causal, float scale, unsigned long long* cycles,
+                                   size_t cycles_len, void* stream) {
+  if (!q || !k || !v || !o || !cycles) return fail(EA_ERR_INVALID, "q, k, v, o and cycles must be non-null");
+  if (B <= 0 || Nq <= 0 || Nk <= 0 || Hq <= 0 || Hkv <= 0)
+    return fail(EA_ERR_INVALID, "B, Nq, Nk, Hq and Hkv must be positive");
+  if (Hq % Hkv) return fail(EA_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if (!finite_pos(scale)) return fail(EA_ERR_INVALID, "scale must be finite and positive");
+  if (causal != 0 && causal != 1) return fail(EA_ERR_INVALID, "causal must be 0 or 1");
+  if ((long long)B * Nq >= (1LL << 31) || (long long)B * Nk >= (1LL << 31))
+    return fail(EA_ERR_UNSUPPORTED, "B * N must be below 2^31");
+  const size_t need = ea_test_fwd_phase_cycles_len(B, Nq, Hq);
+  if (need == 0) return fail(EA_ERR_HIP, "device CU count unavailable");
+  if (cycles_len < need) return fail(EA_ERR_WORKSPACE, "cycles needs %zu entries, %zu given", need, cycles_len);
+  ea::FwdArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.o = (uint16_t*)o;
+  a.lse = lse;
+  a.nseq = B;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.group = Hq / Hkv;
+  a.total_q = B * Nq;
+  a.n_mb = (Nq + ea::kPpBlockM - 1) / ea::kPpBlockM;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.tau = 8.0f;
+  a.cycles = cycles;
+  a.persist_wgs = persistent_workgroups();
+  if (hipError_t e = hipMemsetAsync(cycles, 0, need * sizeof(unsigned long long), (hipStream_t)stream);
+      e != hipSuccess)
+    return hip_status(e, "phase-cycle clear");
+  return hip_status(ea::launch_fwd_pp_stats(a, causal != 0, 2, (hipStream_t)stream), "phase-cycle forward launch");
 }
 
 ea_status ea_attn_fwd_tuned(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -366,12 +366,18 @@ __device__ __forceinline__ uint32_t dma_lane_off(int piece, int lane, size_t str
   return (uint32_t)(r * (int)stride * 2 + ((sl ^ swz<DD>(r)) << 4));
 }
 
-// One work tile: the whole forward of its 256 rows. STATS: also write, per
+// One work tile: the whole forward of its 256 rows. STATS 1: also write, per
 // wave, the number of steps with live keys, of lazy rescales, and the shader
 // clock cycles (s_memtime) and constant-rate wall clock ticks (s_memrealtime)
 // its step loop took, to a.stats[4 (8 (8 j + xcd) + wave) + {0, 1, 2, 3}]
-// (plain vector stores).
-template <int D, int DV, bool CAUSAL, bool VARLEN, int EXPMODE, bool STATS = false>
+// (plain vector stores). STATS 2: add, per wave, the shader cycles of each
+// phase of the tile to a.cycles[8 (8 blockIdx + wave) + {0..7}]: the MFMA
+// parts, the waits at the barriers after them, the VALU parts (with the DMA
+// issue of group A), the waits at the barriers after those, the prologue
+// (tile start to the first step), the epilogue (last step to the issued
+// stores), the steps and the tiles (each read with an immediate wait, so the
+// launch runs a few per cent slower than the plain one).
+template <int D, int DV, bool CAUSAL, bool VARLEN, int EXPMODE, int STATS = 0>
 __device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) {
   constexpr int BN = kFwdBlockN;
   constexpr int TILE = BN * D;               // bf16 elements per K stage
@@ -396,12 +402,24 @@ __device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) 
       al.seq_order = lpt_o;
     }
   }
+  // STATS 2: shader clock now (low 32 bits: a tile's phases take fewer than
+  // 2^32 cycles), read with an immediate wait
+  auto stamp = [&]() __attribute__((always_inline)) -> uint32_t {
+    sched_fence();
+    const uint32_t c = (uint32_t)__builtin_amdgcn_s_memtime();
+    wait_lgkm0();
+    sched_fence();
+    return c;
+  };
+  uint32_t ph[6] = {0, 0, 0, 0, 0, 0};
+  uint32_t t_entry = 0;
+  if constexpr (STATS == 2) t_entry = stamp();
   PpTile t;
   if (!pp_locate<CAUSAL, VARLEN>(al, xcd, j, t)) return;
   const int off = t.lk - t.lq;  // bottom-right causal alignment
   const int nkb = t.nkb;
 
-  PpCore<D, DV, CAUSAL, EXPMODE, STATS> cr;
+  PpCore<D, DV, CAUSAL, EXPMODE, STATS == 1> cr;
   cr.init();
   cr.set_tau(a.tau);
   const int tid = threadIdx.x;
@@ -458,15 +476,28 @@ __device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) 
   // pieces in flight -- before the barrier after which both groups read them.
   auto step = [&](int r, int s) __attribute__((always_inline)) {
     const bool act = s < nkb && !tile_dead(s);
+    uint32_t c0 = 0, c1 = 0, c2 = 0, c3 = 0;
+    if constexpr (STATS == 2) c0 = stamp();
     cr.mfma_part(kstage(r), vstage((r + 2) % 3));
+    if constexpr (STATS == 2) c1 = stamp();
     pp_barrier();
+    if constexpr (STATS == 2) c2 = stamp();
     if (grp == 0) {
       dma_tile(kstage((r + 2) % 3), kg_base, s + 2, KTILE{});
       dma_tile(vstage((r + 1) % 3), vg_base, s + 1, VTILE_{});
     }
     cr.valu_part(s, act, qi, wrow, t.lk, off, sl, a.tau);
+    if constexpr (STATS == 2) c3 = stamp();
     if (grp == 0) wait_vmcnt<IPW + IPWV>();
     pp_barrier();
+    if constexpr (STATS == 2) {
+      const uint32_t c4 = stamp();
+      // the sums live in vector registers (launder): the scalar file is full
+      ph[0] = (uint32_t)launder((int)(ph[0] + (c1 - c0)));
+      ph[1] = (uint32_t)launder((int)(ph[1] + (c2 - c1)));
+      ph[2] = (uint32_t)launder((int)(ph[2] + (c3 - c2)));
+      ph[3] = (uint32_t)launder((int)(ph[3] + (c4 - c3)));
+    }
   };
 
   // prologue: K_0, K_1 and V_0 (read in steps 0 and 1); the V stage that
@@ -484,9 +515,10 @@ __device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) 
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  if constexpr (STATS == 2) ph[4] = stamp() - t_entry;
 
   unsigned long long cyc0 = 0, rt0 = 0;
-  if constexpr (STATS) {
+  if constexpr (STATS == 1) {
     cyc0 = __builtin_amdgcn_s_memtime();
     rt0 = __builtin_amdgcn_s_memrealtime();
   }
@@ -499,7 +531,9 @@ __device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) 
   if (grp == 0) pp_barrier();
   // no DMA may still be writing this workgroup's LDS when it exits
   __builtin_amdgcn_s_waitcnt(0);
-  if constexpr (STATS) {
+  uint32_t t_loop_end = 0;
+  if constexpr (STATS == 2) t_loop_end = stamp();
+  if constexpr (STATS == 1) {
     const unsigned long long cyc1 = __builtin_amdgcn_s_memtime();
     const unsigned long long rt1 = __builtin_amdgcn_s_memrealtime();
     if (lane == 0) {
@@ -511,6 +545,17 @@ __device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) 
     }
   }
   cr.template store<VARLEN>(a, t.seq, t.h, t.row_lo, t.q0, t.lq);
+  if constexpr (STATS == 2) {
+    ph[5] = stamp() - t_loop_end;
+    if (lane == 0) {
+      // this wave's slots: only it adds to them, one tile after the other
+      unsigned long long* cyc = a.cycles + 8 * (8 * blockIdx.x + w);
+#pragma unroll
+      for (int i = 0; i < 6; ++i) cyc[i] += (unsigned long long)ph[i];
+      cyc[6] += (unsigned long long)(nkb + 1);
+      cyc[7] += 1;
+    }
+  }
 }
 
 // Persistent walk with the K/V pipeline running on across tiles (the
@@ -759,7 +804,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
 // Persistent form (persistent_snake in ea_fwd_common.h): one workgroup per
 // CU runs the one-tile body for each tile of its list. STATS: the test-only
 // statistics launch (per-wave step and rescale counts in a.stats).
-template <int D, int DV, bool CAUSAL, bool VARLEN, int EXPMODE, bool STATS = false>
+template <int D, int DV, bool CAUSAL, bool VARLEN, int EXPMODE, int STATS = 0>
 __global__ __launch_bounds__(512, 1) void fwd_pp_persistent_kernel(FwdArgs a) {
   persistent_snake(uniform(a.tiles_per_xcd),
                    [&](int xcd, int j) { pp_tile<D, DV, CAUSAL, VARLEN, EXPMODE, STATS>(a, xcd, j); });
@@ -768,17 +813,32 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_persistent_kernel(FwdArgs a) {
 // Test-only: the default dense forward (persistent ping-pong, d = 128,
 // hardware exp) with per-wave lazy-rescale and clock statistics in a.stats,
 // which must hold 32 ints per work tile.
-hipError_t launch_fwd_pp_stats(const FwdArgs& a, bool causal, hipStream_t s) {
+// mode 1: a.stats; mode 2: the per-phase shader cycles in a.cycles (8 per
+// wave of each of the launch's workgroups, added to, so zeroed by the caller)
+hipError_t launch_fwd_pp_stats(const FwdArgs& a, bool causal, int mode, hipStream_t s) {
   FwdArgs b = a;
   const int grid = fwd_grid(a, false);
   b.tiles_per_xcd = grid / 8;
   const int w = max(min(a.persist_wgs / 8, b.tiles_per_xcd), 1);
-  if (causal) {
-    hipLaunchKernelGGL((fwd_pp_persistent_kernel<128, 128, true, false, 0, true>), dim3(8 * w), dim3(512), 0, s, b);
+  if (mode == 2) {
+    if (causal) {
+      hipLaunchKernelGGL((fwd_pp_persistent_kernel<128, 128, true, false, 0, 2>), dim3(8 * w), dim3(512), 0, s, b);
+    } else {
+      hipLaunchKernelGGL((fwd_pp_persistent_kernel<128, 128, false, false, 0, 2>), dim3(8 * w), dim3(512), 0, s, b);
+    }
+  } else if (causal) {
+    hipLaunchKernelGGL((fwd_pp_persistent_kernel<128, 128, true, false, 0, 1>), dim3(8 * w), dim3(512), 0, s, b);
   } else {
-    hipLaunchKernelGGL((fwd_pp_persistent_kernel<128, 128, false, false, 0, true>), dim3(8 * w), dim3(512), 0, s, b);
+    hipLaunchKernelGGL((fwd_pp_persistent_kernel<128, 128, false, false, 0, 1>), dim3(8 * w), dim3(512), 0, s, b);
   }
   return hipGetLastError();
+}
+
+// workgroups of the persistent launch for this problem (the cycles array
+// holds 64 entries per workgroup)
+int fwd_pp_persistent_grid(const FwdArgs& a) {
+  const int tiles_per_xcd = fwd_grid(a, false) / 8;
+  return 8 * max(min(a.persist_wgs / 8, tiles_per_xcd), 1);
 }
 
 // Test-only: work tile t of the dense per-tile launch (t = 8 j + XCD, the

@@ -31,6 +31,7 @@ struct FwdArgs {
   int unroll_kv;       // with persist_wgs > 0 and equal head dims: 1 runs the walk whose
                        // K/V pipeline continues across tiles (unroll-KV schedule)
   int* stats;          // test-only statistics launch: per-wave counts (else unused)
+  unsigned long long* cycles;  // test-only phase-cycle launch: per-wave sums (else unused)
 };
 
 constexpr int kFwdBlockM = 128;  // query rows per workgroup (4 waves x 32)
@@ -51,7 +52,8 @@ hipError_t launch_fwd_pp(const FwdArgs& a, int d, int dv, bool causal, bool varl
 // test-only: the persistent ping-pong forward (dense, d = 128, hardware exp)
 // writing per-wave live-step and lazy-rescale counts to a.stats (16 ints per
 // work tile); a.n_mb counts kPpBlockM-row blocks, a.persist_wgs is set
-hipError_t launch_fwd_pp_stats(const FwdArgs& a, bool causal, hipStream_t s);
+hipError_t launch_fwd_pp_stats(const FwdArgs& a, bool causal, int mode, hipStream_t s);
+int fwd_pp_persistent_grid(const FwdArgs& a);
 // test-only: (sequence, head, row block) of every dense work tile, 3 ints each
 hipError_t launch_fwd_tile_order(const FwdArgs& a, bool causal, int* out, hipStream_t s);
 

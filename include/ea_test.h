@@ -132,6 +132,31 @@ ea_status ea_test_varlen_lds_order(const int* cu_seqlens_q, const int* cu_seqlen
                                    int* order, void* stream);
 
 /*
+ * ea_test_fwd_phase_cycles -- the default dense forward of ea_test_fwd_rescale_stats
+ * (persistent ping-pong, d = 128, lazy-rescale threshold 2^8) with a shader-
+ * clock stamp (s_memtime, read with an immediate wait) at every phase edge,
+ * adding per wave of each of its workgroups (one per CU, 8 waves each):
+ *   cycles[8 (8 g + w) + 0] MFMA parts (issue of S = K Q^T and O += V P),
+ *                       + 1 waits at the barriers after them,
+ *                       + 2 VALU parts (softmax; waves 0-3 also issue the K/V DMA),
+ *                       + 3 waits at the barriers after those,
+ *                       + 4 tile prologues (tile start to the first step),
+ *                       + 5 tile epilogues (last step to the output stores issued),
+ *                       + 6 steps, + 7 tiles.
+ * With two waves per SIMD, a wave's MFMA part runs beside the other group's
+ * VALU part. o and lse are written as by ea_attn_fwd; the stamps make the
+ * launch a few per cent slower. cycles: device array of at least
+ * ea_test_fwd_phase_cycles_len(B, Nq, Hq) entries (EA_ERR_WORKSPACE otherwise),
+ * cleared by the call (hipMemsetAsync) before it adds. Other errors as for
+ * ea_test_fwd_rescale_stats. ea_test_fwd_phase_cycles_len returns 0 for
+ * non-positive sizes or when the CU count is unavailable.
+ */
+size_t ea_test_fwd_phase_cycles_len(int B, int Nq, int Hq);
+ea_status ea_test_fwd_phase_cycles(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Nq,
+                                   int Nk, int Hq, int Hkv, int causal, float scale, unsigned long long* cycles,
+                                   size_t cycles_len, void* stream);
+
+/*
  * ea_test_fwd_tiles / ea_test_fwd_tile_order -- the work order of the dense
  * bf16 forward ("FlashAttention4 close reading", section 3.3: the cache-aware
  * hierarchical LPT traversal). ea_test_fwd_tiles returns the number of work

@@ -174,6 +174,21 @@ def test_mfma_loop_data_argument_errors(lib):
     assert f(P, n0, P, 4, 10, 1, None) == -4     # fp8 pairs take twice the bytes
 
 
+def test_phase_cycles_argument_errors(lib):
+    assert lib.ea_test_fwd_phase_cycles_len(0, 8, 2) == 0
+    f = lib.ea_test_fwd_phase_cycles
+
+    def call(q=P, cyc=P, B=1, Nq=8, Nk=8, Hq=2, Hkv=2, causal=1, scale=0.1, n=1 << 20):
+        return f(q, P, P, P, None, B, Nq, Nk, Hq, Hkv, causal, scale, cyc, n, None)
+
+    assert call(q=None) == -1
+    assert call(cyc=None) == -1
+    assert call(Nk=0) == -1
+    assert call(Hq=3) == -1
+    assert call(causal=2) == -1
+    assert call(scale=0.0) == -1
+
+
 def test_varlen_lds_order_argument_errors(lib):
     f = lib.ea_test_varlen_lds_order
     assert f(None, P, 4, 1, P, None) == -1

@@ -102,3 +102,36 @@ def test_prefill_workload_skipped_fraction():
     mhz = cyc[has].sum() / ticks[has].sum() * ea.test_wall_clock_khz() / 1e3
     log(f"prefill: shader clock over the step loops {mhz:.0f} MHz")
     assert 300 < mhz < 3000
+
+
+@pytest.mark.parametrize("shape", [(1, 1000, 1000, 2, 2, True), (4, 8192, 8192, 16, 16, True)])
+def test_phase_cycles(shape):
+    """The phase-stamped launch: outputs bit for bit those of the default
+    forward, every wave's steps and tiles counted once (steps = key tiles + 1
+    per tile, as the pipeline runs one step past the last tile), and positive
+    cycles in every phase of a wave that ran tiles."""
+    import exact_attention_amd as ea
+    B, Nq, Nk, Hq, Hkv, causal = shape
+    inp = W.dense(B, Nq, Nk, Hq, Hkv, 128, causal, seed=420 + Nq)
+    q, k, v = dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v)
+    o_ref, l_ref = ea.attn_fwd(q, k, v, causal, inp.scale)
+    o, lse, cyc = ea.test_fwd_phase_cycles(q, k, v, causal, inp.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(lse, l_ref)
+    c = cyc.cpu().numpy()
+    n_mb = -(-Nq // 256)
+    groups = B * Hq
+    want_steps = 0
+    for mb in range(n_mb):
+        nkeys = min(Nk, 256 * mb + 256 + Nk - Nq) if causal else Nk
+        want_steps += -(-max(nkeys, 0) // 64) + 1
+    want_steps *= groups
+    assert c[:, :, 6].sum() == 8 * want_steps
+    assert c[:, :, 7].sum() == 8 * groups * n_mb
+    ran = c[:, 0, 7] > 0
+    assert np.all(c[ran][:, :, :6] > 0)
+    st = c[:, :, 6].sum(axis=0)
+    per_step = c[:, :, :4].sum(axis=0) / st[:, None]
+    log(f"  {shape}: cycles per step, waves 0-3 (MFMA, wait, VALU+DMA, wait): "
+        f"{np.round(per_step[:4].mean(axis=0))}; waves 4-7: {np.round(per_step[4:].mean(axis=0))}; "
+        f"prologue + epilogue per tile {np.round(c[:, :, 4:6].sum(axis=(0, 1)) / c[:, :, 7].sum())}")
