@@ -450,6 +450,32 @@ __device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) 
     for (int i = 0; i < NP; ++i)
       buffer_load16_lds(rs, (EA_LDS void*)(stage + 512 * ((w & 3) * NP + i)), V ? dma_voff[i] : dma_off[i]);
   };
+  // The same DMA inside the step loop with little scalar work in front of
+  // the softmax it precedes: the tile's address advances by one tile per step
+  // from a running pointer, and its record count is that of a whole tile, of
+  // the last fetched tile (nkb - 1), or 0 past it. A tile at or past nkb gets
+  // no records, so nothing is read from wherever its address points.
+  const int rows_last = nkb > 0 ? min(t.lk - (nkb - 1) * BN, BN) : 0;
+  const uint32_t nrk_full = uniform((BN - 1) * (int)kstride * 2 + D * 2);
+  const uint32_t nrk_last = uniform(rows_last > 0 ? (rows_last - 1) * (int)kstride * 2 + D * 2 : 0);
+  // next tiles the loop fetches: K_2 and V_1 (the prologue fetches K_0, K_1, V_0)
+  const uint16_t* kdma = uniform_ptr(kg_base + (size_t)2 * BN * kstride);
+  const uint16_t* vdma = uniform_ptr(vg_base + (size_t)BN * vstride);
+  auto dma_next = [&](EA_LDS uint16_t* stage, const uint16_t*& cur, int tt, auto v_tile) __attribute__((always_inline)) {
+    constexpr bool V = decltype(v_tile)::value;
+    constexpr int NP = V ? IPWV : IPW;
+    uint32_t nfull = nrk_full, nlast = nrk_last;
+    if constexpr (V && DV != D) {  // V rows differ from K rows only for (192, 128)
+      nfull = uniform((BN - 1) * (int)vstride * 2 + DV * 2);
+      nlast = uniform(rows_last > 0 ? (rows_last - 1) * (int)vstride * 2 + DV * 2 : 0);
+    }
+    const uint32_t nrec = tt < nkb - 1 ? nfull : (tt == nkb - 1 ? nlast : 0u);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(cur, nrec);
+    cur += (size_t)BN * (V ? vstride : kstride);
+#pragma unroll
+    for (int i = 0; i < NP; ++i)
+      buffer_load16_lds(rs, (EA_LDS void*)(stage + 512 * ((w & 3) * NP + i)), V ? dma_voff[i] : dma_off[i]);
+  };
   using KTILE = std::integral_constant<bool, false>;
   using VTILE_ = std::integral_constant<bool, true>;
   // stage r is a constant wherever these are inlined, so every access names
@@ -483,8 +509,8 @@ __device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) 
     pp_barrier();
     if constexpr (STATS == 2) c2 = stamp();
     if (grp == 0) {
-      dma_tile(kstage((r + 2) % 3), kg_base, s + 2, KTILE{});
-      dma_tile(vstage((r + 1) % 3), vg_base, s + 1, VTILE_{});
+      dma_next(kstage((r + 2) % 3), kdma, s + 2, KTILE{});
+      dma_next(vstage((r + 1) % 3), vdma, s + 1, VTILE_{});
     }
     cr.valu_part(s, act, qi, wrow, t.lk, off, sl, a.tau);
     if constexpr (STATS == 2) c3 = stamp();
