@@ -57,14 +57,14 @@ FP8_NORM_TOL, FP8_LSE_TOL = 5e-2, 5e-2            # MX fp8: normwise per (batch,
 # on; a kernel not listed (or changed since) reports traffic null. Sources:
 # profiles/*_counters.md.
 TRAFFIC = {
-    # fwd_pp_persistent_kernel<128, 128, causal>: 223,048 KiB fetched, 134,141 KiB written
-    "ea::fwd_pp_persistent_kernel<128, 128, causal>": 594_162_381,
+    # fwd_pp_persistent_kernel<128, 128, causal>: 211,182 KiB fetched, 134,629 KiB written
+    "ea::fwd_pp_persistent_kernel<128, 128, causal>": 570_360_832,
     # decode_split_kernel<true> + combine: 2,373,166 KiB fetched, 5,807 KiB written
     "ea::decode_split_kernel<page16> + ea::decode_combine_kernel": 4_866_191_360,
     # fwd_mx8_sp_kernel<causal, e4m3>: 173,648 KiB fetched, 133,336 KiB written
     "ea::fwd_mx8_sp_kernel<causal, e4m3>": 492_166_827,
-    # fwd_mx8_pp_persistent_kernel<causal, e4m3>: 126,308 KiB fetched, 133,125 KiB written
-    "ea::fwd_mx8_pp_persistent_kernel<causal, e4m3>": 394_997_248,
+    # fwd_mx8_pp_persistent_kernel<causal, e4m3>: 124,175 KiB fetched, 133,146 KiB written
+    "ea::fwd_mx8_pp_persistent_kernel<causal, e4m3>": 390_651_904,
 }
 
 
