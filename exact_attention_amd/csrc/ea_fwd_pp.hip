@@ -246,9 +246,18 @@ struct PpCore {
   // pb), m, l, rescale. act: the tile holds keys this
   // wave sees. qi: this lane's query row; wave_first_q: the wave's first row;
   // lk: keys of the sequence; off = lk - lq (bottom-right causal alignment).
+  // NDMA > 0: dma(i) for i < NDMA issues the wave's DMA pieces; they are
+  // spread over the exponentials of the first P (piece i after quarter i mod
+  // 4), so the CU's address unit takes them one at a time instead of the
+  // wave stalling behind a burst.
+  template <int NDMA = 0, typename F = int>
   __device__ __forceinline__ void valu_part(int s, bool act, int qi, int wave_first_q, int lk, int off, float sl,
-                                            float tau) {
+                                            float tau, const F& dma = 0) {
     if (!act) {
+      if constexpr (NDMA > 0) {
+#pragma unroll
+        for (int i = 0; i < NDMA; ++i) dma(i);
+      }
 #pragma unroll
       for (int st = 0; st < 4; ++st) pb[st] = bf16x8{};
       return;
@@ -275,7 +284,7 @@ struct PpCore {
     // yet) the row max is taken from S, still intact, and the rule applied as
     // written, forming P again if m moved.
     if constexpr (STATS) ++n_live;
-    float lsum = form_p(neg_m_run, sl);
+    float lsum = form_p<NDMA>(neg_m_run, sl, dma);
     if (__ballot(!(lsum <= thr_run))) {
       float mx = kNegInf;
 #pragma unroll
@@ -292,7 +301,7 @@ struct PpCore {
         m_run = m_new;
         neg_m_run = (m_run == kNegInf) ? 0.f : -m_run;
         thr_run = (m_run == kNegInf) ? -1.f : thr_tau;
-        lsum = form_p(neg_m_run, sl);
+        lsum = form_p<0>(neg_m_run, sl, 0);
       }
     }
     // the row sum in fp32, before the bf16 rounding of P
@@ -301,24 +310,41 @@ struct PpCore {
 
   // P = 2^(S sl + neg_m) over this lane's 32 scores (S is left intact): P^T
   // as bf16 MFMA operands in pb (keys 0..15 of s0, 16..31, then s1), and the
-  // fp32 sum of the 32 values
-  __device__ __forceinline__ float form_p(float neg_m, float sl) {
-    float ls = 0.f;
+  // fp32 sum of the 32 values (four partial sums, so the adds do not form one
+  // dependent chain). NDMA > 0: DMA pieces issued between the quarters.
+  template <int NDMA, typename F>
+  __device__ __forceinline__ float form_p(float neg_m, float sl, const F& dma) {
+    float ls4[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
+      if constexpr (NDMA > 0) {
+#pragma unroll
+        for (int i = st; i < NDMA; i += 4) dma(i);
+      }
       const f32x16& sv = st < 2 ? s0 : s1;
       const int i0 = 8 * (st & 1);
       float p[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         p[k] = pp_exp2<EXPMODE>(__builtin_fmaf(sv[i0 + k], sl, neg_m), i0 + k);
-        ls = (st == 0 && k == 0) ? p[k] : ls + p[k];
+        ls4[k & 3] = (st == 0 && k < 4) ? p[k] : ls4[k & 3] + p[k];
       }
       const i32x4 t = {(int)pack_bf16x2(p[0], p[1]), (int)pack_bf16x2(p[2], p[3]), (int)pack_bf16x2(p[4], p[5]),
                        (int)pack_bf16x2(p[6], p[7])};
       pb[st] = __builtin_bit_cast(bf16x8, t);
     }
-    return ls;
+    if constexpr (NDMA > 0) {
+      // each quarter's DMA pieces, then about a quarter of the vector work
+      __builtin_amdgcn_sched_group_barrier(0x010, (NDMA + 3) / 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 28, 0);
+      __builtin_amdgcn_sched_group_barrier(0x010, (NDMA + 2) / 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 28, 0);
+      __builtin_amdgcn_sched_group_barrier(0x010, (NDMA + 1) / 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 28, 0);
+      __builtin_amdgcn_sched_group_barrier(0x010, NDMA / 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 28, 0);
+    }
+    return (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]);
   }
 
   // ---- end of a tile: O = acc / l (bf16), lse = ln2 * (m + log2 l)
@@ -450,8 +476,8 @@ __device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) 
     for (int i = 0; i < NP; ++i)
       buffer_load16_lds(rs, (EA_LDS void*)(stage + 512 * ((w & 3) * NP + i)), V ? dma_voff[i] : dma_off[i]);
   };
-  // The same DMA inside the step loop with little scalar work in front of
-  // the softmax it precedes: the tile's address advances by one tile per step
+  // The DMA inside the step loop with little scalar work in front of the
+  // softmax it runs in: the tile's address advances by one tile per step
   // from a running pointer, and its record count is that of a whole tile, of
   // the last fetched tile (nkb - 1), or 0 past it. A tile at or past nkb gets
   // no records, so nothing is read from wherever its address points.
@@ -461,20 +487,29 @@ __device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) 
   // next tiles the loop fetches: K_2 and V_1 (the prologue fetches K_0, K_1, V_0)
   const uint16_t* kdma = uniform_ptr(kg_base + (size_t)2 * BN * kstride);
   const uint16_t* vdma = uniform_ptr(vg_base + (size_t)BN * vstride);
-  auto dma_next = [&](EA_LDS uint16_t* stage, const uint16_t*& cur, int tt, auto v_tile) __attribute__((always_inline)) {
-    constexpr bool V = decltype(v_tile)::value;
-    constexpr int NP = V ? IPWV : IPW;
-    uint32_t nfull = nrk_full, nlast = nrk_last;
-    if constexpr (V && DV != D) {  // V rows differ from K rows only for (192, 128)
-      nfull = uniform((BN - 1) * (int)vstride * 2 + DV * 2);
-      nlast = uniform(rows_last > 0 ? (rows_last - 1) * (int)vstride * 2 + DV * 2 : 0);
+  // The DMA of step s (K_{s+2} into kst, V_{s+1} into vst) as pieces for
+  // the VALU part to issue between its exponentials: piece i < IPW is this
+  // wave's i-th 1 KB piece of the K tile, the others its V pieces.
+  auto dma_pieces = [&](EA_LDS uint16_t* kst, EA_LDS uint16_t* vst, int s) __attribute__((always_inline)) {
+    uint32_t vfull = nrk_full, vlast = nrk_last;
+    if constexpr (DV != D) {  // V rows differ from K rows only for (192, 128)
+      vfull = uniform((BN - 1) * (int)vstride * 2 + DV * 2);
+      vlast = uniform(rows_last > 0 ? (rows_last - 1) * (int)vstride * 2 + DV * 2 : 0);
     }
-    const uint32_t nrec = tt < nkb - 1 ? nfull : (tt == nkb - 1 ? nlast : 0u);
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(cur, nrec);
-    cur += (size_t)BN * (V ? vstride : kstride);
-#pragma unroll
-    for (int i = 0; i < NP; ++i)
-      buffer_load16_lds(rs, (EA_LDS void*)(stage + 512 * ((w & 3) * NP + i)), V ? dma_voff[i] : dma_off[i]);
+    const int tk = s + 2, tv = s + 1;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kdma, tk < nkb - 1 ? nrk_full : (tk == nkb - 1 ? nrk_last : 0u));
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vdma, tv < nkb - 1 ? vfull : (tv == nkb - 1 ? vlast : 0u));
+    kdma += (size_t)BN * kstride;
+    vdma += (size_t)BN * vstride;
+    EA_LDS uint16_t* kd = kst + 512 * ((w & 3) * IPW);
+    EA_LDS uint16_t* vd = vst + 512 * ((w & 3) * IPWV);
+    return [=](int i) __attribute__((always_inline)) {
+      if (i < IPW) {
+        buffer_load16_lds(rk, (EA_LDS void*)(kd + 512 * i), dma_off[i]);
+      } else {
+        buffer_load16_lds(rv, (EA_LDS void*)(vd + 512 * (i - IPW)), dma_voff[i - IPW]);
+      }
+    };
   };
   using KTILE = std::integral_constant<bool, false>;
   using VTILE_ = std::integral_constant<bool, true>;
@@ -496,11 +531,13 @@ __device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) 
   // barrier late, so in phase 2s group A runs the MFMA part of step s while B
   // runs the VALU part of step s - 1, and in phase 2s + 1 A runs the VALU
   // part of s while B runs the MFMA part of s. Group A alone issues the DMA,
-  // at the start of its VALU part (phase 2s + 1, off the MFMA issue path):
-  // K_{s+2} and V_{s+1}, whose stages were last read in phase 2s - 1. It
+  // in its VALU part (phase 2s + 1, off the MFMA issue path), spread over the
+  // exponentials: K_{s+2} and V_{s+1}, whose stages were last read in phase
+  // 2s - 1. It
   // waits for them at the end of phase 2s + 3 -- leaving the next step's
   // pieces in flight -- before the barrier after which both groups read them.
-  auto step = [&](int r, int s) __attribute__((always_inline)) {
+  auto step = [&](int r, int s, auto issuer) __attribute__((always_inline)) {
+    constexpr bool A = decltype(issuer)::value;  // group A: issues the DMA
     const bool act = s < nkb && !tile_dead(s);
     uint32_t c0 = 0, c1 = 0, c2 = 0, c3 = 0;
     if constexpr (STATS == 2) c0 = stamp();
@@ -508,13 +545,14 @@ __device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) 
     if constexpr (STATS == 2) c1 = stamp();
     pp_barrier();
     if constexpr (STATS == 2) c2 = stamp();
-    if (grp == 0) {
-      dma_next(kstage((r + 2) % 3), kdma, s + 2, KTILE{});
-      dma_next(vstage((r + 1) % 3), vdma, s + 1, VTILE_{});
+    if constexpr (A) {
+      cr.template valu_part<IPW + IPWV>(s, act, qi, wrow, t.lk, off, sl, a.tau,
+                                        dma_pieces(kstage((r + 2) % 3), vstage((r + 1) % 3), s));
+    } else {
+      cr.valu_part(s, act, qi, wrow, t.lk, off, sl, a.tau);
     }
-    cr.valu_part(s, act, qi, wrow, t.lk, off, sl, a.tau);
     if constexpr (STATS == 2) c3 = stamp();
-    if (grp == 0) wait_vmcnt<IPW + IPWV>();
+    if constexpr (A) wait_vmcnt<IPW + IPWV>();
     pp_barrier();
     if constexpr (STATS == 2) {
       const uint32_t c4 = stamp();
@@ -548,13 +586,22 @@ __device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) 
     cyc0 = __builtin_amdgcn_s_memtime();
     rt0 = __builtin_amdgcn_s_memrealtime();
   }
-  if (grp == 1) pp_barrier();  // group B runs one phase behind
-  for (int s = 0; s <= nkb; s += 3) {
-    step(0, s);
-    if (s + 1 <= nkb) step(1, s + 1);
-    if (s + 2 <= nkb) step(2, s + 2);
+  // each group runs its own copy of the step loop (only group A's issues the
+  // DMA), so no branch on the group sits inside a step
+  auto loop = [&](auto issuer) __attribute__((always_inline)) {
+    for (int s = 0; s <= nkb; s += 3) {
+      step(0, s, issuer);
+      if (s + 1 <= nkb) step(1, s + 1, issuer);
+      if (s + 2 <= nkb) step(2, s + 2, issuer);
+    }
+  };
+  if (grp == 0) {
+    loop(std::integral_constant<bool, true>{});
+    pp_barrier();
+  } else {
+    pp_barrier();  // group B runs one phase behind
+    loop(std::integral_constant<bool, false>{});
   }
-  if (grp == 0) pp_barrier();
   // no DMA may still be writing this workgroup's LDS when it exits
   __builtin_amdgcn_s_waitcnt(0);
   uint32_t t_loop_end = 0;
