@@ -63,8 +63,8 @@ TRAFFIC = {
     "ea::decode_split_kernel<page16> + ea::decode_combine_kernel": 4_866_191_360,
     # fwd_mx8_sp_kernel<causal, e4m3>: 173,648 KiB fetched, 133,336 KiB written
     "ea::fwd_mx8_sp_kernel<causal, e4m3>": 492_166_827,
-    # fwd_mx8_pp_persistent_kernel<causal, e4m3>: 124,175 KiB fetched, 133,146 KiB written
-    "ea::fwd_mx8_pp_persistent_kernel<causal, e4m3>": 390_651_904,
+    # fwd_mx8_pp_persistent_kernel<causal, e4m3>: 101,508 KiB fetched, 133,122 KiB written
+    "ea::fwd_mx8_pp_persistent_kernel<causal, e4m3>": 344_206_080,
 }
 
 
@@ -737,7 +737,7 @@ def main():
         wave_cycles = cy[:, :, :6].sum()
         out["prefill"]["phases"] = {
             "what": "shader cycles per 64-key step and per tile, mean over waves (ea_test_fwd_phase_cycles); "
-                    "waves 0-3 issue the K/V DMA at the start of their VALU part; a wave's MFMA part runs beside "
+                    "waves 0-3 issue the K/V DMA spread over their VALU part; a wave's MFMA part runs beside "
                     "the other group's VALU part on the same SIMD; ideal MFMA part = 32 MFMAs x 32 cycles = 1024",
             "group_a_per_step": {"mfma_part": float(part[:4, 0].mean()), "wait_after_mfma": float(part[:4, 1].mean()),
                                  "valu_part_with_dma": float(part[:4, 2].mean()),

@@ -742,14 +742,21 @@ __device__ __forceinline__ void mx8_pp_tile(const Mx8Args& a, const int xcd, con
   __shared__ __attribute__((aligned(1024))) uint8_t ks0[STAGE], ks1[STAGE], ks2[STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t vs0[STAGE], vs1[STAGE], vs2[STAGE];
 
-  // ---------------- tile assignment: XCD-grouped, heaviest causal row blocks first
+  // ---------------- tile assignment: XCD-grouped. One workgroup per tile:
+  // heaviest causal row blocks first (dynamic dispatch balances the end).
+  // Persistent form: a (batch, head)'s row blocks in ascending order. The
+  // snake walk hands each workgroup a light and a heavy block, so every
+  // workgroup's load is as balanced as in descending order; when a head has
+  // more row blocks than its XCD has workgroups, the heavy blocks of the
+  // later round then start on the keys the light blocks of the earlier round
+  // have just brought into the XCD's L2, instead of rereading them from HBM.
   const int kg = j / a.n_mb;
   const int r0 = j - kg * a.n_mb;
   const int g = xcd + 8 * kg;
   if (g >= a.B * a.Hq) return;
   const int b = uniform(g / a.Hq);
   const int h = uniform(g - b * a.Hq);
-  const int mb = uniform(a.n_mb - 1 - r0);
+  const int mb = uniform(a.persist_wgs > 0 ? r0 : a.n_mb - 1 - r0);
   const int hk = uniform(h / a.group);
   const int N = a.N;
   const int row_lo = mb * BM;
