@@ -57,8 +57,8 @@ FP8_NORM_TOL, FP8_LSE_TOL = 5e-2, 5e-2            # MX fp8: normwise per (batch,
 # on; a kernel not listed (or changed since) reports traffic null. Sources:
 # profiles/*_counters.md.
 TRAFFIC = {
-    # fwd_pp_persistent_kernel<128, 128, causal>: 211,182 KiB fetched, 134,629 KiB written
-    "ea::fwd_pp_persistent_kernel<128, 128, causal>": 570_360_832,
+    # fwd_pp_persistent_kernel<128, 128, causal>: 214,301 KiB fetched, 134,763 KiB written
+    "ea::fwd_pp_persistent_kernel<128, 128, causal>": 576_886_428,
     # decode_split_kernel<true> + combine: 2,373,166 KiB fetched, 5,807 KiB written
     "ea::decode_split_kernel<page16> + ea::decode_combine_kernel": 4_866_191_360,
     # fwd_mx8_sp_kernel<causal, e4m3>: 173,648 KiB fetched, 133,336 KiB written
