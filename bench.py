@@ -737,7 +737,7 @@ def main():
         wave_cycles = cy[:, :, :6].sum()
         out["prefill"]["phases"] = {
             "what": "shader cycles per 64-key step and per tile, mean over waves (ea_test_fwd_phase_cycles); "
-                    "waves 0-3 issue the K/V DMA spread over their VALU part; a wave's MFMA part runs beside "
+                    "waves 0-3 fetch K and waves 4-7 fetch V, spread over their VALU parts; a wave's MFMA part runs beside "
                     "the other group's VALU part on the same SIMD; ideal MFMA part = 32 MFMAs x 32 cycles = 1024",
             "group_a_per_step": {"mfma_part": float(part[:4, 0].mean()), "wait_after_mfma": float(part[:4, 1].mean()),
                                  "valu_part_with_dma": float(part[:4, 2].mean()),

@@ -484,32 +484,31 @@ __device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) 
   const int rows_last = nkb > 0 ? min(t.lk - (nkb - 1) * BN, BN) : 0;
   const uint32_t nrk_full = uniform((BN - 1) * (int)kstride * 2 + D * 2);
   const uint32_t nrk_last = uniform(rows_last > 0 ? (rows_last - 1) * (int)kstride * 2 + D * 2 : 0);
-  // next tiles the loop fetches: K_2 and V_1 (the prologue fetches K_0, K_1, V_0)
+  // next tiles the loop fetches: K_2 by group A and V_2 by group B (the
+  // prologue fetches K_0, K_1, V_0, V_1)
   const uint16_t* kdma = uniform_ptr(kg_base + (size_t)2 * BN * kstride);
-  const uint16_t* vdma = uniform_ptr(vg_base + (size_t)BN * vstride);
-  // The DMA of step s (K_{s+2} into kst, V_{s+1} into vst) as pieces for
-  // the VALU part to issue between its exponentials: piece i < IPW is this
-  // wave's i-th 1 KB piece of the K tile, the others its V pieces.
-  auto dma_pieces = [&](EA_LDS uint16_t* kst, EA_LDS uint16_t* vst, int s) __attribute__((always_inline)) {
+  const uint16_t* vdma = uniform_ptr(vg_base + (size_t)2 * BN * vstride);
+  // The DMA of step s as pieces for the VALU part to issue between its
+  // exponentials: group A's K_{s+2} into kst (IPW pieces per wave), group B's
+  // V_{s+2} into vst (IPWV pieces per wave).
+  auto dma_k_pieces = [&](EA_LDS uint16_t* kst, int s) __attribute__((always_inline)) {
+    const int tk = s + 2;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kdma, tk < nkb - 1 ? nrk_full : (tk == nkb - 1 ? nrk_last : 0u));
+    kdma += (size_t)BN * kstride;
+    EA_LDS uint16_t* kd = kst + 512 * ((w & 3) * IPW);
+    return [=](int i) __attribute__((always_inline)) { buffer_load16_lds(rk, (EA_LDS void*)(kd + 512 * i), dma_off[i]); };
+  };
+  auto dma_v_pieces = [&](EA_LDS uint16_t* vst, int s) __attribute__((always_inline)) {
     uint32_t vfull = nrk_full, vlast = nrk_last;
     if constexpr (DV != D) {  // V rows differ from K rows only for (192, 128)
       vfull = uniform((BN - 1) * (int)vstride * 2 + DV * 2);
       vlast = uniform(rows_last > 0 ? (rows_last - 1) * (int)vstride * 2 + DV * 2 : 0);
     }
-    const int tk = s + 2, tv = s + 1;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kdma, tk < nkb - 1 ? nrk_full : (tk == nkb - 1 ? nrk_last : 0u));
+    const int tv = s + 2;
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vdma, tv < nkb - 1 ? vfull : (tv == nkb - 1 ? vlast : 0u));
-    kdma += (size_t)BN * kstride;
     vdma += (size_t)BN * vstride;
-    EA_LDS uint16_t* kd = kst + 512 * ((w & 3) * IPW);
     EA_LDS uint16_t* vd = vst + 512 * ((w & 3) * IPWV);
-    return [=](int i) __attribute__((always_inline)) {
-      if (i < IPW) {
-        buffer_load16_lds(rk, (EA_LDS void*)(kd + 512 * i), dma_off[i]);
-      } else {
-        buffer_load16_lds(rv, (EA_LDS void*)(vd + 512 * (i - IPW)), dma_voff[i - IPW]);
-      }
-    };
+    return [=](int i) __attribute__((always_inline)) { buffer_load16_lds(rv, (EA_LDS void*)(vd + 512 * i), dma_voff[i]); };
   };
   using KTILE = std::integral_constant<bool, false>;
   using VTILE_ = std::integral_constant<bool, true>;
@@ -530,29 +529,36 @@ __device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) 
   // ---- one step: MFMA part, barrier, VALU part, barrier. Group B starts one
   // barrier late, so in phase 2s group A runs the MFMA part of step s while B
   // runs the VALU part of step s - 1, and in phase 2s + 1 A runs the VALU
-  // part of s while B runs the MFMA part of s. Group A alone issues the DMA,
-  // in its VALU part (phase 2s + 1, off the MFMA issue path), spread over the
-  // exponentials: K_{s+2} and V_{s+1}, whose stages were last read in phase
-  // 2s - 1. It
-  // waits for them at the end of phase 2s + 3 -- leaving the next step's
-  // pieces in flight -- before the barrier after which both groups read them.
+  // part of s while B runs the MFMA part of s. Each group issues half of the
+  // DMA in its VALU part (off the MFMA issue path), spread over the
+  // exponentials, so the data lands in both groups' MFMA parts alike:
+  //  * group A, phase 2s + 1: K_{s+2}, into the stage K_{s-1} left (last read
+  //    in phase 2s - 1); it waits for it at the end of phase 2s + 3, leaving
+  //    the next step's pieces in flight;
+  //  * group B, phase 2s + 2: V_{s+2}, into the stage V_{s-1} left (last read
+  //    in phase 2s + 1); it waits for it at the end of its MFMA part of step
+  //    s + 2 (phase 2s + 5), leaving V_{s+3} in flight.
+  // Either wait comes before the barrier after which the other group first
+  // reads the tile (K_{s+2} in phase 2s + 4, V_{s+2} in phase 2s + 6).
   auto step = [&](int r, int s, auto issuer) __attribute__((always_inline)) {
     constexpr bool A = decltype(issuer)::value;  // group A: issues the DMA
     const bool act = s < nkb && !tile_dead(s);
     uint32_t c0 = 0, c1 = 0, c2 = 0, c3 = 0;
     if constexpr (STATS == 2) c0 = stamp();
     cr.mfma_part(kstage(r), vstage((r + 2) % 3));
+    // group B: V_s (issued two steps earlier) has landed before the barrier
+    // after which group A reads it; V_{s+1} may stay in flight
+    if constexpr (!A) wait_vmcnt<IPWV>();
     if constexpr (STATS == 2) c1 = stamp();
     pp_barrier();
     if constexpr (STATS == 2) c2 = stamp();
     if constexpr (A) {
-      cr.template valu_part<IPW + IPWV>(s, act, qi, wrow, t.lk, off, sl, a.tau,
-                                        dma_pieces(kstage((r + 2) % 3), vstage((r + 1) % 3), s));
+      cr.template valu_part<IPW>(s, act, qi, wrow, t.lk, off, sl, a.tau, dma_k_pieces(kstage((r + 2) % 3), s));
     } else {
-      cr.valu_part(s, act, qi, wrow, t.lk, off, sl, a.tau);
+      cr.template valu_part<IPWV>(s, act, qi, wrow, t.lk, off, sl, a.tau, dma_v_pieces(vstage((r + 2) % 3), s));
     }
     if constexpr (STATS == 2) c3 = stamp();
-    if constexpr (A) wait_vmcnt<IPW + IPWV>();
+    if constexpr (A) wait_vmcnt<IPW>();
     pp_barrier();
     if constexpr (STATS == 2) {
       const uint32_t c4 = stamp();
@@ -575,7 +581,9 @@ __device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) 
   if (grp == 0) {
     dma_tile(kstage(0), kg_base, 0, KTILE{});
     dma_tile(kstage(1), kg_base, 1, KTILE{});
+  } else {
     dma_tile(vstage(0), vg_base, 0, VTILE_{});
+    dma_tile(vstage(1), vg_base, 1, VTILE_{});
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
