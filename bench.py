@@ -57,14 +57,14 @@ FP8_NORM_TOL, FP8_LSE_TOL = 5e-2, 5e-2            # MX fp8: normwise per (batch,
 # on; a kernel not listed (or changed since) reports traffic null. Sources:
 # profiles/*_counters.md.
 TRAFFIC = {
-    # fwd_pp_persistent_kernel<128, 128, causal>: 214,301 KiB fetched, 134,763 KiB written
-    "ea::fwd_pp_persistent_kernel<128, 128, causal>": 576_886_428,
+    # fwd_pp_persistent_kernel<128, 128, causal>: 212,354 KiB fetched, 135,234 KiB written
+    "ea::fwd_pp_persistent_kernel<128, 128, causal>": 573_380_511,
     # decode_split_kernel<true> + combine: 2,373,166 KiB fetched, 5,807 KiB written
     "ea::decode_split_kernel<page16> + ea::decode_combine_kernel": 4_866_191_360,
     # fwd_mx8_sp_kernel<causal, e4m3>: 173,648 KiB fetched, 133,336 KiB written
     "ea::fwd_mx8_sp_kernel<causal, e4m3>": 492_166_827,
-    # fwd_mx8_pp_persistent_kernel<causal, e4m3>: 101,508 KiB fetched, 133,122 KiB written
-    "ea::fwd_mx8_pp_persistent_kernel<causal, e4m3>": 344_206_080,
+    # fwd_mx8_pp_persistent_kernel<causal, e4m3>: 101,508 KiB fetched, 133,124 KiB written
+    "ea::fwd_mx8_pp_persistent_kernel<causal, e4m3>": 344_208_693,
 }
 
 
@@ -740,7 +740,7 @@ def main():
                     "waves 0-3 fetch K and waves 4-7 fetch V, spread over their VALU parts; a wave's MFMA part runs beside "
                     "the other group's VALU part on the same SIMD; ideal MFMA part = 32 MFMAs x 32 cycles = 1024",
             "group_a_per_step": {"mfma_part": float(part[:4, 0].mean()), "wait_after_mfma": float(part[:4, 1].mean()),
-                                 "valu_part_with_dma": float(part[:4, 2].mean()),
+                                 "valu_part": float(part[:4, 2].mean()),
                                  "wait_after_valu": float(part[:4, 3].mean())},
             "group_b_per_step": {"mfma_part": float(part[4:, 0].mean()), "wait_after_mfma": float(part[4:, 1].mean()),
                                  "valu_part": float(part[4:, 2].mean()), "wait_after_valu": float(part[4:, 3].mean())},
