@@ -227,7 +227,11 @@ ea_status ea_attn_fwd_mx8(const void* q8, const void* k8, const void* v8,
  * products and the softmax, as the bf16 ping-pong kernel), EA_FWD_KERNEL_PERSISTENT
  * (that kernel with one workgroup per CU; AUTO: this form) or
  * EA_FWD_KERNEL_PIPELINED (8 waves, each interleaving its own products and
- * softmax); EA_FWD_KERNEL_UNROLL_KV,
+ * softmax). The per-tile forms take the causal row blocks heaviest first;
+ * the persistent form takes a (batch, head)'s row blocks in ascending order
+ * (its snake walk pairs light and heavy blocks on each workgroup either way;
+ * ascending, a head whose row blocks outnumber its XCD's workgroups rereads
+ * fewer keys from HBM). EA_FWD_KERNEL_UNROLL_KV,
  * exp_mode other than EA_EXP_HW and natural_order = 1 return
  * EA_ERR_UNSUPPORTED. rescale_log2 is the lazy-rescale threshold, which also
  * bounds P before its e4m3 rounding (P <= 2^rescale_log2): values above 8.807
