@@ -252,19 +252,17 @@ __device__ __forceinline__ void dq_tile(const BwdArgs& a, const int xcd, const i
     __syncthreads();
   }
 
-  // dQ = scale * acc, rows in lanes, d in elements (the forward's O layout)
+  // dQ = scale * acc, rows in lanes, d in elements (the forward's O layout),
+  // written as 16-byte row pieces (every lane takes part in the packing)
+  uint4 pk[NDT][2];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) pack_rows16(dq[dt], a.scale, pk[dt]);
   if (qi < lq) {
     uint16_t* op = a.dq + (q0 + qi) * qstride + (size_t)h * D;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = 32 * dt + 8 * g4 + 4 * hh;
-        uint2 val;
-        val.x = pack_bf16x2(dq[dt][4 * g4] * a.scale, dq[dt][4 * g4 + 1] * a.scale);
-        val.y = pack_bf16x2(dq[dt][4 * g4 + 2] * a.scale, dq[dt][4 * g4 + 3] * a.scale);
-        *(uint2*)(op + d0) = val;
-      }
+      for (int j = 0; j < 2; ++j) *(uint4*)(op + 32 * dt + 16 * j + 8 * hh) = pk[dt][j];
     }
   }
 }
@@ -565,19 +563,16 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, const int xcd, const
   __builtin_amdgcn_s_waitcnt(0);
 
   // dV = acc (role A), dK = scale * acc (role B): keys in lanes, d in elements
+  const float f = role_b ? a.scale : 1.0f;
+  uint4 pk[NDT][2];  // 16-byte row pieces (every lane takes part)
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) pack_rows16(acc[dt], f, pk[dt]);
   if (kj < lk) {
     uint16_t* dst = (role_b ? a.dk : a.dv) + (k0 + kj) * kstride + (size_t)hk * D;
-    const float f = role_b ? a.scale : 1.0f;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = 32 * dt + 8 * g4 + 4 * hh;
-        uint2 val;
-        val.x = pack_bf16x2(acc[dt][4 * g4] * f, acc[dt][4 * g4 + 1] * f);
-        val.y = pack_bf16x2(acc[dt][4 * g4 + 2] * f, acc[dt][4 * g4 + 3] * f);
-        *(uint2*)(dst + d0) = val;
-      }
+      for (int j = 0; j < 2; ++j) *(uint4*)(dst + 32 * dt + 16 * j + 8 * hh) = pk[dt][j];
     }
   }
 }

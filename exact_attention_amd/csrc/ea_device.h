@@ -98,6 +98,30 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// One 32-wide d tile of a transposed output accumulator (a lane holds row c
+// = lane mod 32 and d chunks 8 g + 4 hh .. + 3, g = 0..3, hh = lane div 32),
+// scaled by f and rounded to bf16, as 16-byte row pieces: lanes c and c + 32
+// trade one chunk of each pair (g = 2 j, 2 j + 1) across the lane halves, so
+// out[j] holds d 16 j + 8 hh .. + 7 of row c. Writing 16 bytes per lane halves
+// the store instructions of the 8-byte chunks. Every lane of the wave must
+// call it (the partners of a row hold the same row).
+__device__ __forceinline__ void pack_rows16(const f32x16& acc, float f, uint4 (&out)[2]) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int ga = 2 * j, gb = 2 * j + 1;
+    const uint32_t a0 = pack_bf16x2(acc[4 * ga] * f, acc[4 * ga + 1] * f);
+    const uint32_t a1 = pack_bf16x2(acc[4 * ga + 2] * f, acc[4 * ga + 3] * f);
+    const uint32_t b0 = pack_bf16x2(acc[4 * gb] * f, acc[4 * gb + 1] * f);
+    const uint32_t b1 = pack_bf16x2(acc[4 * gb + 2] * f, acc[4 * gb + 3] * f);
+    // lanes 32..63 of the first operand trade with lanes 0..31 of the second:
+    // lane c keeps its chunk 2 j and takes its partner's, lane c + 32 takes
+    // lane c's chunk 2 j + 1 and keeps its own
+    const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+    out[j] = uint4{s0[0], s1[0], s0[1], s1[1]};
+  }
+}
+
 // Sum of the two bf16 halves of a packed word, accumulated in fp32
 // (v_dot2c_f32_bf16 with (1,1)).
 __device__ __forceinline__ float add_bf16x2(uint32_t packed, float acc) {

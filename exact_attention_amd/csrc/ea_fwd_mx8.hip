@@ -1088,18 +1088,15 @@ __device__ __forceinline__ void mx8_pp_tile(const Mx8Args& a, const int xcd, con
   // ---------------- epilogue
   const float l_tot = sum_with_partner32(l_run);
   const float inv = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
+  uint4 pk[NDT][2];  // 16-byte row pieces (every lane takes part)
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) pack_rows16(oacc[dt], inv, pk[dt]);
   if (qi < N) {
     uint16_t* op = a.o + ((size_t)b * N + qi) * qstride + (size_t)h * D;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = 32 * dt + 8 * g4 + 4 * hh;
-        uint2 val;
-        val.x = pack_bf16x2(oacc[dt][4 * g4] * inv, oacc[dt][4 * g4 + 1] * inv);
-        val.y = pack_bf16x2(oacc[dt][4 * g4 + 2] * inv, oacc[dt][4 * g4 + 3] * inv);
-        *(uint2*)(op + d0) = val;
-      }
+      for (int j = 0; j < 2; ++j) *(uint4*)(op + 32 * dt + 16 * j + 8 * hh) = pk[dt][j];
     }
     if (a.lse != nullptr && hh == 0) {
       const float v = (l_tot > 0.f && m_run != kNegInf) ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
