@@ -452,8 +452,9 @@ __device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) 
   const size_t kstride = (size_t)a.Hkv * D, vstride = (size_t)a.Hkv * DV;
   cr.load_q(a, t);
 
-  // ---------------- K/V DMA: wave w of group A fills 1 KB pieces w*IPW ..
-  // w*IPW+IPW-1 of a tile
+  // ---------------- K/V DMA: wave w of the group that fetches an operand
+  // (K: group A, V: group B) fills 1 KB pieces (w mod 4) NP .. (w mod 4) NP +
+  // NP - 1 of its tile (NP = IPW for K, IPWV for V)
   const uint16_t* kg_base = a.k + (size_t)t.k0 * kstride + (size_t)t.hk * D;
   const uint16_t* vg_base = a.v + (size_t)t.k0 * vstride + (size_t)t.hk * DV;
   uint32_t dma_off[IPW], dma_voff[IPWV];
@@ -538,7 +539,7 @@ __device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) 
   // Either wait comes before the barrier after which the other group first
   // reads the tile (K_{s+2} in phase 2s + 4, V_{s+2} in phase 2s + 6).
   auto step = [&](int r, int s, auto issuer) __attribute__((always_inline)) {
-    constexpr bool A = decltype(issuer)::value;  // group A: issues the DMA
+    constexpr bool A = decltype(issuer)::value;  // group A (fetches K; group B fetches V)
     const bool act = s < nkb && !tile_dead(s);
     uint32_t c0 = 0, c1 = 0, c2 = 0, c3 = 0;
     if constexpr (STATS == 2) c0 = stamp();
@@ -567,8 +568,9 @@ __device__ __forceinline__ void pp_tile(const FwdArgs& a, const int xcd, int j) 
     }
   };
 
-  // prologue: K_0, K_1 and V_0 (read in steps 0 and 1); the V stage that
-  // step 0 multiplies by P = 0 is zeroed so it holds no stale NaN
+  // prologue: K_0, K_1 by group A, V_0, V_1 by group B (read in steps 0 to
+  // 2); the V stage that step 0 multiplies by P = 0 is zeroed so it holds no
+  // stale NaN
   {
     static_assert(VTILE % (8 * 512) == 0, "stage zeroing covers the tile");
 #pragma unroll
