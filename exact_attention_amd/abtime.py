@@ -5,6 +5,7 @@
 WHAT is one of
   bf16     the prefill forward, B=4 H=16 N=8192 d=128 causal (ea_attn_fwd_hd)
   bf16nc   the same, non-causal
+  bf16d64  the same shape with d = 64, causal (the 4-wave kernel by default)
   fp8      the MX fp8 forward, B=2 H=16 N=16384 d=128 causal e4m3 (ea_attn_fwd_mx8_fmt)
   bwd      the backward of the bf16 prefill workload (ea_attn_bwd_ex)
 with the default tuning of each build. Each library is loaded on its own
@@ -36,7 +37,7 @@ def _load(path, signatures):
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
-    ap.add_argument("what", choices=["bf16", "bf16nc", "fp8", "bwd"])
+    ap.add_argument("what", choices=["bf16", "bf16nc", "bf16d64", "fp8", "bwd"])
     ap.add_argument("libs", nargs="+")
     ap.add_argument("--rounds", type=int, default=5)
     ap.add_argument("--launches", type=int, default=20)
@@ -85,8 +86,8 @@ def main(argv=None):
             if st != 0:
                 raise RuntimeError(f"{args.libs[i]}: ea_attn_bwd_ex returned {st}")
     else:
-        causal = args.what == "bf16"
-        inp = W.prefill(causal)
+        causal = args.what != "bf16nc"
+        inp = W.dense(4, 8192, 8192, 16, 16, 64, True, seed=1002) if args.what == "bf16d64" else W.prefill(causal)
         q, k, v = bf16(inp.q), bf16(inp.k), bf16(inp.v)
         B, N, H, d = q.shape
         outs = [(torch.empty_like(q), torch.empty((B, H, N), dtype=torch.float32, device=dev)) for _ in libs]

@@ -306,18 +306,15 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
   // ---------------- epilogue: O = acc / l (bf16), lse = ln2 * (m + log2 l)
   const float l_tot = sum_with_partner32(l_run);
   const float inv = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
+  uint4 pk[NDT][2];  // 16-byte row pieces (every lane takes part)
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) pack_rows16(oacc[dt], inv, pk[dt]);
   if (qi < lq) {
     uint16_t* op = a.o + (size_t)(q0 + qi) * qstride + (size_t)h * D;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = 32 * dt + 8 * g4 + 4 * hh;
-        uint2 val;
-        val.x = pack_bf16x2(oacc[dt][4 * g4] * inv, oacc[dt][4 * g4 + 1] * inv);
-        val.y = pack_bf16x2(oacc[dt][4 * g4 + 2] * inv, oacc[dt][4 * g4 + 3] * inv);
-        *(uint2*)(op + d0) = val;
-      }
+      for (int j = 0; j < 2; ++j) *(uint4*)(op + 32 * dt + 16 * j + 8 * hh) = pk[dt][j];
     }
     if (a.lse != nullptr && hh == 0) {
       const float v = (l_tot > 0.f && m_run != kNegInf) ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
