@@ -361,7 +361,13 @@ struct PpCore {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) *(uint4*)(op + 32 * dt + 16 * j + 8 * hh) = pk[dt][j];
+        for (int j = 0; j < 2; ++j) {
+          // streaming stores: O does not displace the K/V lines other
+          // workgroups of the XCD are about to read from L2
+          const uint4 u = pk[dt][j];
+          const i32x4 v4 = {(int)u.x, (int)u.y, (int)u.z, (int)u.w};
+          __builtin_nontemporal_store(v4, (i32x4*)(op + 32 * dt + 16 * j + 8 * hh));
+        }
       }
       if (a.lse != nullptr && hh == 0) {
         const float v = (l_tot > 0.f && m_run != kNegInf) ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
