@@ -1096,6 +1096,9 @@ __device__ __forceinline__ void mx8_pp_tile(const Mx8Args& a, const int xcd, con
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
+      // (plain stores: streaming ones measured 1.2% faster here but let the
+      // 32-byte row pieces reach HBM unmerged, 1.10x the algorithmic bytes
+      // instead of 1.00x)
       for (int j = 0; j < 2; ++j) *(uint4*)(op + 32 * dt + 16 * j + 8 * hh) = pk[dt][j];
     }
     if (a.lse != nullptr && hh == 0) {
