@@ -7,6 +7,7 @@ WHAT is one of
   bf16nc   the same, non-causal
   bf16d64  the same shape with d = 64, causal (the 4-wave kernel by default)
   fp8      the MX fp8 forward, B=2 H=16 N=16384 d=128 causal e4m3 (ea_attn_fwd_mx8_fmt)
+  decode   the paged decode, B=64 Hq=32 Hkv=8 d=128, contexts U[512, 32768], page 16 (ea_attn_decode_paged)
   bwd      the backward of the bf16 prefill workload (ea_attn_bwd_ex)
 with the default tuning of each build. Each library is loaded on its own
 (RTLD_LOCAL) before the GPU is touched; every build gets 30 warm-up launches,
@@ -37,7 +38,7 @@ def _load(path, signatures):
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
-    ap.add_argument("what", choices=["bf16", "bf16nc", "bf16d64", "fp8", "bwd"])
+    ap.add_argument("what", choices=["bf16", "bf16nc", "bf16d64", "fp8", "bwd", "decode"])
     ap.add_argument("libs", nargs="+")
     ap.add_argument("--rounds", type=int, default=5)
     ap.add_argument("--launches", type=int, default=20)
@@ -69,6 +70,25 @@ def main(argv=None):
                                              m8.scale, 0, ctypes.byref(tun), stream.cuda_stream)
             if st != 0:
                 raise RuntimeError(f"{args.libs[i]}: ea_attn_fwd_mx8_fmt returned {st}")
+    elif args.what == "decode":
+        pg = W.paged_decode_device(dev)
+        q = bf16(pg.q)
+        kc, vc = pg.k_cache, pg.v_cache
+        bt = torch.from_numpy(pg.block_table).to(dev)
+        sl = torch.from_numpy(pg.seq_lens).to(dev)
+        B, Hq, d = q.shape
+        P_, ps, Hkv, _ = kc.shape
+        max_pages = bt.shape[1]
+        wsb = int(libs[0].ea_decode_workspace_size(B, Hq, Hkv, d, max_pages * ps, ps, 0))
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+        outs = [(torch.empty_like(q), torch.empty((B, Hq), dtype=torch.float32, device=dev)) for _ in libs]
+
+        def launch(i):
+            st = libs[i].ea_attn_decode_paged(P(q), P(kc), P(vc), P(bt), P(sl), P(outs[i][0]), P(outs[i][1]), B, Hq,
+                                              Hkv, d, ps, P_, max_pages, pg.scale, 0, P(ws), ws.numel(),
+                                              stream.cuda_stream)
+            if st != 0:
+                raise RuntimeError(f"{args.libs[i]}: ea_attn_decode_paged returned {st}")
     elif args.what == "bwd":
         inp = W.prefill(True)
         q, k, v = bf16(inp.q), bf16(inp.k), bf16(inp.v)

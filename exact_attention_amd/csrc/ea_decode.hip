@@ -207,8 +207,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(DecodeArgs
       for (int tl = 0; tl < 2; ++tl)
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          rk[4 * tl + u] = buffer_load16(rs[tl][0], voff0 + 4 * u * row_bytes);
-          rv[4 * tl + u] = buffer_load16(rs[tl][1], voff0 + 4 * u * row_bytes);
+          // streaming loads: every K/V byte is read once per launch
+          rk[4 * tl + u] = buffer_load16_nt(rs[tl][0], voff0 + 4 * u * row_bytes);
+          rv[4 * tl + u] = buffer_load16_nt(rs[tl][1], voff0 + 4 * u * row_bytes);
         }
     };
     // per-token path (page sizes 16 does not divide): lane i < 32 holds the
@@ -235,8 +236,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(DecodeArgs
           const int ri = __shfl(rows, 16 * tl + 4 * u + grp);
           i32x4 kx = i32x4{}, vx = i32x4{};
           if (ri >= 0) {
-            kx = *(const i32x4*)(kbase + (size_t)ri * row_elems);
-            vx = *(const i32x4*)(vbase + (size_t)ri * row_elems);
+            kx = __builtin_nontemporal_load((const i32x4*)(kbase + (size_t)ri * row_elems));
+            vx = __builtin_nontemporal_load((const i32x4*)(vbase + (size_t)ri * row_elems));
           }
           rk[4 * tl + u] = kx;
           rv[4 * tl + u] = vx;
