@@ -65,8 +65,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
   float acc = 0.f;
   if (t < rows && 8 * l16 < D) {
     const size_t base = (size_t)t * D + 8 * l16;
-    const bf16x8 o = *(const bf16x8*)(a.o + base);
-    const bf16x8 g = *(const bf16x8*)(a.dout + base);
+    // streaming loads: each byte of O and dO is read once here
+    const bf16x8 o = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load((const i32x4*)(a.o + base)));
+    const bf16x8 g = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load((const i32x4*)(a.dout + base)));
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc = __builtin_fmaf((float)o[i], (float)g[i], acc);
   }
