@@ -59,8 +59,9 @@ FP8_NORM_TOL, FP8_LSE_TOL = 5e-2, 5e-2            # MX fp8: normwise per (batch,
 TRAFFIC = {
     # fwd_pp_persistent_kernel<128, 128, causal>: 203,929 KiB fetched, 160,455 KiB written
     "ea::fwd_pp_persistent_kernel<128, 128, causal>": 581_953_599,
-    # decode_split_kernel<true> + combine: 2,372,533 KiB fetched, 5,738 KiB written
-    "ea::decode_split_kernel<page16> + ea::decode_combine_kernel": 4_864_823_296,
+    # decode_split_kernel + combine: 2,372,532 KiB fetched, 5,728 KiB written
+    "ea::decode_split_kernel + ea::decode_combine_kernel": 4_864_811_069,
+
     # fwd_mx8_sp_kernel<causal, e4m3>: 173,648 KiB fetched, 133,336 KiB written
     "ea::fwd_mx8_sp_kernel<causal, e4m3>": 492_166_827,
     # fwd_mx8_pp_persistent_kernel<causal, e4m3>: 101,508 KiB fetched, 133,125 KiB written
@@ -643,7 +644,7 @@ def main():
                          "launches": int(t_dc.size)}
         out["roofline_decode"] = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                   "frac": gbs / PEAK_HBM_GBS,
-                                  "kernel": f"ea::decode_split_kernel<{'page16' if pg.page_size % 16 == 0 else 'any'}>"
+                                  "kernel": "ea::decode_split_kernel"
                                             " + ea::decode_combine_kernel"}
         # the counters were taken at page size 16
         out["roofline_decode"]["traffic"] = (TRAFFIC.get(out["roofline_decode"]["kernel"])

@@ -23,19 +23,17 @@
 //  * A workgroup of 8 waves serves 8 KV heads, one wave per head, all walking
 //    the same chunks. In the [pages, page_size, Hkv, d] cache a token's rows for
 //    all KV heads are adjacent, so the workgroup streams whole contiguous rows.
-//  * A chunk is two 16-token tiles. When 16 divides page_size a tile lies in
-//    one page: page indices are loaded 128 tiles at a time (two per lane) and
-//    read with v_readlane in the loop; each tile is a buffer resource bounded
-//    by the sequence length, so tokens at or past it (stale or poisoned slots
-//    of a last page) and page indices outside the pool read as zeros, no
-//    branch.
-//  * Any other page size (down to 1) takes the per-token path. Address
-//    generation is decoupled from use, as in the pages' transposed scheme for
-//    small pages: lane i < 32 looks up the page of the chunk's token i once
-//    (block-table entry prefetched one chunk ahead) and forms its row index;
-//    each lane then fetches the row indices of the 8 tokens it copies with
-//    lane shuffles instead of recomputing them. Tokens at or past the sequence
-//    end and pages outside the pool read as zeros.
+//  * A chunk is two 16-token tiles, loaded token by token for every page size
+//    (down to 1). Address generation is decoupled from use, as in the pages'
+//    transposed scheme for small pages: lane i < 32 looks up the page of the
+//    chunk's token i once (block-table entry prefetched one chunk ahead) and
+//    forms its row index; each lane then fetches the row indices of the 8
+//    tokens it copies with lane shuffles instead of recomputing them. Tokens
+//    at or past the sequence end and pages outside the pool read as zeros.
+//    Every K/V byte is read once per launch, so the loads are streaming
+//    (non-temporal). (A per-tile path for page sizes that 16 divides -- one
+//    buffer resource per 16-token tile -- measured 1.8% slower than this one
+//    at page 16 once both used streaming loads.)
 //  * Query heads: the G = Hq / Hkv heads of one KV head are packed as columns
 //    of 16-wide blocks (PR 2186's GQA packing for any ratio). G <= 16 leaves
 //    unused columns; G > 16 gives a KV head several blocks, one wave each, and
@@ -99,7 +97,7 @@ __device__ __forceinline__ int range_start(int w, int Tc, int W) {
 // DUMP (test-only): every wave of a KV head's first column block also writes
 // the K and V rows it staged for each chunk, as gathered, to a.dump_k /
 // a.dump_v at (sequence, token, KV head).
-template <bool PAGE16, bool DUMP = false>
+template <bool DUMP = false>
 __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(DecodeArgs a) {
   constexpr int D = kD;
   constexpr int TILE = kChunk * D;  // bf16 elements per K or V chunk
@@ -128,12 +126,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(DecodeArgs
 
   const int grp = lane >> 4, col = lane & 15;
   const int ps = a.page_size;
-  const int row_bytes = a.Hkv * D * 2;  // bytes between consecutive slots of a page
   EA_LDS uint16_t* ks = sm + wv * 2 * TILE;
   EA_LDS uint16_t* vs = ks + TILE;
 
   // loop-invariant LDS offsets
-  const uint32_t voff0 = (uint32_t)(grp * row_bytes + col * 16);
   int st_off[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
@@ -172,47 +168,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(DecodeArgs
       for (int kk = 0; kk < D / 32; ++kk) qf[kk] = (col < ncols) ? *(const bf16x8*)(qp + 32 * kk) : bf16x8{};
     }
 
-    // Page indices of 128 consecutive 16-token tiles (64 chunks), two per lane;
-    // in the loop they come from v_readlane, so no memory access there has a
-    // wait that would also wait for the K/V loads in flight.
-    int lane_page[2];
-    auto load_pages = [&](int ci0) {
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int tt = t_begin + kChunk * ci0 + 16 * (64 * r + lane);
-        lane_page[r] = (tt < t_end) ? bt[tt / ps] : -1;
-      }
-    };
-    // A tile's buffer resource starts at its first slot for this KV head and
-    // ends after the last valid token.
-    auto tile_rsrc = [&](const uint16_t* cache, int tt, int page) {
-      const int slot = uniform(tt % ps);
-      const bool ok = (unsigned)page < (unsigned)a.num_pages && tt < t_end;
-      const int nvalid = ok ? min(16, t_end - tt) : 0;
-      const uint16_t* base = uniform_ptr(cache + (((size_t)(ok ? page : 0) * ps + slot) * a.Hkv + hkv) * D);
-      return make_rsrc(base, nvalid > 0 ? (uint32_t)((nvalid - 1) * row_bytes + D * 2) : 0u);
-    };
-    // chunk staging: lane handles rows 4u + grp (u = 0..7), 16-byte column chunk col.
-    // Both tiles' page indices are read before the chunk's first load, where no
-    // load is in flight, so their waits cost nothing.
+    // chunk staging: lane handles rows 4u + grp (u = 0..7), 16-byte column chunk col
     i32x4 rk[8], rv[8];
-    auto gload = [&](int ci) {
-      const int idx = 2 * (ci & 31);
-      const int lp = (ci & 32) ? lane_page[1] : lane_page[0];
-      const int page0 = __builtin_amdgcn_readlane(lp, idx), page1 = __builtin_amdgcn_readlane(lp, idx + 1);
-      const int tt = uniform(t_begin + kChunk * ci);
-      const __amdgpu_buffer_rsrc_t rs[2][2] = {{tile_rsrc(a.kc, tt, page0), tile_rsrc(a.vc, tt, page0)},
-                                               {tile_rsrc(a.kc, tt + 16, page1), tile_rsrc(a.vc, tt + 16, page1)}};
-#pragma unroll
-      for (int tl = 0; tl < 2; ++tl)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          // streaming loads: every K/V byte is read once per launch
-          rk[4 * tl + u] = buffer_load16_nt(rs[tl][0], voff0 + 4 * u * row_bytes);
-          rv[4 * tl + u] = buffer_load16_nt(rs[tl][1], voff0 + 4 * u * row_bytes);
-        }
-    };
-    // per-token path (page sizes 16 does not divide): lane i < 32 holds the
+    // lane i < 32 holds the
     // block-table entry and slot of token i of a chunk, and from them the row
     // index page * page_size + slot, or -1 for a token past the end or a page
     // outside the pool.
@@ -272,11 +230,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(DecodeArgs
 #pragma unroll
     for (int mt = 0; mt < D / 16; ++mt) oacc[mt] = f32x4{};
 
-    int ent_next = -1, slot_next = 0;  // per-token path: entry of chunk ci + 1
-    if constexpr (PAGE16) {
-      load_pages(0);
-      gload(0);
-    } else {
+    int ent_next = -1, slot_next = 0;  // entry of chunk ci + 1
+    {
       int slot0;
       const int ent0 = bt_entry(0, slot0);
       if (nck > 1) ent_next = bt_entry(1, slot_next);
@@ -288,16 +243,11 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(DecodeArgs
     for (int ci = 0; ci < nck; ++ci) {
       const int t0 = t_begin + kChunk * ci;
       if (ci + 1 < nck) {
-        if constexpr (PAGE16) {
-          if (((ci + 1) & 63) == 0) load_pages(ci + 1);
-          gload(ci + 1);
-        } else {
-          // the entry of chunk ci + 1 was loaded one chunk ago (before the
-          // loads of chunk ci, which the last sstore waited for)
-          const int rows = row_index(ent_next, slot_next);
-          if (ci + 2 < nck) ent_next = bt_entry(ci + 2, slot_next);
-          gload_rows(rows);
-        }
+        // the entry of chunk ci + 1 was loaded one chunk ago (before the
+        // loads of chunk ci, which the last sstore waited for)
+        const int rows = row_index(ent_next, slot_next);
+        if (ci + 2 < nck) ent_next = bt_entry(ci + 2, slot_next);
+        gload_rows(rows);
       }
       // ---- S^T = K Q^T for two 16-token tiles
       f32x4 s[2];
@@ -449,9 +399,8 @@ void decode_bind_workspace(DecodeArgs& a, void* workspace) {
   a.plan = (int*)p;
 }
 
-template <bool PAGE16>
 static hipError_t launch_p(const DecodeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(decode_split_kernel<PAGE16>, dim3(a.num_ranges, decode_head_groups(a.Hkv, a.group)),
+  hipLaunchKernelGGL(decode_split_kernel<false>, dim3(a.num_ranges, decode_head_groups(a.Hkv, a.group)),
                      dim3(64 * kWaves), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -463,17 +412,13 @@ hipError_t launch_decode_gather_dump(const DecodeArgs& a, hipStream_t s) {
   if (a.num_ranges <= 0 || a.part_o == nullptr || a.plan == nullptr || a.dump_k == nullptr || a.dump_v == nullptr)
     return hipErrorInvalidValue;
   const dim3 grid(a.num_ranges, decode_head_groups(a.Hkv, a.group));
-  if (a.page_size % 16 == 0) {
-    hipLaunchKernelGGL((decode_split_kernel<true, true>), grid, dim3(64 * kWaves), 0, s, a);
-  } else {
-    hipLaunchKernelGGL((decode_split_kernel<false, true>), grid, dim3(64 * kWaves), 0, s, a);
-  }
+  hipLaunchKernelGGL((decode_split_kernel<true>), grid, dim3(64 * kWaves), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   if (a.num_ranges <= 0 || a.part_o == nullptr || a.plan == nullptr) return hipErrorInvalidValue;
-  return (a.page_size % 16 == 0) ? launch_p<true>(a, s) : launch_p<false>(a, s);
+  return launch_p(a, s);
 }
 
 // ---------------------------------------------------------------------------

@@ -190,11 +190,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ i32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
 }
-// the same as a streaming load (cache policy nt): for data read once, which
-// then does not displace reused lines from the caches
-__device__ __forceinline__ i32x4 buffer_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 2);
-}
 // LDS DMA: 16 bytes per lane from the buffer at voff into LDS; lane s lands at
 // lds + 16 s (lds must be wave-uniform). Out-of-range lanes write zeros.
 __device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, EA_LDS void* lds, uint32_t voff) {

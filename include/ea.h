@@ -312,8 +312,8 @@ ea_status ea_attn_fwd_mx8_fmt(const void* q8, const void* k8, const void* v8,
  *   seq_lens [B] int32, each in [0, max_pages_per_seq * page_size] (larger
  *          values are clamped to that capacity)
  *   o      [B, Hq, d] bf16 (written); lse [B, Hq] fp32 or NULL
- *   page_size >= 1 (multiples of 16 take a per-tile load path, other sizes
- *          a per-token one). The arithmetic follows the logical token order
+ *   page_size >= 1 (every size takes the same token-by-token load path).
+ *          The arithmetic follows the logical token order
  *          only, so the same tokens give bitwise the same output whatever the
  *          page size and page placement. d == 128; any Hq that is a multiple
  *          of Hkv; num_pages * page_size < 2^31.
